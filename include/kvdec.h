@@ -1,0 +1,281 @@
+/*
+ * kvdec -- single-query (one new token per slot) grouped-query decode
+ * attention over a long KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The method is split-KV flash decoding.  A slot's cells are cut into
+ * 128-cell tiles; each workgroup streams a contiguous range of tiles of one
+ * (slot, KV head) and produces an online-softmax partial (running maximum m,
+ * sum l, unnormalised output o); a log-sum-exp merge combines the partials.
+ * The same merge joins a resident window with a tail streamed from pinned
+ * host memory ("Rolling-KV -- overflow throughput evaluations
+ * (consolidated)", sections 1 and 3: the window is attended on the device,
+ * the host tail is re-read every step, and the log-sum-exp channel is what
+ * lets the two results combine).  Caches may be f16 or block-scaled int8 /
+ * 4-bit, and cells may be given either as a contiguous range or as an
+ * indirect list that the planner turns into a record-grouped plan with -1
+ * holes ("KVARN KV Performance optimizations", beellama.cpp issue 140,
+ * "What was implemented", items 3, 4 and 9).
+ *
+ * What is computed, for slot s and query head h (G = n_q_heads / n_kv_heads,
+ * KV head g = floor(h / G), C_s the slot's attended cells):
+ *     s_c = scale * sum_d q[s,h,d] * K[c,g,d]             for c in C_s
+ *     m = max_c s_c,  l = sum_c e^(s_c - m),  o = sum_c e^(s_c - m) V[c,g,:]
+ *     out[s,h,:] = o / l,   lse[s,h] = m + ln l
+ * An empty C_s gives out = 0 and lse = -inf.  K and V are the dequantised
+ * cache values: f16 as stored; int8 code q -> d * q; 4-bit code u -> d * (u - 8),
+ * with one f16 scale d per 32 consecutive elements of a (cell, KV head) row
+ * and element 2i of a 4-bit row in the low nibble of byte i.
+ *
+ * Arithmetic: fp32 accumulation.  q and the softmax weights may be rounded
+ * to f16 inside packed dot products; results match a float64 evaluation of
+ * the formula above to 2e-3 absolute for inputs of the magnitudes a decode
+ * step sees (|q| far below the f16 limit of 65504).
+ *
+ * Ownership and threading.  The caller owns every buffer: q, the caches,
+ * outputs and the workspace (device memory) and the pinned host tail.  The
+ * library never allocates device memory and keeps no pointer after a call
+ * returns, apart from work it has enqueued on the caller's streams.  A plan
+ * is an immutable host object, safe to share between threads; it must be
+ * rebuilt whenever the cache metadata it was built from changes.  A
+ * workspace must not be used by two calls that may run at the same time.
+ *
+ * Errors.  Every entry point returns KVDEC_OK (0) or a negative code.
+ * Arguments are validated before anything is enqueued, so a failed call has
+ * no side effects; kvdec_last_error() gives a message for the calling
+ * thread's most recent failure.  Faults inside enqueued device work surface
+ * at the next synchronisation of the stream, as for any HIP kernel.
+ */
+#ifndef KVDEC_H
+#define KVDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVDEC_VERSION 10000 /* 1.0.0 */
+
+/* Status codes. */
+#define KVDEC_OK 0
+#define KVDEC_E_INVALID (-1)     /* bad shape, null or misaligned pointer, bad enum */
+#define KVDEC_E_RANGE (-2)       /* a cell >= capacity, or negative and not -1 */
+#define KVDEC_E_UNSUPPORTED (-3) /* valid request with no compiled kernel for it */
+#define KVDEC_E_WORKSPACE (-4)   /* workspace null or smaller than the plan needs */
+#define KVDEC_E_NOMEM (-5)       /* host allocation failed */
+#define KVDEC_E_DEVICE (-6)      /* a HIP runtime call failed */
+
+/* Cache storage kinds (k_type, v_type). */
+#define KVDEC_F16 0    /* binary16, 2 bytes per element */
+#define KVDEC_Q8_B32 1 /* int8 codes + one f16 scale per 32 elements */
+#define KVDEC_Q4_B32 2 /* 4-bit codes, two per byte, + one f16 scale per 32 elements */
+
+/* Cells per tile and per physical record of an indirect plan. */
+#define KVDEC_TILE_CELLS 128
+
+/* Largest slot count a single plan accepts. */
+#define KVDEC_MAX_SLOTS 64
+
+/*
+ * Problem description, read by kvdec_plan (host memory only; nothing is
+ * retained after the call returns).
+ *
+ * n_q_heads, n_kv_heads: n_q_heads must be a multiple of n_kv_heads and the
+ *   group size G = n_q_heads / n_kv_heads must lie in 1..16; kernels are
+ *   built for G <= 8, larger groups give KVDEC_E_UNSUPPORTED.
+ * head_dim: 64, 128 or 256.
+ * n_slots: 1..KVDEC_MAX_SLOTS (one query row per slot).
+ * k_type, v_type: KVDEC_F16 / KVDEC_Q8_B32 / KVDEC_Q4_B32.
+ * scale: multiplies q.k before the softmax (usually 1/sqrt(head_dim)).
+ * capacity_cells: number of device cells addressable through the K/V
+ *   pointers of kvdec_attend; every attended cell must lie below it.
+ *
+ * Cell selection, one of:
+ *   contiguous (cells == NULL): slot s attends device cells
+ *     [cell_begin[s], cell_begin[s] + n_occupied[s]); cell_begin may be NULL
+ *     (all zero).  n_occupied[s] may be 0.
+ *   indirect (cells != NULL): slot s's raw list is
+ *     cells[cells_off[s] .. cells_off[s+1]-1]; -1 entries are holes, any other
+ *     negative entry or an entry >= capacity_cells is KVDEC_E_RANGE, and
+ *     duplicates are dropped (first occurrence kept).  The planner groups the
+ *     kept cells by physical 128-cell record (cell / 128), takes the records
+ *     in ascending order and emits one 128-entry segment per record whose
+ *     entry k is record*128 + k when that cell was kept and -1 otherwise
+ *     ("KVARN KV Performance optimizations", items 3 and 4).
+ *
+ * Host tail (optional, contiguous mode only): when n_tail != NULL, slot s
+ *   also attends cells [tail_begin[s], tail_begin[s] + n_tail[s]) of the
+ *   pinned host tail arrays passed to kvdec_attend (dense
+ *   [tail cell][kv head][row], scales likewise); tail_begin may be NULL (all
+ *   zero) and tail_capacity_cells bounds the tail arrays.  The tail is copied
+ *   to the device in chunks of tail_chunk_cells (a multiple of 128; 0 picks
+ *   2048) through a ring of tail_ring_depth staging slots (>= 2; 0 picks 4)
+ *   inside the workspace.
+ *
+ * tiles_per_split: 128-cell tiles per workgroup; 0 lets the planner choose
+ *   so that the launch fills the device.  Only the floating-point summation
+ *   order depends on it.
+ */
+typedef struct kvdec_problem {
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t n_slots;
+    int32_t k_type;
+    int32_t v_type;
+    float scale;
+    int32_t tiles_per_split;
+    int64_t capacity_cells;
+    const int64_t* cell_begin; /* [n_slots] or NULL */
+    const int64_t* n_occupied; /* [n_slots], contiguous mode */
+    const int32_t* cells;      /* indirect mode raw lists, or NULL */
+    const int64_t* cells_off;  /* [n_slots + 1], indirect mode */
+    const int64_t* tail_begin; /* [n_slots] or NULL */
+    const int64_t* n_tail;     /* [n_slots] or NULL (no tail) */
+    int64_t tail_capacity_cells;
+    int64_t tail_chunk_cells;
+    int32_t tail_ring_depth;
+    int32_t reserved;
+} kvdec_problem;
+
+/* Opaque, immutable plan. */
+typedef struct kvdec_plan kvdec_plan_t;
+
+/*
+ * Device buffers and outputs of one kvdec_attend call.
+ *
+ * q: device fp32 [n_slots][n_q_heads][head_dim].
+ * k, v: device code arrays.  Row (cell c, KV head g) starts at byte
+ *   c * cell_stride + g * head_stride; a row holds head_dim f16 values,
+ *   head_dim int8 codes, or head_dim / 2 bytes of 4-bit codes.  A stride of 0
+ *   means the dense layout [cell][kv head][row].  Base pointers and strides
+ *   must be multiples of 16 bytes (of 8 bytes for 4-bit rows).
+ * k_scales, v_scales: device f16 scales, dense [cell][kv head][head_dim/32],
+ *   required for the block-scaled kinds and ignored for f16.
+ * plan_cells: device int32 copy of the plan's entries (kvdec_plan_cells) in
+ *   indirect mode, else NULL.  Entries outside [0, capacity_cells) are read
+ *   as holes.
+ * k_tail, v_tail (+ k_tail_scales, v_tail_scales): pinned host tail arrays
+ *   when the plan has a tail, else NULL.  They must stay valid and unchanged
+ *   until the work enqueued by the call has finished.
+ * out: device fp32 [n_slots][n_q_heads][head_dim] or NULL.
+ * lse: device fp32 [n_slots][n_q_heads] or NULL.
+ * part_m, part_l, part_o: device fp32 [n_slots][n_q_heads] (m, l) and
+ *   [n_slots][n_q_heads][head_dim] (o): the call's whole result as one
+ *   partial (m in score units, l and o relative to e^m, o unnormalised), for
+ *   merging with other partials through kvdec_merge; all three or none.
+ * At least one of out and the partial triple must be given.
+ */
+typedef struct kvdec_io {
+    const float* q;
+    const void* k;
+    const void* v;
+    const void* k_scales;
+    const void* v_scales;
+    int64_t k_cell_stride;
+    int64_t k_head_stride;
+    int64_t v_cell_stride;
+    int64_t v_head_stride;
+    const int32_t* plan_cells;
+    const void* k_tail;
+    const void* v_tail;
+    const void* k_tail_scales;
+    const void* v_tail_scales;
+    float* out;
+    float* lse;
+    float* part_m;
+    float* part_l;
+    float* part_o;
+} kvdec_io;
+
+/* One partial result set for kvdec_merge: rows are (slot, query head) pairs,
+ * m and l are [n_rows], o is [n_rows][head_dim], all device fp32. */
+typedef struct kvdec_partial {
+    const float* m;
+    const float* l;
+    const float* o;
+} kvdec_partial;
+
+/*
+ * Build a plan (host only, deterministic).  n_cu is the number of compute
+ * units to fill; 0 queries the current HIP device.  On success *out receives
+ * the plan and *workspace_bytes the size of the device workspace that
+ * kvdec_attend needs with it (the tile/split partials, merge tickets and the
+ * tail staging ring).  A workspace must be zero-filled once before its first
+ * use; every completed call leaves its ticket words at zero again.
+ * Errors: KVDEC_E_INVALID, KVDEC_E_RANGE, KVDEC_E_UNSUPPORTED, KVDEC_E_NOMEM,
+ * KVDEC_E_DEVICE (only when n_cu == 0 and the device query fails).
+ */
+int kvdec_plan(const kvdec_problem* problem, int32_t n_cu, kvdec_plan_t** out, size_t* workspace_bytes);
+
+/* Copy out the plan's indirect entries (int32, -1 holes) and per-slot entry
+ * offsets (int64 [n_slots + 1]) for upload to the device.  With
+ * cells_out == NULL only *n_entries is written.  A contiguous plan has zero
+ * entries.  Errors: KVDEC_E_INVALID. */
+int kvdec_plan_cells(const kvdec_plan_t* plan, int32_t* cells_out, int64_t* offsets_out, int64_t* n_entries);
+
+/* Summary of a plan, for logs and tests. */
+typedef struct kvdec_plan_info {
+    int32_t n_slots;
+    int32_t group;            /* G */
+    int32_t n_workgroups;     /* workgroups of the resident launch */
+    int32_t tiles_per_split;  /* largest tile count of any split */
+    int64_t n_tiles;          /* tiles over all slots and KV heads */
+    int64_t n_entries;        /* indirect entries (0 when contiguous) */
+    int64_t n_tail_chunks;    /* tail chunks over all slots */
+    int64_t workspace_bytes;
+} kvdec_plan_info;
+
+int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info);
+
+/* Split table: for each workgroup of the resident launch, 4 int64 values
+ * (slot, kv head, first tile, tile count).  With splits_out == NULL only
+ * *n_splits is written. */
+int kvdec_plan_splits(const kvdec_plan_t* plan, int64_t* splits_out, int64_t* n_splits);
+
+void kvdec_plan_free(kvdec_plan_t* plan);
+
+/*
+ * Enqueue one decode-attention evaluation on `stream` (a hipStream_t; NULL is
+ * the default stream).  `copy_stream` carries the host-to-device copies of
+ * the tail (needed only when the plan has a tail; NULL then means `stream`).
+ * workspace: device memory of at least the plan's workspace_bytes, 256-byte
+ * aligned, zero-filled before its first use.  Asynchronous: returns once the
+ * work is enqueued.
+ * Errors: KVDEC_E_INVALID, KVDEC_E_WORKSPACE, KVDEC_E_UNSUPPORTED,
+ * KVDEC_E_DEVICE.
+ */
+int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, size_t workspace_bytes,
+                 void* stream, void* copy_stream);
+
+/*
+ * Log-sum-exp merge of n_parts partial sets over the same n_rows rows
+ * (section 9 of "KVARN KV Performance optimizations": partial windows keep
+ * their maximum, numerator and denominator and are merged afterwards):
+ *     M = max_p m_p,  L = sum_p l_p e^(m_p - M),  O = sum_p o_p e^(m_p - M)
+ *     out = O / L,    lse = M + ln L
+ * Partials with m = -inf contribute nothing; rows where all are empty give
+ * out = 0, lse = -inf and the merged partial (-inf, 0, 0).  out, lse and the
+ * merged triple (merged_m, merged_l, merged_o) are each optional (NULL), but
+ * at least one output must be given.  `parts` is host memory holding device
+ * pointers; 1 <= n_parts <= 64; head_dim in 1..1024.  Asynchronous on stream.
+ * Errors: KVDEC_E_INVALID, KVDEC_E_DEVICE.
+ */
+int kvdec_merge(int32_t n_parts, const kvdec_partial* parts, int64_t n_rows, int32_t head_dim, float* out,
+                float* lse, float* merged_m, float* merged_l, float* merged_o, void* stream);
+
+/* Static description of a status code. */
+const char* kvdec_strerror(int status);
+
+/* Message for the calling thread's most recent failure ("" if none). */
+const char* kvdec_last_error(void);
+
+/* KVDEC_VERSION of the built library. */
+int kvdec_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVDEC_H */

@@ -1,0 +1,356 @@
+// C-ABI entry points of libkvdec: plan construction, argument validation,
+// kernel dispatch and the pinned-host tail streamer.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& msg) {
+    g_last_error = msg;
+    return status;
+}
+
+int device_fail(hipError_t e, const char* what) {
+    g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+    return KVDEC_E_DEVICE;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Fill the per-launch fields shared by the resident and the tail launches.
+void common_args(const kvdec_plan_t& p, const kvdec_io& io, kvdec::SplitArgs& a) {
+    std::memset(&a, 0, sizeof(a));
+    a.q = io.q;
+    a.scale_log2 = p.scale * 1.4426950408889634f;
+    a.n_q_heads = p.n_q_heads;
+    a.n_kv_heads = p.n_kv_heads;
+    a.out = io.out;
+    a.lse = io.lse;
+    a.pm = io.part_m;
+    a.pl = io.part_l;
+    a.po = io.part_o;
+    a.acc_rows = p.n_slots * p.n_q_heads;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvdec_version(void) { return KVDEC_VERSION; }
+
+const char* kvdec_strerror(int status) {
+    switch (status) {
+        case KVDEC_OK: return "ok";
+        case KVDEC_E_INVALID: return "invalid argument";
+        case KVDEC_E_RANGE: return "cell index out of range";
+        case KVDEC_E_UNSUPPORTED: return "unsupported configuration";
+        case KVDEC_E_WORKSPACE: return "workspace missing or too small";
+        case KVDEC_E_NOMEM: return "host out of memory";
+        case KVDEC_E_DEVICE: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* kvdec_last_error(void) { return g_last_error.c_str(); }
+
+int kvdec_plan(const kvdec_problem* problem, int32_t n_cu, kvdec_plan_t** out, size_t* workspace_bytes) {
+    g_last_error.clear();
+    if (!problem || !out) return fail(KVDEC_E_INVALID, "problem and out must be non-null");
+    *out = nullptr;
+    if (n_cu < 0) return fail(KVDEC_E_INVALID, "n_cu must be >= 0");
+    if (n_cu == 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+        e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return device_fail(e, "hipDeviceGetAttribute");
+    }
+    kvdec_plan_t* plan = nullptr;
+    try {
+        plan = new kvdec_plan_t();
+        std::string err;
+        const int st = kvdec::build_plan(*problem, n_cu, *plan, err);
+        if (st != KVDEC_OK) {
+            delete plan;
+            return fail(st, err);
+        }
+    } catch (const std::bad_alloc&) {
+        delete plan;
+        return fail(KVDEC_E_NOMEM, "host allocation failed while planning");
+    }
+    *out = plan;
+    if (workspace_bytes) *workspace_bytes = plan->workspace_bytes;
+    return KVDEC_OK;
+}
+
+int kvdec_plan_cells(const kvdec_plan_t* plan, int32_t* cells_out, int64_t* offsets_out, int64_t* n_entries) {
+    if (!plan || !n_entries) return fail(KVDEC_E_INVALID, "plan and n_entries must be non-null");
+    *n_entries = (int64_t)plan->cells.size();
+    if (cells_out && !plan->cells.empty()) std::memcpy(cells_out, plan->cells.data(), plan->cells.size() * 4);
+    if (offsets_out) {
+        for (int s = 0; s <= plan->n_slots; ++s)
+            offsets_out[s] = plan->indirect ? plan->cells_off[s] : 0;
+    }
+    return KVDEC_OK;
+}
+
+int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info) {
+    if (!plan || !info) return fail(KVDEC_E_INVALID, "plan and info must be non-null");
+    info->n_slots = plan->n_slots;
+    info->group = plan->group;
+    info->n_workgroups = plan->n_workgroups;
+    info->tiles_per_split = plan->max_tiles_per_split;
+    info->n_tiles = plan->n_tiles;
+    info->n_entries = (int64_t)plan->cells.size();
+    info->n_tail_chunks = plan->n_tail_chunks;
+    info->workspace_bytes = (int64_t)plan->workspace_bytes;
+    return KVDEC_OK;
+}
+
+int kvdec_plan_splits(const kvdec_plan_t* plan, int64_t* splits_out, int64_t* n_splits) {
+    if (!plan || !n_splits) return fail(KVDEC_E_INVALID, "plan and n_splits must be non-null");
+    *n_splits = plan->n_workgroups;
+    if (!splits_out) return KVDEC_OK;
+    int64_t i = 0;
+    for (int s = 0; s < plan->n_slots; ++s) {
+        const kvdec::SlotArg& sa = plan->slots[s];
+        for (int g = 0; g < plan->n_kv_heads; ++g)
+            for (int sp = 0; sp < sa.n_splits; ++sp) {
+                const int64_t t0 = (int64_t)sp * sa.n_tiles / sa.n_splits;
+                const int64_t t1 = (int64_t)(sp + 1) * sa.n_tiles / sa.n_splits;
+                splits_out[4 * i + 0] = s;
+                splits_out[4 * i + 1] = g;
+                splits_out[4 * i + 2] = t0;
+                splits_out[4 * i + 3] = t1 - t0;
+                ++i;
+            }
+    }
+    return KVDEC_OK;
+}
+
+void kvdec_plan_free(kvdec_plan_t* plan) { delete plan; }
+
+int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, size_t workspace_bytes, void* stream,
+                 void* copy_stream) {
+    g_last_error.clear();
+    if (!plan || !io) return fail(KVDEC_E_INVALID, "plan and io must be non-null");
+    const kvdec_plan_t& p = *plan;
+    const int D = p.head_dim;
+    if (!workspace || workspace_bytes < p.workspace_bytes)
+        return fail(KVDEC_E_WORKSPACE, "workspace needs " + std::to_string(p.workspace_bytes) + " bytes");
+    if (!aligned(workspace, 256)) return fail(KVDEC_E_INVALID, "workspace must be 256-byte aligned");
+    if (!io->q || !aligned(io->q, 8)) return fail(KVDEC_E_INVALID, "q must be non-null and 8-byte aligned");
+    if (!io->k || !io->v) return fail(KVDEC_E_INVALID, "k and v must be non-null");
+    const int64_t krow = kvdec::row_bytes(p.k_type, D), vrow = kvdec::row_bytes(p.v_type, D);
+    const int64_t k_cs = io->k_cell_stride ? io->k_cell_stride : krow * p.n_kv_heads;
+    const int64_t k_hs = io->k_head_stride ? io->k_head_stride : krow;
+    const int64_t v_cs = io->v_cell_stride ? io->v_cell_stride : vrow * p.n_kv_heads;
+    const int64_t v_hs = io->v_head_stride ? io->v_head_stride : vrow;
+    const size_t kal = p.k_type == KVDEC_Q4_B32 ? 8 : 16, val = p.v_type == KVDEC_Q4_B32 ? 8 : 16;
+    if (!aligned(io->k, kal) || k_cs % (int64_t)kal || k_hs % (int64_t)kal || k_cs < 0 || k_hs < 0)
+        return fail(KVDEC_E_INVALID, "k pointer and strides must be non-negative multiples of the row load size");
+    if (!aligned(io->v, val) || v_cs % (int64_t)val || v_hs % (int64_t)val || v_cs < 0 || v_hs < 0)
+        return fail(KVDEC_E_INVALID, "v pointer and strides must be non-negative multiples of the row load size");
+    if (kvdec::is_scaled(p.k_type) && (!io->k_scales || !aligned(io->k_scales, 2)))
+        return fail(KVDEC_E_INVALID, "k_scales required (2-byte aligned) for block-scaled K");
+    if (kvdec::is_scaled(p.v_type) && (!io->v_scales || !aligned(io->v_scales, 2)))
+        return fail(KVDEC_E_INVALID, "v_scales required (2-byte aligned) for block-scaled V");
+    if (p.indirect && !io->plan_cells) return fail(KVDEC_E_INVALID, "indirect plan needs plan_cells on the device");
+    const bool any_part = io->part_m || io->part_l || io->part_o;
+    const bool all_part = io->part_m && io->part_l && io->part_o;
+    if (any_part && !all_part) return fail(KVDEC_E_INVALID, "part_m, part_l and part_o go together");
+    if (!io->out && !all_part) return fail(KVDEC_E_INVALID, "give out or the partial triple");
+    if (p.has_tail) {
+        if (!io->k_tail || !io->v_tail) return fail(KVDEC_E_INVALID, "the plan has a tail: k_tail and v_tail needed");
+        if ((kvdec::is_scaled(p.k_type) && !io->k_tail_scales) || (kvdec::is_scaled(p.v_type) && !io->v_tail_scales))
+            return fail(KVDEC_E_INVALID, "tail scales needed for block-scaled kinds");
+    }
+    if (!kvdec::split_instance_exists(D, p.group, p.k_type, p.v_type))
+        return fail(KVDEC_E_UNSUPPORTED, "no kernel for this configuration");
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    kvdec::SplitArgs a;
+    common_args(p, *io, a);
+    a.k = static_cast<const uint8_t*>(io->k);
+    a.v = static_cast<const uint8_t*>(io->v);
+    a.ks = static_cast<const uint16_t*>(io->k_scales);
+    a.vs = static_cast<const uint16_t*>(io->v_scales);
+    a.k_cs = k_cs;
+    a.k_hs = k_hs;
+    a.v_cs = v_cs;
+    a.v_hs = v_hs;
+    a.plan = p.indirect ? io->plan_cells : nullptr;
+    a.capacity = p.capacity;
+    a.part = reinterpret_cast<float*>(ws + p.off_parts);
+    a.tickets = reinterpret_cast<uint32_t*>(ws + p.off_tickets);
+    a.n_slots = p.n_slots;
+    a.slot_base = 0;
+    a.n_workgroups = p.n_workgroups;
+    for (int s = 0; s < p.n_slots; ++s) a.slot[s] = p.slots[s];
+    float* acc[2] = {nullptr, nullptr};
+    if (p.has_tail) {
+        acc[0] = reinterpret_cast<float*>(ws + p.off_acc0);
+        acc[1] = reinterpret_cast<float*>(ws + p.off_acc1);
+        a.acc_out = acc[0];
+    }
+
+    if (!p.has_tail) {
+        const int e = kvdec::launch_split(D, p.group, p.k_type, p.v_type, a, stream);
+        if (e != hipSuccess) return device_fail((hipError_t)e, "split kernel launch");
+        return KVDEC_OK;
+    }
+
+    // ---- resident window + pinned-host tail.
+    // The window launch writes each tailed slot's partial to acc0; then every
+    // tail chunk is copied host -> device into a ring slot on copy_stream and
+    // attended on `stream`, its last workgroup merging the running partial
+    // (acc0 <-> acc1 ping-pong) and, on the slot's last chunk, writing the
+    // outputs.  Ring reuse is ordered by events: the copy into a ring slot
+    // waits until the kernel that read the slot's previous chunk has finished.
+    hipStream_t cs = static_cast<hipStream_t>(copy_stream ? copy_stream : stream);
+    hipStream_t ks = static_cast<hipStream_t>(stream);
+    const int depth = p.ring_depth;
+    hipEvent_t ev_start = nullptr, ev_landed[16] = {}, ev_free[16] = {};
+    auto destroy = [&]() {
+        if (ev_start) (void)hipEventDestroy(ev_start);
+        for (int i = 0; i < depth; ++i) {
+            if (ev_landed[i]) (void)hipEventDestroy(ev_landed[i]);
+            if (ev_free[i]) (void)hipEventDestroy(ev_free[i]);
+        }
+    };
+    hipError_t e = hipEventCreateWithFlags(&ev_start, hipEventDisableTiming);
+    for (int i = 0; i < depth && e == hipSuccess; ++i) {
+        e = hipEventCreateWithFlags(&ev_landed[i], hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_free[i], hipEventDisableTiming);
+    }
+    if (e != hipSuccess) {
+        destroy();
+        return device_fail(e, "hipEventCreate");
+    }
+    // Copies start only after all work already on `stream` (which may still
+    // read the ring through an earlier call).
+    e = hipEventRecord(ev_start, ks);
+    if (e == hipSuccess && cs != ks) e = hipStreamWaitEvent(cs, ev_start, 0);
+    if (e != hipSuccess) {
+        destroy();
+        return device_fail(e, "stream ordering");
+    }
+    int le = kvdec::launch_split(D, p.group, p.k_type, p.v_type, a, stream);
+    if (le != hipSuccess) {
+        destroy();
+        return device_fail((hipError_t)le, "window kernel launch");
+    }
+
+    const int64_t krow_b = kvdec::row_bytes(p.k_type, D) * p.n_kv_heads;
+    const int64_t vrow_b = kvdec::row_bytes(p.v_type, D) * p.n_kv_heads;
+    const int64_t srow_b = (int64_t)(D / kvdec::kBlock) * 2 * p.n_kv_heads;
+    const uint8_t* hk = static_cast<const uint8_t*>(io->k_tail);
+    const uint8_t* hv = static_cast<const uint8_t*>(io->v_tail);
+    const uint8_t* hks = static_cast<const uint8_t*>(io->k_tail_scales);
+    const uint8_t* hvs = static_cast<const uint8_t*>(io->v_tail_scales);
+    int64_t chunk_no = 0;
+    for (int s = 0; s < p.n_slots && e == hipSuccess; ++s) {
+        const int64_t n = p.tail_n[s];
+        const int64_t n_chunks = (n + p.chunk_cells - 1) / p.chunk_cells;
+        for (int64_t c = 0; c < n_chunks; ++c, ++chunk_no) {
+            const int r = (int)(chunk_no % depth);
+            uint8_t* slot = ws + p.off_ring + (size_t)r * p.ring_slot_bytes;
+            const int64_t c0 = p.tail_begin[s] + c * p.chunk_cells;
+            const int64_t nc = std::min<int64_t>(p.chunk_cells, n - c * p.chunk_cells);
+            if (chunk_no >= depth) e = hipStreamWaitEvent(cs, ev_free[r], 0);
+            if (e == hipSuccess)
+                e = hipMemcpyAsync(slot + p.ring_k, hk + c0 * krow_b, nc * krow_b, hipMemcpyHostToDevice, cs);
+            if (e == hipSuccess)
+                e = hipMemcpyAsync(slot + p.ring_v, hv + c0 * vrow_b, nc * vrow_b, hipMemcpyHostToDevice, cs);
+            if (e == hipSuccess && kvdec::is_scaled(p.k_type))
+                e = hipMemcpyAsync(slot + p.ring_ks, hks + c0 * srow_b, nc * srow_b, hipMemcpyHostToDevice, cs);
+            if (e == hipSuccess && kvdec::is_scaled(p.v_type))
+                e = hipMemcpyAsync(slot + p.ring_vs, hvs + c0 * srow_b, nc * srow_b, hipMemcpyHostToDevice, cs);
+            if (e == hipSuccess) e = hipEventRecord(ev_landed[r], cs);
+            if (e == hipSuccess && cs != ks) e = hipStreamWaitEvent(ks, ev_landed[r], 0);
+            if (e != hipSuccess) break;
+
+            kvdec::SplitArgs t;
+            common_args(p, *io, t);
+            t.k = slot + p.ring_k;
+            t.v = slot + p.ring_v;
+            t.ks = reinterpret_cast<const uint16_t*>(slot + p.ring_ks);
+            t.vs = reinterpret_cast<const uint16_t*>(slot + p.ring_vs);
+            t.k_hs = kvdec::row_bytes(p.k_type, D);
+            t.k_cs = krow_b;
+            t.v_hs = kvdec::row_bytes(p.v_type, D);
+            t.v_cs = vrow_b;
+            t.plan = nullptr;
+            t.capacity = nc;
+            t.part = a.part;
+            t.tickets = a.tickets;
+            t.n_slots = 1;
+            t.slot_base = s;
+            const int32_t tiles = (int32_t)((nc + kvdec::kTile - 1) / kvdec::kTile);
+            const int32_t splits = std::max<int32_t>(1, (tiles + p.chunk_tiles_per_split - 1) / p.chunk_tiles_per_split);
+            t.slot[0].first = 0;
+            t.slot[0].n = nc;
+            t.slot[0].n_tiles = tiles;
+            t.slot[0].n_splits = splits;
+            t.slot[0].wg_begin = 0;
+            t.slot[0].part_begin = 0;
+            t.slot[0].to_acc = (c + 1 < n_chunks) ? 1 : 0;
+            t.n_workgroups = splits * p.n_kv_heads;
+            t.acc_in = acc[c % 2];
+            t.acc_out = acc[(c + 1) % 2];
+            le = kvdec::launch_split(D, p.group, p.k_type, p.v_type, t, stream);
+            if (le != hipSuccess) {
+                e = (hipError_t)le;
+                break;
+            }
+            e = hipEventRecord(ev_free[r], ks);
+        }
+    }
+    destroy();
+    if (e != hipSuccess) return device_fail(e, "tail streaming");
+    return KVDEC_OK;
+}
+
+int kvdec_merge(int32_t n_parts, const kvdec_partial* parts, int64_t n_rows, int32_t head_dim, float* out, float* lse,
+                float* merged_m, float* merged_l, float* merged_o, void* stream) {
+    g_last_error.clear();
+    if (n_parts < 1 || n_parts > kvdec::kMergeMaxParts || !parts)
+        return fail(KVDEC_E_INVALID, "n_parts must be in 1..64 with a parts array");
+    if (n_rows < 0 || n_rows > 0x7fffffff || head_dim < 1 || head_dim > 1024)
+        return fail(KVDEC_E_INVALID, "n_rows must be in 0..2^31-1 and head_dim in 1..1024");
+    const bool any_m = merged_m || merged_l || merged_o;
+    const bool all_m = merged_m && merged_l && merged_o;
+    if (any_m && !all_m) return fail(KVDEC_E_INVALID, "merged_m, merged_l and merged_o go together");
+    if (!out && !lse && !all_m) return fail(KVDEC_E_INVALID, "no output given");
+    kvdec::MergeArgs a;
+    std::memset(&a, 0, sizeof(a));
+    for (int i = 0; i < n_parts; ++i) {
+        if (!parts[i].m || !parts[i].l || !parts[i].o) return fail(KVDEC_E_INVALID, "partial with a null pointer");
+        a.m[i] = parts[i].m;
+        a.l[i] = parts[i].l;
+        a.o[i] = parts[i].o;
+    }
+    a.n_parts = n_parts;
+    a.head_dim = head_dim;
+    a.n_rows = n_rows;
+    a.out = out;
+    a.lse = lse;
+    a.mm = merged_m;
+    a.ml = merged_l;
+    a.mo = merged_o;
+    if (n_rows == 0) return KVDEC_OK;
+    const int e = kvdec::launch_merge(a, stream);
+    if (e != hipSuccess) return device_fail((hipError_t)e, "merge kernel launch");
+    return KVDEC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// Internal declarations shared by the planner, the host runtime and the HIP
+// kernels of libkvdec.  Not part of the public C ABI (include/kvdec.h).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvdec.h"
+
+#ifdef __cplusplus
+#include <string>
+#include <vector>
+#endif
+
+namespace kvdec {
+
+constexpr int kTile = KVDEC_TILE_CELLS;  // cells per tile / per physical record
+constexpr int kBlock = 32;               // elements sharing one f16 scale
+constexpr int kThreads = 256;            // threads per split workgroup (4 waves)
+constexpr int kMaxGroup = 8;             // largest compiled GQA group
+constexpr int kMergeMaxParts = 64;       // kvdec_merge fan-in
+
+// Bytes of one stored (cell, KV head) row of codes.
+inline constexpr int64_t row_bytes(int type, int head_dim) {
+    return type == KVDEC_F16 ? 2 * (int64_t)head_dim : type == KVDEC_Q8_B32 ? (int64_t)head_dim : (int64_t)head_dim / 2;
+}
+inline constexpr bool is_scaled(int type) { return type != KVDEC_F16; }
+
+// Per-slot launch description, passed to the split kernel by value.
+struct SlotArg {
+    int64_t first;     // contiguous: first cell; indirect: first plan entry
+    int64_t n;         // contiguous: occupied cells; indirect: plan entries
+    int32_t n_tiles;   // ceil(n / 128)
+    int32_t n_splits;  // splits per KV head (>= 1)
+    int32_t wg_begin;  // first workgroup of this slot (n_kv_heads * n_splits of them)
+    int32_t part_begin;  // first partial record of this slot
+    int32_t to_acc;    // 1: the slot's result goes to acc_out (more partials follow)
+    int32_t pad;
+};
+
+// Kernel arguments of one split launch (fits the 4 KiB kernarg segment).
+struct SplitArgs {
+    const float* q;          // [slots][Hq][D] fp32 (row of slot s: q + (slot_base + s) * Hq * D)
+    const uint8_t* k;        // codes
+    const uint8_t* v;
+    const uint16_t* ks;      // f16 scales, dense [cell][Hkv][D/32]
+    const uint16_t* vs;
+    int64_t k_cs, k_hs;      // byte strides (cell, head) of K rows
+    int64_t v_cs, v_hs;
+    const int32_t* plan;     // indirect entries, or null for contiguous cells
+    int64_t capacity;        // cells addressable through k / v (indirect bound check)
+    float* part;             // partial records [part][G][D + 2]: m2[G], l[G], o[G][D]
+    uint32_t* tickets;       // one per (slot, KV head)
+    float* out;              // [slots][Hq][D] or null
+    float* lse;              // [slots][Hq] or null
+    float* pm;               // whole-call partial (m natural units, l, o) or null
+    float* pl;
+    float* po;
+    const float* acc_in;     // running partial merged in by the last workgroup, or null
+    float* acc_out;          // running partial written for slots with to_acc
+    int32_t acc_rows;        // rows of a running partial: m2 [rows], l [rows], o [rows][D]
+    int32_t pad0;
+    float scale_log2;        // scale * log2(e)
+    int32_t n_slots;         // slots in this launch
+    int32_t slot_base;       // index of slot 0 of this launch in q / out / lse / p*
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t n_workgroups;
+    SlotArg slot[KVDEC_MAX_SLOTS];
+};
+
+struct MergeArgs {
+    const float* m[kMergeMaxParts];
+    const float* l[kMergeMaxParts];
+    const float* o[kMergeMaxParts];
+    int32_t n_parts;
+    int32_t head_dim;
+    int64_t n_rows;
+    float* out;
+    float* lse;
+    float* mm;
+    float* ml;
+    float* mo;
+};
+
+// Kernel launchers (kernels.hip).  Return a hipError_t value.
+int launch_split(int head_dim, int group, int k_type, int v_type, const SplitArgs& a, void* stream);
+int launch_merge(const MergeArgs& a, void* stream);
+bool split_instance_exists(int head_dim, int group, int k_type, int v_type);
+
+}  // namespace kvdec
+
+#ifdef __cplusplus
+// The plan object behind the opaque kvdec_plan_t.
+struct kvdec_plan {
+    int32_t n_q_heads = 0, n_kv_heads = 0, head_dim = 0, n_slots = 0, group = 0;
+    int32_t k_type = 0, v_type = 0;
+    float scale = 0.f;
+    int64_t capacity = 0;
+    bool indirect = false;
+    std::vector<kvdec::SlotArg> slots;
+    int32_t n_workgroups = 0;
+    int32_t n_part_records = 0;
+    int32_t max_tiles_per_split = 0;
+    int64_t n_tiles = 0;
+    std::vector<int32_t> cells;      // indirect entries
+    std::vector<int64_t> cells_off;  // [n_slots + 1]
+
+    // Tail: per slot, host cell range and chunking.
+    bool has_tail = false;
+    std::vector<int64_t> tail_begin, tail_n;
+    int64_t tail_capacity = 0;
+    int64_t chunk_cells = 0;
+    int32_t ring_depth = 0;
+    int32_t chunk_tiles_per_split = 1;
+    int32_t chunk_splits = 0;        // splits per KV head of a full chunk
+    int64_t n_tail_chunks = 0;
+
+    // Workspace layout (byte offsets, 256-aligned).
+    // acc0 / acc1: running partials (ping-pong) of the window + tail chain.
+    size_t off_tickets = 0, off_parts = 0, off_acc0 = 0, off_acc1 = 0, off_ring = 0;
+    int32_t n_part_capacity = 0;     // partial records the parts region holds
+    size_t ring_slot_bytes = 0, ring_k = 0, ring_v = 0, ring_ks = 0, ring_vs = 0;
+    size_t workspace_bytes = 0;
+};
+
+namespace kvdec {
+// Host-only planning (plan.cpp).  Returns a status code; on failure `err`
+// holds a message.
+int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::string& err);
+}  // namespace kvdec
+#endif

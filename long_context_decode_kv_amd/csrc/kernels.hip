@@ -1,0 +1,606 @@
+// HIP kernels of libkvdec for gfx950 (MI355X): the split-KV decode kernel
+// and the log-sum-exp merge kernel.
+//
+// Split kernel.  One workgroup (4 waves) streams a contiguous range of
+// 128-cell tiles of one (slot, KV head), in steps where each lane holds 4
+// cells and each wave a contiguous run of cells.  R consecutive lanes share
+// one cell and split its head_dim
+// elements into R slices of D/R; every 16-byte (8-byte for 4-bit rows) load
+// of a wave covers whole 128-byte lines of consecutive cells, so the KV
+// stream is read with coalesced 128-bit loads.  The G query rows of the KV
+// head's group are held in every lane (f16-packed, its D/R slice only), so
+// each K row fetched once serves all G query heads ("KVARN KV Performance
+// optimizations", "What was implemented" item 6: decoded K/V reused across
+// query rows).  Scores are reduced over the R lanes of a cell with DPP
+// moves; each group of lanes that shares a cell stream keeps its own online
+// softmax state (m, l, o), and the states are merged at the end of the split
+// with the log-sum-exp rule, first across the wave, then across the 4 waves
+// through LDS.
+//
+// Partials are written as (m2 = running max in log2 units, l, o).  When a
+// (slot, KV head) has several splits, the last workgroup to finish (atomic
+// ticket in the workspace) merges all of them and writes the output, so one
+// launch does the whole evaluation -- the partials carry their max and sum
+// in the same pass and nothing is recomputed ("Rolling-KV -- overflow
+// throughput evaluations (consolidated)", section 3: the log-sum-exp channel
+// replaced a per-tile recompute).
+
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace kvdec {
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kNegInf = -__builtin_inff();
+// Softmax weights are formed as 2^(s - m + kPOff) so that, when they are
+// rounded to f16 for packed dot products, weights down to 2^-29 of the
+// maximum stay normal f16 numbers; l and o carry the same factor, which is
+// removed when a partial leaves the workgroup.
+constexpr float kPOff = 15.0f;
+constexpr float kPOffInv = 1.0f / 32768.0f;
+
+__device__ __forceinline__ h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each group of R consecutive lanes; every lane receives its group's sum.
+template <int R>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (R >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+    if constexpr (R >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+    if constexpr (R >= 8) x += dpp<0x141>(x);  // row_half_mirror
+    if constexpr (R >= 16) x += dpp<0x140>(x); // row_mirror
+    if constexpr (R >= 32) x += __shfl_xor(x, 16);
+    if constexpr (R >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Storage formats: a lane reads its d-slice of a row in chunks of at most 16
+// bytes; EPC elements per chunk (a divisor of the 32-element scale block).
+template <int T, int DL>
+struct Fmt;
+template <int DL>
+struct Fmt<KVDEC_F16, DL> {
+    static constexpr int EPC = DL < 8 ? DL : 8;
+    static constexpr int CB = 2 * EPC;
+    static constexpr bool scaled = false;
+};
+template <int DL>
+struct Fmt<KVDEC_Q8_B32, DL> {
+    static constexpr int EPC = DL < 16 ? DL : 16;
+    static constexpr int CB = EPC;
+    static constexpr bool scaled = true;
+};
+template <int DL>
+struct Fmt<KVDEC_Q4_B32, DL> {
+    static constexpr int EPC = DL < 16 ? DL : 16;
+    static constexpr int CB = EPC / 2;
+    static constexpr bool scaled = true;
+};
+
+template <int CB>
+struct Chunk {
+    uint32_t w[CB / 4];
+};
+
+template <int CB>
+__device__ __forceinline__ Chunk<CB> load_chunk(const uint8_t* p) {
+    Chunk<CB> c;
+    if constexpr (CB == 16) {
+        const uint4 x = *reinterpret_cast<const uint4*>(p);
+        c.w[0] = x.x;
+        c.w[1] = x.y;
+        c.w[2] = x.z;
+        c.w[3] = x.w;
+    } else if constexpr (CB == 8) {
+        const uint2 x = *reinterpret_cast<const uint2*>(p);
+        c.w[0] = x.x;
+        c.w[1] = x.y;
+    } else {
+        static_assert(CB == 4, "chunk size");
+        c.w[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+    return c;
+}
+
+template <int CB>
+__device__ __forceinline__ Chunk<CB> zero_chunk() {
+    Chunk<CB> c;
+#pragma unroll
+    for (int i = 0; i < CB / 4; ++i) c.w[i] = 0;
+    return c;
+}
+
+// Stored codes of one chunk -> pairs (element 2i, element 2i+1) as f16, exactly.
+// int8 code x: the byte x ^ 0x80 = x + 128 becomes the low byte of the f16
+// 0x64__ = 1024 + (x + 128); subtracting 1152 leaves x.  4-bit code u: the
+// nibble becomes the low byte of 0x64__ = 1024 + u; subtracting 1032 leaves
+// u - 8.  Element 2i of a 4-bit row is the low nibble of byte i.
+template <int T, int CB, int NP>
+__device__ __forceinline__ void to_pairs(const Chunk<CB>& c, h2 (&p)[NP]) {
+    constexpr int NW = CB / 4;
+    if constexpr (T == KVDEC_F16) {
+        static_assert(NP == NW, "pairs");
+#pragma unroll
+        for (int i = 0; i < NW; ++i) p[i] = as_h2(c.w[i]);
+    } else if constexpr (T == KVDEC_Q8_B32) {
+        static_assert(NP == 2 * NW, "pairs");
+        const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const uint32_t x = c.w[i] ^ 0x80808080u;
+            p[2 * i] = as_h2(__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u)) - bias;
+            p[2 * i + 1] = as_h2(__builtin_amdgcn_perm(0x64646464u, x, 0x04030402u)) - bias;
+        }
+    } else {
+        static_assert(NP == 4 * NW, "pairs");
+        const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const uint32_t lo = c.w[i] & 0x0F0F0F0Fu;
+            const uint32_t hi = (c.w[i] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + b) << 16) | (uint32_t)b;
+                p[4 * i + b] = as_h2(__builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u) - bias;
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// Lane geometry.  Per-lane d-slice DL: 16 elements for groups up to 5, 8
+// above (register budget).  R lanes per cell, CPW cells per wave per load,
+// NB cells per lane per step, so a workgroup step covers 4 * CPW * NB cells.
+template <int D, int G>
+struct Geo {
+    static constexpr int DL = (G <= 5) ? 16 : 8;
+    static constexpr int R = D / DL;
+    static constexpr int CPW = 64 / R;
+    static constexpr int NB = 4;
+    static constexpr int STEP = 4 * CPW * NB;
+    static_assert(R >= 4 && R <= 32, "lane geometry");
+};
+
+// Final or running-partial output of one (row, d) after the merge.
+__device__ __forceinline__ void emit(const SplitArgs& a, int to_acc, int64_t row, int d, int D, float M2, float L,
+                                     float O) {
+    if (to_acc) {
+        float* acc = a.acc_out;
+        if (d == 0) {
+            acc[row] = M2;
+            acc[a.acc_rows + row] = L;
+        }
+        acc[2 * (int64_t)a.acc_rows + row * D + d] = O;
+        return;
+    }
+    const bool empty = !(L > 0.f);
+    if (a.out) a.out[row * D + d] = empty ? 0.f : O / L;
+    if (d == 0) {
+        if (a.lse) a.lse[row] = empty ? kNegInf : (M2 + log2f(L)) * kLn2;
+        if (a.pm) {
+            a.pm[row] = empty ? kNegInf : M2 * kLn2;
+            a.pl[row] = L;
+        }
+    }
+    if (a.po) a.po[row * D + d] = O;
+}
+
+// Merge of two log2-domain partials (M2a, La, Oa) and (M2b, Lb, Ob).
+__device__ __forceinline__ void merge2(float& M, float& L, float& O, float mb, float lb, float ob) {
+    const float mn = fmaxf(M, mb);
+    const float fa = (M == kNegInf) ? 0.f : exp2_fast(M - mn);
+    const float fb = (mb == kNegInf) ? 0.f : exp2_fast(mb - mn);
+    L = L * fa + lb * fb;
+    O = O * fa + ob * fb;
+    M = mn;
+}
+
+template <int D, int G, int KT, int VT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void split_kernel(const SplitArgs a) {
+    using Gm = Geo<D, G>;
+    constexpr int DL = Gm::DL, R = Gm::R, CPW = Gm::CPW, NCW = Gm::NB, STEP = Gm::STEP;
+    using FK = Fmt<KT, DL>;
+    using FV = Fmt<VT, DL>;
+    constexpr int NCK = DL / FK::EPC;  // K chunks per lane per cell
+    constexpr int NCV = DL / FV::EPC;  // V chunks per lane per cell
+    static_assert(NCK >= 1 && NCV >= 1 && NCK * FK::EPC == DL && NCV * FV::EPC == DL, "chunking");
+    constexpr int NB = D / kBlock;     // scales per row
+
+    __shared__ float sm_m[4][G];
+    __shared__ float sm_l[4][G];
+    __shared__ float sm_o[4][G][D];
+    __shared__ int sm_last;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int sub = lane % R;
+    const int cl = lane / R;
+
+    // Which (slot, KV head, split) this workgroup owns.
+    const int wg = blockIdx.x;
+    int s = 0;
+    while (s + 1 < a.n_slots && a.slot[s + 1].wg_begin <= wg) ++s;
+    const SlotArg sa = a.slot[s];
+    const int local = wg - sa.wg_begin;
+    const int g = local / sa.n_splits;
+    const int split = local - g * sa.n_splits;
+    const int t0 = (int)(((int64_t)split * sa.n_tiles) / sa.n_splits);
+    const int t1 = (int)(((int64_t)(split + 1) * sa.n_tiles) / sa.n_splits);
+    const int hq0 = g * G;  // first query head of the group
+    const int64_t row0 = (int64_t)(a.slot_base + s) * a.n_q_heads + hq0;
+
+    // Query rows of the group, f16 pairs, this lane's K d-slice only.
+    h2 qh[G][DL / 2];
+    {
+        const float* qp = a.q + row0 * D;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+            for (int c = 0; c < NCK; ++c) {
+                const int e = (c * R + sub) * FK::EPC;
+#pragma unroll
+                for (int i = 0; i < FK::EPC / 2; ++i) {
+                    const float2 x = *reinterpret_cast<const float2*>(qp + h * D + e + 2 * i);
+                    qh[h][c * (FK::EPC / 2) + i] = h2{(_Float16)x.x, (_Float16)x.y};
+                }
+            }
+        }
+    }
+
+    float m[G], l[G], o[G][DL];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = kNegInf;
+        l[h] = 0.f;
+#pragma unroll
+        for (int i = 0; i < DL; ++i) o[h][i] = 0.f;
+    }
+
+    const uint8_t* kbase = a.k + (int64_t)g * a.k_hs;
+    const uint8_t* vbase = a.v + (int64_t)g * a.v_hs;
+    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+
+    const int64_t tile_end = (int64_t)t1 * kTile;
+    const int64_t pos_end = tile_end < sa.n ? tile_end : sa.n;
+    for (int64_t base = (int64_t)t0 * kTile; base < pos_end; base += STEP) {
+        // Cells of this lane in the step.
+        int64_t cell[NCW];
+        bool valid[NCW];
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) {
+            const int64_t pos = base + (wave * NCW + j) * CPW + cl;  // position in the slot
+            if (a.plan) {
+                const bool in = pos < pos_end;
+                const int64_t c = in ? (int64_t)a.plan[sa.first + pos] : -1;
+                valid[j] = c >= 0 && c < a.capacity;
+                cell[j] = valid[j] ? c : 0;
+            } else {
+                valid[j] = pos < pos_end;
+                cell[j] = sa.first + (valid[j] ? pos : 0);
+            }
+        }
+
+        // Loads: K and V chunks (and scales) of all NCW cells, issued together.
+        Chunk<FK::CB> kc[NCW][NCK];
+        Chunk<FV::CB> vc[NCW][NCV];
+        float kd[NCW][NCK], vd[NCW][NCV];
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) {
+            const uint8_t* kr = kbase + cell[j] * a.k_cs;
+            const uint8_t* vr = vbase + cell[j] * a.v_cs;
+#pragma unroll
+            for (int c = 0; c < NCK; ++c)
+                kc[j][c] = valid[j] ? load_chunk<FK::CB>(kr + (c * R + sub) * FK::CB) : zero_chunk<FK::CB>();
+#pragma unroll
+            for (int c = 0; c < NCV; ++c)
+                vc[j][c] = valid[j] ? load_chunk<FV::CB>(vr + (c * R + sub) * FV::CB) : zero_chunk<FV::CB>();
+            if constexpr (FK::scaled) {
+#pragma unroll
+                for (int c = 0; c < NCK; ++c) {
+                    const int blk = ((c * R + sub) * FK::EPC) / kBlock;
+                    kd[j][c] = valid[j] ? half_bits_to_float(a.ks[(cell[j] * a.n_kv_heads + g) * NB + blk]) : 0.f;
+                }
+            }
+            if constexpr (FV::scaled) {
+#pragma unroll
+                for (int c = 0; c < NCV; ++c) {
+                    const int blk = ((c * R + sub) * FV::EPC) / kBlock;
+                    vd[j][c] = valid[j] ? half_bits_to_float(a.vs[(cell[j] * a.n_kv_heads + g) * NB + blk]) : 0.f;
+                }
+            }
+        }
+
+        // Scores (log2 units).
+        float sc[NCW][G];
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) {
+            float acc[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) acc[h] = 0.f;
+#pragma unroll
+            for (int c = 0; c < NCK; ++c) {
+                h2 kp[FK::EPC / 2];
+                to_pairs<KT>(kc[j][c], kp);
+                if constexpr (FK::scaled) {
+                    float part[G];
+#pragma unroll
+                    for (int h = 0; h < G; ++h) part[h] = 0.f;
+#pragma unroll
+                    for (int i = 0; i < FK::EPC / 2; ++i)
+#pragma unroll
+                        for (int h = 0; h < G; ++h)
+                            part[h] = __builtin_amdgcn_fdot2(kp[i], qh[h][c * (FK::EPC / 2) + i], part[h], false);
+#pragma unroll
+                    for (int h = 0; h < G; ++h) acc[h] = fmaf(part[h], kd[j][c], acc[h]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < FK::EPC / 2; ++i)
+#pragma unroll
+                        for (int h = 0; h < G; ++h)
+                            acc[h] = __builtin_amdgcn_fdot2(kp[i], qh[h][c * (FK::EPC / 2) + i], acc[h], false);
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float full = group_sum<R>(acc[h]);
+                sc[j][h] = valid[j] ? full * a.scale_log2 : kNegInf;
+            }
+        }
+
+        // Online softmax update for the tile.
+        float p[NCW][G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float mt = sc[0][h];
+#pragma unroll
+            for (int j = 1; j < NCW; ++j) mt = fmaxf(mt, sc[j][h]);
+            const float mn = fmaxf(m[h], mt);
+            const float alpha = (mn == kNegInf) ? 1.f : exp2_fast(m[h] - mn);
+            l[h] *= alpha;
+#pragma unroll
+            for (int i = 0; i < DL; ++i) o[h][i] *= alpha;
+            m[h] = mn;
+#pragma unroll
+            for (int j = 0; j < NCW; ++j) p[j][h] = (sc[j][h] == kNegInf) ? 0.f : exp2_fast(sc[j][h] - mn + kPOff);
+        }
+
+        // P.V
+        if constexpr (VT == KVDEC_F16) {
+            // Pairs of cells: (V[A][d], V[B][d]) . (pA, pB) in one packed dot.
+#pragma unroll
+            for (int jp = 0; jp < NCW / 2; ++jp) {
+                const int A = 2 * jp, B = 2 * jp + 1;
+                h2 pp[G];
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    pp[h] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p[A][h], p[B][h]));
+                    l[h] = __builtin_amdgcn_fdot2(pp[h], ones, l[h], false);
+                }
+#pragma unroll
+                for (int c = 0; c < NCV; ++c) {
+#pragma unroll
+                    for (int i = 0; i < FV::CB / 4; ++i) {
+                        const h2 lo = as_h2(__builtin_amdgcn_perm(vc[B][c].w[i], vc[A][c].w[i], 0x05040100u));
+                        const h2 hi = as_h2(__builtin_amdgcn_perm(vc[B][c].w[i], vc[A][c].w[i], 0x07060302u));
+                        const int dd = c * FV::EPC + 2 * i;
+#pragma unroll
+                        for (int h = 0; h < G; ++h) {
+                            o[h][dd] = __builtin_amdgcn_fdot2(lo, pp[h], o[h][dd], false);
+                            o[h][dd + 1] = __builtin_amdgcn_fdot2(hi, pp[h], o[h][dd + 1], false);
+                        }
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NCW; ++j) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) l[h] += p[j][h];
+#pragma unroll
+                for (int c = 0; c < NCV; ++c) {
+                    h2 vp[FV::EPC / 2];
+                    to_pairs<VT>(vc[j][c], vp);
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        const float pd = p[j][h] * vd[j][c];
+#pragma unroll
+                        for (int i = 0; i < FV::EPC / 2; ++i) {
+                            o[h][c * FV::EPC + 2 * i] = fmaf((float)vp[i].x, pd, o[h][c * FV::EPC + 2 * i]);
+                            o[h][c * FV::EPC + 2 * i + 1] = fmaf((float)vp[i].y, pd, o[h][c * FV::EPC + 2 * i + 1]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+
+    // Merge the cell streams of the wave (lanes with the same sub).
+#pragma unroll
+    for (int mask = R; mask < 64; mask <<= 1) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float mo = __shfl_xor(m[h], mask);
+            const float lo = __shfl_xor(l[h], mask);
+            const float mn = fmaxf(m[h], mo);
+            const float fa = (m[h] == kNegInf) ? 0.f : exp2_fast(m[h] - mn);
+            const float fb = (mo == kNegInf) ? 0.f : exp2_fast(mo - mn);
+            l[h] = l[h] * fa + lo * fb;
+#pragma unroll
+            for (int i = 0; i < DL; ++i) o[h][i] = o[h][i] * fa + __shfl_xor(o[h][i], mask) * fb;
+            m[h] = mn;
+        }
+    }
+    if (cl == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            if (sub == 0) {
+                sm_m[wave][h] = m[h];
+                sm_l[wave][h] = l[h] * kPOffInv;
+            }
+#pragma unroll
+            for (int c = 0; c < NCV; ++c)
+#pragma unroll
+                for (int i = 0; i < FV::EPC; ++i) sm_o[wave][h][(c * R + sub) * FV::EPC + i] = o[h][c * FV::EPC + i] * kPOffInv;
+        }
+    }
+    __syncthreads();
+
+    // Merge the 4 waves: thread -> (h, d).  Result of this split in log2 units.
+    const int n_splits = sa.n_splits;
+    const bool single = (n_splits == 1);
+    float* rec = a.part + (int64_t)(sa.part_begin + g * n_splits + split) * G * (D + 2);
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+        const int h = idx / D, d = idx - h * D;
+        float M = sm_m[0][h], L = sm_l[0][h], O = sm_o[0][h][d];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) merge2(M, L, O, sm_m[w][h], sm_l[w][h], sm_o[w][h][d]);
+        if (single) {
+            if (a.acc_in) {
+                const int64_t row = row0 + h;
+                merge2(M, L, O, a.acc_in[row], a.acc_in[a.acc_rows + row], a.acc_in[2 * (int64_t)a.acc_rows + row * D + d]);
+            }
+            emit(a, sa.to_acc, row0 + h, d, D, M, L, O);
+        } else {
+            if (d == 0) {
+                rec[h] = M;
+                rec[G + h] = L;
+            }
+            rec[2 * G + h * D + d] = O;
+        }
+    }
+    if (single) return;
+
+    // Last workgroup of the (slot, KV head) merges every split.
+    __threadfence();
+    __syncthreads();
+    uint32_t* ticket = a.tickets + (int64_t)(a.slot_base + s) * a.n_kv_heads + g;
+    if (tid == 0) {
+        const uint32_t prev = atomicAdd(ticket, 1u);
+        sm_last = (prev == (uint32_t)(n_splits - 1));
+    }
+    __syncthreads();
+    if (!sm_last) return;
+    __threadfence();
+    const float* base = a.part + (int64_t)(sa.part_begin + g * n_splits) * G * (D + 2);
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+        const int h = idx / D, d = idx - h * D;
+        float M = kNegInf, L = 0.f, O = 0.f;
+        for (int sp = 0; sp < n_splits; ++sp) {
+            const float* r = base + (int64_t)sp * G * (D + 2);
+            merge2(M, L, O, r[h], r[G + h], r[2 * G + h * D + d]);
+        }
+        if (a.acc_in) {
+            const int64_t row = row0 + h;
+            merge2(M, L, O, a.acc_in[row], a.acc_in[a.acc_rows + row], a.acc_in[2 * (int64_t)a.acc_rows + row * D + d]);
+        }
+        emit(a, sa.to_acc, row0 + h, d, D, M, L, O);
+    }
+    if (tid == 0) atomicExch(ticket, 0u);
+}
+
+// kvdec_merge: one workgroup per row, one thread per element of head_dim.
+__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
+    const int64_t row = blockIdx.x;
+    for (int d = threadIdx.x; d < a.head_dim; d += blockDim.x) {
+        float M = kNegInf;
+        for (int p = 0; p < a.n_parts; ++p) M = fmaxf(M, a.m[p][row]);
+        float L = 0.f, O = 0.f;
+        if (M != kNegInf) {
+            for (int p = 0; p < a.n_parts; ++p) {
+                const float mp = a.m[p][row];
+                if (mp == kNegInf) continue;
+                const float f = __expf(mp - M);
+                L += a.l[p][row] * f;
+                O += a.o[p][row * a.head_dim + d] * f;
+            }
+        }
+        const bool empty = !(L > 0.f);
+        if (a.out) a.out[row * a.head_dim + d] = empty ? 0.f : O / L;
+        if (a.mo) a.mo[row * a.head_dim + d] = O;
+        if (d == 0) {
+            if (a.lse) a.lse[row] = empty ? kNegInf : M + __logf(L);
+            if (a.mm) {
+                a.mm[row] = empty ? kNegInf : M;
+                a.ml[row] = L;
+            }
+        }
+    }
+}
+
+template <int D, int G, int KT, int VT>
+int launch_one(const SplitArgs& a, void* stream) {
+    hipLaunchKernelGGL((split_kernel<D, G, KT, VT>), dim3(a.n_workgroups), dim3(kThreads), 0, (hipStream_t)stream, a);
+    return (int)hipGetLastError();
+}
+
+using LaunchFn = int (*)(const SplitArgs&, void*);
+
+template <int D, int KT, int VT>
+LaunchFn pick_g(int g) {
+    switch (g) {
+        case 1: return &launch_one<D, 1, KT, VT>;
+        case 2: return &launch_one<D, 2, KT, VT>;
+        case 3: return &launch_one<D, 3, KT, VT>;
+        case 4: return &launch_one<D, 4, KT, VT>;
+        case 5: return &launch_one<D, 5, KT, VT>;
+        case 6: return &launch_one<D, 6, KT, VT>;
+        case 7: return &launch_one<D, 7, KT, VT>;
+        case 8: return &launch_one<D, 8, KT, VT>;
+        default: return nullptr;
+    }
+}
+
+template <int D>
+LaunchFn pick_types(int g, int kt, int vt) {
+    // Same storage kind for K and V.
+    if (kt != vt) return nullptr;
+    switch (kt) {
+        case KVDEC_F16: return pick_g<D, KVDEC_F16, KVDEC_F16>(g);
+        case KVDEC_Q8_B32: return pick_g<D, KVDEC_Q8_B32, KVDEC_Q8_B32>(g);
+        case KVDEC_Q4_B32: return pick_g<D, KVDEC_Q4_B32, KVDEC_Q4_B32>(g);
+        default: return nullptr;
+    }
+}
+
+LaunchFn pick(int head_dim, int g, int kt, int vt) {
+    switch (head_dim) {
+        case 64: return pick_types<64>(g, kt, vt);
+        case 128: return pick_types<128>(g, kt, vt);
+        case 256: return pick_types<256>(g, kt, vt);
+        default: return nullptr;
+    }
+}
+
+}  // namespace
+
+bool split_instance_exists(int head_dim, int group, int k_type, int v_type) {
+    return pick(head_dim, group, k_type, v_type) != nullptr;
+}
+
+int launch_split(int head_dim, int group, int k_type, int v_type, const SplitArgs& a, void* stream) {
+    LaunchFn f = pick(head_dim, group, k_type, v_type);
+    if (!f) return (int)hipErrorInvalidValue;
+    return f(a, stream);
+}
+
+int launch_merge(const MergeArgs& a, void* stream) {
+    const int threads = a.head_dim >= 256 ? 256 : (a.head_dim >= 64 ? ((a.head_dim + 63) / 64) * 64 : 64);
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)a.n_rows), dim3(threads), 0, (hipStream_t)stream, a);
+    return (int)hipGetLastError();
+}
+
+}  // namespace kvdec

@@ -1,0 +1,268 @@
+// Host-only planner of libkvdec: validation, the record-grouped compact plan
+// of indirect cell lists, the split decomposition over the compute units and
+// the workspace layout.  No HIP dependency.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "internal.h"
+
+namespace kvdec {
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compact read plan of one slot's raw cell list ("KVARN KV Performance
+// optimizations", "What was implemented" items 3 and 4): holes (-1) dropped,
+// other negatives and cells >= capacity rejected, duplicates filtered with a
+// capacity-sized bitmap (first occurrence kept), kept cells grouped by their
+// physical 128-cell record, records in ascending order, one 128-entry segment
+// per record with -1 in the positions that were not kept.  `bitmap` is
+// capacity bits, all zero on entry and on return.
+int compact_slot(const int32_t* raw, int64_t n, int64_t capacity, std::vector<uint64_t>& bitmap,
+                 std::vector<int64_t>& records, std::vector<int32_t>& out, std::string& err) {
+    records.clear();
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t c = raw[i];
+        if (c == -1) continue;
+        if (c < -1 || c >= capacity) {
+            err = "cell " + std::to_string(c) + " at raw index " + std::to_string(i) + " outside [0, capacity)";
+            std::fill(bitmap.begin(), bitmap.end(), 0);
+            return KVDEC_E_RANGE;
+        }
+        uint64_t& word = bitmap[(size_t)c >> 6];
+        const uint64_t bit = 1ull << (c & 63);
+        if (word & bit) continue;  // duplicate: first occurrence already kept
+        // A record is listed when its first cell is kept.
+        const int64_t rec = c / kTile;
+        bool rec_seen = false;
+        for (int k = 0; k < kTile / 64; ++k)
+            if (bitmap[(size_t)rec * (kTile / 64) + k]) rec_seen = true;
+        if (!rec_seen) records.push_back(rec);
+        word |= bit;
+    }
+    std::sort(records.begin(), records.end());
+    for (int64_t rec : records) {
+        for (int k = 0; k < kTile; ++k) {
+            const int64_t c = rec * kTile + k;
+            const bool kept = (bitmap[(size_t)c >> 6] >> (c & 63)) & 1;
+            out.push_back(kept ? (int32_t)c : -1);
+        }
+        for (int k = 0; k < kTile / 64; ++k) bitmap[(size_t)rec * (kTile / 64) + k] = 0;
+    }
+    return KVDEC_OK;
+}
+
+}  // namespace
+
+int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::string& err) {
+    // ---- shape
+    if (p.n_q_heads < 1 || p.n_kv_heads < 1 || p.n_q_heads % p.n_kv_heads != 0) {
+        err = "n_q_heads must be a positive multiple of n_kv_heads";
+        return KVDEC_E_INVALID;
+    }
+    const int group = p.n_q_heads / p.n_kv_heads;
+    if (group > 16) {
+        err = "group size n_q_heads / n_kv_heads must be at most 16";
+        return KVDEC_E_INVALID;
+    }
+    if (p.head_dim != 64 && p.head_dim != 128 && p.head_dim != 256) {
+        err = "head_dim must be 64, 128 or 256";
+        return KVDEC_E_INVALID;
+    }
+    if (p.n_slots < 1) {
+        err = "n_slots must be >= 1";
+        return KVDEC_E_INVALID;
+    }
+    if (p.n_slots > KVDEC_MAX_SLOTS) {
+        err = "n_slots above KVDEC_MAX_SLOTS";
+        return KVDEC_E_UNSUPPORTED;
+    }
+    for (int t : {p.k_type, p.v_type})
+        if (t != KVDEC_F16 && t != KVDEC_Q8_B32 && t != KVDEC_Q4_B32) {
+            err = "k_type / v_type must be KVDEC_F16, KVDEC_Q8_B32 or KVDEC_Q4_B32";
+            return KVDEC_E_INVALID;
+        }
+    if (!std::isfinite(p.scale)) {
+        err = "scale must be finite";
+        return KVDEC_E_INVALID;
+    }
+    if (p.capacity_cells < 0 || p.tiles_per_split < 0 || n_cu < 1) {
+        err = "capacity_cells, tiles_per_split must be >= 0 and n_cu >= 1";
+        return KVDEC_E_INVALID;
+    }
+    const bool indirect = p.cells != nullptr;
+    if (indirect && !p.cells_off) {
+        err = "indirect mode needs cells_off";
+        return KVDEC_E_INVALID;
+    }
+    if (!indirect && !p.n_occupied) {
+        err = "contiguous mode needs n_occupied";
+        return KVDEC_E_INVALID;
+    }
+    const bool has_tail = p.n_tail != nullptr;
+    if (has_tail && indirect) {
+        err = "a host tail is supported with contiguous cells only";
+        return KVDEC_E_UNSUPPORTED;
+    }
+    if (group > kMaxGroup) {
+        err = "no kernel for group sizes above 8";
+        return KVDEC_E_UNSUPPORTED;
+    }
+    if (!split_instance_exists(p.head_dim, group, p.k_type, p.v_type)) {
+        err = "no kernel for this (head_dim, group, k_type, v_type)";
+        return KVDEC_E_UNSUPPORTED;
+    }
+
+    plan.n_q_heads = p.n_q_heads;
+    plan.n_kv_heads = p.n_kv_heads;
+    plan.head_dim = p.head_dim;
+    plan.n_slots = p.n_slots;
+    plan.group = group;
+    plan.k_type = p.k_type;
+    plan.v_type = p.v_type;
+    plan.scale = p.scale;
+    plan.capacity = p.capacity_cells;
+    plan.indirect = indirect;
+    plan.slots.assign(p.n_slots, SlotArg{});
+
+    // ---- cells of each slot
+    if (indirect) {
+        plan.cells_off.assign(p.n_slots + 1, 0);
+        for (int s = 0; s < p.n_slots; ++s) {
+            if (p.cells_off[s] < 0 || p.cells_off[s + 1] < p.cells_off[s]) {
+                err = "cells_off must be non-negative and non-decreasing";
+                return KVDEC_E_INVALID;
+            }
+        }
+        std::vector<uint64_t> bitmap((size_t)ceil_div(std::max<int64_t>(p.capacity_cells, 1), kTile) * (kTile / 64), 0);
+        std::vector<int64_t> records;
+        for (int s = 0; s < p.n_slots; ++s) {
+            const int64_t b = p.cells_off[s], e = p.cells_off[s + 1];
+            const size_t before = plan.cells.size();
+            const int st = compact_slot(p.cells + b, e - b, p.capacity_cells, bitmap, records, plan.cells, err);
+            if (st != KVDEC_OK) {
+                err = "slot " + std::to_string(s) + ": " + err;
+                return st;
+            }
+            plan.slots[s].first = (int64_t)before;
+            plan.slots[s].n = (int64_t)(plan.cells.size() - before);
+            plan.cells_off[s + 1] = (int64_t)plan.cells.size();
+        }
+    } else {
+        for (int s = 0; s < p.n_slots; ++s) {
+            const int64_t b = p.cell_begin ? p.cell_begin[s] : 0;
+            const int64_t n = p.n_occupied[s];
+            if (b < 0 || n < 0 || b + n > p.capacity_cells) {
+                err = "slot " + std::to_string(s) + ": cells [" + std::to_string(b) + ", " + std::to_string(b + n) +
+                      ") outside [0, capacity)";
+                return KVDEC_E_RANGE;
+            }
+            plan.slots[s].first = b;
+            plan.slots[s].n = n;
+        }
+    }
+
+    // ---- split decomposition: tiles of every (slot, KV head) spread over
+    // about two workgroups per compute unit.
+    int64_t total_tiles = 0;
+    for (auto& sa : plan.slots) {
+        const int64_t t = ceil_div(sa.n, kTile);
+        if (t > (1 << 30)) {
+            err = "slot too long";
+            return KVDEC_E_UNSUPPORTED;
+        }
+        sa.n_tiles = (int32_t)t;
+        total_tiles += t * p.n_kv_heads;
+    }
+    plan.n_tiles = total_tiles;
+    int64_t tps = p.tiles_per_split;
+    if (tps == 0) tps = std::max<int64_t>(1, ceil_div(total_tiles, 2 * (int64_t)n_cu));
+    int64_t wgs = 0;
+    plan.max_tiles_per_split = 0;
+    for (auto& sa : plan.slots) {
+        const int64_t ns = std::max<int64_t>(1, ceil_div(sa.n_tiles, tps));
+        sa.n_splits = (int32_t)ns;
+        sa.wg_begin = (int32_t)wgs;
+        sa.part_begin = (int32_t)wgs;
+        sa.to_acc = 0;
+        wgs += ns * p.n_kv_heads;
+        if (wgs > (1ll << 30)) {
+            err = "too many workgroups";
+            return KVDEC_E_UNSUPPORTED;
+        }
+        plan.max_tiles_per_split = std::max<int32_t>(plan.max_tiles_per_split, (int32_t)ceil_div(sa.n_tiles, ns));
+    }
+    plan.n_workgroups = (int32_t)wgs;
+    plan.n_part_records = (int32_t)wgs;
+
+    // ---- host tail
+    plan.has_tail = has_tail;
+    int64_t part_capacity = wgs;
+    if (has_tail) {
+        plan.tail_capacity = p.tail_capacity_cells;
+        plan.chunk_cells = p.tail_chunk_cells ? p.tail_chunk_cells : 2048;
+        plan.ring_depth = p.tail_ring_depth ? p.tail_ring_depth : 4;
+        if (plan.chunk_cells < kTile || plan.chunk_cells % kTile != 0 || plan.ring_depth < 2 || plan.ring_depth > 16 ||
+            plan.tail_capacity < 0) {
+            err = "tail_chunk_cells must be a positive multiple of 128 and tail_ring_depth in 2..16";
+            return KVDEC_E_INVALID;
+        }
+        plan.tail_begin.assign(p.n_slots, 0);
+        plan.tail_n.assign(p.n_slots, 0);
+        plan.n_tail_chunks = 0;
+        for (int s = 0; s < p.n_slots; ++s) {
+            const int64_t b = p.tail_begin ? p.tail_begin[s] : 0;
+            const int64_t n = p.n_tail[s];
+            if (b < 0 || n < 0 || b + n > plan.tail_capacity) {
+                err = "slot " + std::to_string(s) + ": tail cells outside [0, tail_capacity_cells)";
+                return KVDEC_E_RANGE;
+            }
+            plan.tail_begin[s] = b;
+            plan.tail_n[s] = n;
+            const int64_t chunks = ceil_div(n, plan.chunk_cells);
+            plan.n_tail_chunks += chunks;
+            plan.slots[s].to_acc = chunks > 0 ? 1 : 0;
+        }
+        const int64_t chunk_tiles = plan.chunk_cells / kTile;
+        const int64_t ctps = std::max<int64_t>(1, ceil_div(chunk_tiles * p.n_kv_heads, 2 * (int64_t)n_cu));
+        plan.chunk_tiles_per_split = (int32_t)ctps;
+        plan.chunk_splits = (int32_t)std::max<int64_t>(1, ceil_div(chunk_tiles, ctps));
+        part_capacity = std::max<int64_t>(part_capacity, (int64_t)plan.chunk_splits * p.n_kv_heads);
+    }
+    plan.n_part_capacity = (int32_t)part_capacity;
+
+    // ---- workspace layout
+    const size_t D = (size_t)p.head_dim;
+    size_t off = 0;
+    plan.off_tickets = off;
+    off = align_up(off + sizeof(uint32_t) * (size_t)p.n_slots * p.n_kv_heads, 256);
+    plan.off_parts = off;
+    off = align_up(off + sizeof(float) * (size_t)part_capacity * group * (D + 2), 256);
+    if (has_tail) {
+        const size_t rows = (size_t)p.n_slots * p.n_q_heads;
+        plan.off_acc0 = off;
+        off = align_up(off + sizeof(float) * rows * (D + 2), 256);
+        plan.off_acc1 = off;
+        off = align_up(off + sizeof(float) * rows * (D + 2), 256);
+        const size_t cc = (size_t)plan.chunk_cells * p.n_kv_heads;
+        plan.ring_k = 0;
+        size_t r = align_up(cc * (size_t)row_bytes(p.k_type, p.head_dim), 256);
+        plan.ring_v = r;
+        r = align_up(r + cc * (size_t)row_bytes(p.v_type, p.head_dim), 256);
+        plan.ring_ks = r;
+        if (is_scaled(p.k_type)) r = align_up(r + cc * (D / kBlock) * 2, 256);
+        plan.ring_vs = r;
+        if (is_scaled(p.v_type)) r = align_up(r + cc * (D / kBlock) * 2, 256);
+        plan.ring_slot_bytes = r;
+        plan.off_ring = off;
+        off += r * (size_t)plan.ring_depth;
+    }
+    plan.workspace_bytes = align_up(std::max<size_t>(off, 256), 256);
+    return KVDEC_OK;
+}
+
+}  // namespace kvdec

@@ -169,3 +169,32 @@ def device_q(seed, n_slots, n_q_heads, head_dim, device="cuda"):
     import torch
     g = device_generator(seed, device)
     return torch.randn((n_slots, n_q_heads, head_dim), generator=g, device=device, dtype=torch.float32)
+
+
+def device_quant_cache(seed, kind, n_cells, n_kv_heads, head_dim, device="cuda"):
+    """x ~ N(0, 1) drawn on the device and encoded per 32-element block with
+    the same rule as ``encode_blocks``: returns (codes, scale bits as int16)."""
+    import torch
+    g = device_generator(seed, device)
+    nb = head_dim // BLOCK
+    row = head_dim if kind == Q8_B32 else head_dim // 2
+    codes = torch.empty((n_cells, n_kv_heads, row), dtype=torch.int8 if kind == Q8_B32 else torch.uint8,
+                        device=device)
+    scales = torch.empty((n_cells, n_kv_heads, nb), dtype=torch.float16, device=device)
+    step = max(1, (1 << 24) // (n_kv_heads * head_dim))
+    qmax = 127.0 if kind == Q8_B32 else 7.0
+    for c0 in range(0, n_cells, step):
+        n = min(step, n_cells - c0)
+        x = torch.randn((n, n_kv_heads, nb, BLOCK), generator=g, device=device, dtype=torch.float32)
+        d16 = (x.abs().amax(dim=-1) / qmax).to(torch.float16)
+        d32 = d16.to(torch.float32)
+        safe = torch.where(d32 == 0, torch.ones_like(d32), d32)[..., None]
+        t = torch.round(x / safe)
+        t = torch.where(d32[..., None] == 0, torch.zeros_like(t), t)
+        if kind == Q8_B32:
+            codes[c0:c0 + n] = t.clamp(-127, 127).to(torch.int8).reshape(n, n_kv_heads, row)
+        else:
+            u = (t.clamp(-8, 7) + 8).to(torch.uint8).reshape(n, n_kv_heads, row, 2)
+            codes[c0:c0 + n] = u[..., 0] | (u[..., 1] << 4)
+        scales[c0:c0 + n] = d16
+    return codes, scales

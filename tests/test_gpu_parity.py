@@ -1,0 +1,207 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle,
+element by element, max |err| <= 2e-3 on out and lse, on seeded inputs that
+span several tiles and ragged tails, every compiled group size and head_dim,
+f16 / int8 / 4-bit caches, contiguous and indirect (record-grouped, -1 holes)
+cells, empty slots, peaked softmax, partial outputs + kvdec_merge, split-count
+independence, strided layouts and NaN-poisoned workspace / unused cells."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from gpu_cases import Case, check, dev, TOL
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    import torch
+    assert torch.cuda.is_available()
+    from long_context_decode_kv_amd import kvdec
+    return kvdec
+
+
+def test_single_layer_4096(K):
+    """32 query heads, 8 KV heads, head_dim 128, 4096 contiguous f16 cells."""
+    c = Case(1001, 32, 8, 128, occupied=[4096])
+    check(*c.run(K), *c.oracle())
+
+
+def test_ragged_lengths_multi_slot(K):
+    occ = [1, 2, 127, 128, 129, 255, 1000, 4099]
+    begins = [5, 900, 0, 3000, 128, 17, 2000, 1]
+    c = Case(11, 8, 2, 128, occupied=occ, begins=begins)
+    check(*c.run(K), *c.oracle())
+
+
+@pytest.mark.parametrize("d,g", [(64, 1), (64, 4), (64, 8), (128, 1), (128, 2), (128, 3), (128, 5), (128, 6),
+                                 (128, 7), (128, 8), (256, 2), (256, 4), (256, 5), (256, 6), (256, 8)])
+def test_group_sizes_and_head_dims(K, d, g):
+    c = Case(20 + d + g, 2 * g, 2, d, occupied=[700, 1500])
+    check(*c.run(K), *c.oracle())
+
+
+def test_empty_slots(K):
+    c = Case(12, 8, 2, 128, occupied=[0, 300, 0])
+    out, lse = c.run(K)
+    wo, wl = c.oracle()
+    check(out, lse, wo, wl)
+    assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0])) and np.all(np.isneginf(lse[2]))
+
+
+@pytest.mark.parametrize("tps", [1, 2, 7, 100000])
+def test_split_count_only_changes_rounding(K, tps):
+    c = Case(13, 32, 8, 128, occupied=[13100])
+    out, lse = c.run(K, tiles_per_split=tps)
+    check(out, lse, *c.oracle())
+
+
+@pytest.mark.parametrize("kind", [O.Q8_B32, O.Q4_B32])
+def test_quantized_indirect_interleaved(K, kind):
+    """GQA-6, head_dim 256, four slots whose 128-cell records are interleaved,
+    raw lists shuffled with duplicates and holes."""
+    c = Case(30 + kind, 24, 4, 256, kind=kind, indirect_lengths=[3000, 1500, 777, 1], shuffle=True, duplicates=25)
+    check(*c.run(K), *c.oracle())
+
+
+@pytest.mark.parametrize("kind", [O.Q8_B32, O.Q4_B32])
+@pytest.mark.parametrize("d,g", [(128, 4), (128, 8), (64, 2), (256, 6)])
+def test_quantized_contiguous(K, kind, d, g):
+    c = Case(40 + kind + d + g, 2 * g, 2, d, kind=kind, occupied=[1000, 129])
+    check(*c.run(K), *c.oracle())
+
+
+def test_indirect_f16_with_empty_and_single_cells(K):
+    c = Case(14, 16, 4, 128, kind=O.F16, indirect_lengths=[0, 1, 128, 129, 2000], shuffle=True, duplicates=3)
+    out, lse = c.run(K)
+    check(out, lse, *c.oracle())
+    assert np.all(np.isneginf(lse[0]))
+
+
+def test_peaked_softmax(K):
+    """Each KV head's first query head has one cell whose K equals its query
+    (rounded to f16): a dominant weight, as with a retrieved needle."""
+    c = Case(15, 32, 8, 128, occupied=[13100], peaked=True)
+    out, lse = c.run(K)
+    wo, wl = c.oracle()
+    check(out, lse, wo, wl)
+    assert np.max(wl) > 8  # the planted cell dominates
+
+
+def test_partials_merge_to_whole(K):
+    import torch
+    c = Case(16, 32, 8, 128, occupied=[5000])
+    whole_out, whole_lse = c.run(K)
+    # two disjoint ranges -> partials -> kvdec_merge
+    c.upload()
+    res = []
+    for b, n in ((0, 1801), (1801, 3199)):
+        p = K.plan(32, 8, 128, 1, c.capacity, n_occupied=[n], cell_begin=[b], scale=c.scale)
+        parts = (torch.empty(1, 32, device="cuda"), torch.empty(1, 32, device="cuda"),
+                 torch.empty(1, 32, 128, device="cuda"))
+        K.attend(p, c.q_d, c.kc_d, c.vc_d, K.workspace(p), part=parts)
+        res.append(parts)
+    out = torch.empty(1, 32, 128, device="cuda")
+    lse = torch.empty(1, 32, device="cuda")
+    mm, ml, mo = torch.empty(1, 32, device="cuda"), torch.empty(1, 32, device="cuda"), torch.empty(1, 32, 128, device="cuda")
+    K.merge(res, 32, 128, out=out, lse=lse, merged=(mm, ml, mo))
+    torch.cuda.synchronize()
+    wo, wl = c.oracle()
+    check(out.cpu().numpy(), lse.cpu().numpy(), wo, wl)
+    check(out.cpu().numpy(), lse.cpu().numpy(), whole_out, whole_lse, tol=1e-4)
+    # the merged partial reproduces out and lse
+    mo_ = mo.cpu().numpy() / ml.cpu().numpy()[..., None]
+    assert np.max(np.abs(mo_ - wo)) <= TOL
+    assert np.max(np.abs(mm.cpu().numpy() + np.log(ml.cpu().numpy()) - wl)) <= TOL
+    # each partial against the oracle's partial of its range
+    for (b, n), (pm, pl, po) in zip(((0, 1801), (1801, 3199)), res):
+        _, _, op = O.decode_attention(c.q, [((O.F16, c.kc, None), (O.F16, c.vc, None), [np.arange(b, b + n)])], 8,
+                                      c.scale, return_partials=True)
+        m, l, o = op[0]
+        gm, gl, go = pm.cpu().numpy(), pl.cpu().numpy(), po.cpu().numpy()
+        assert np.max(np.abs(gm - m)) <= TOL
+        # l and o are relative to e^m; compare them rescaled to the oracle's m
+        f = np.exp(gm - m)
+        assert np.max(np.abs(gl * f / l - 1)) <= TOL
+        assert np.max(np.abs(go * f[..., None] / l[..., None] - o / l[..., None])) <= TOL
+
+
+def test_merge_empty_identity_and_all_empty(K):
+    import torch
+    rows, d = 5, 64
+    r = np.random.default_rng(3)
+    m = torch.tensor(r.standard_normal(rows), dtype=torch.float32, device="cuda")
+    l = torch.tensor(r.uniform(0.5, 3, rows), dtype=torch.float32, device="cuda")
+    o = torch.tensor(r.standard_normal((rows, d)), dtype=torch.float32, device="cuda")
+    em = torch.full((rows,), float("-inf"), device="cuda")
+    el = torch.zeros(rows, device="cuda")
+    eo = torch.zeros(rows, d, device="cuda")
+    out = torch.empty(rows, d, device="cuda")
+    lse = torch.empty(rows, device="cuda")
+    K.merge([(em, el, eo), (m, l, o), (em, el, eo)], rows, d, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.allclose(out, o / l[:, None], atol=1e-6)
+    assert torch.allclose(lse, m + torch.log(l), atol=1e-6)
+    K.merge([(em, el, eo), (em, el, eo)], rows, d, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_deterministic(K):
+    c = Case(17, 32, 8, 128, occupied=[13100])
+    a = c.run(K)
+    b = c.run(K)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_head_major_strided_layout(K):
+    """The same cache stored [kv head][cell][D] through explicit strides."""
+    import torch
+    c = Case(18, 16, 4, 128, occupied=[3000])
+    want = c.run(K)
+    p = c.plan(K)
+    kh = dev(np.ascontiguousarray(c.kc.transpose(1, 0, 2)))
+    vh = dev(np.ascontiguousarray(c.vc.transpose(1, 0, 2)))
+    out = torch.empty(1, 16, 128, device="cuda")
+    lse = torch.empty(1, 16, device="cuda")
+    K.attend(p, c.q_d, kh, vh, K.workspace(p), out=out, lse=lse, k_cell_stride=256, k_head_stride=256 * c.capacity,
+             v_cell_stride=256, v_head_stride=256 * c.capacity)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), want[0]) and np.array_equal(lse.cpu().numpy(), want[1])
+
+
+def test_nan_poisoned_workspace_and_unused_cells(K):
+    """Partial records start as NaN and every cell outside the attended set
+    holds NaN: nothing of it may reach the output."""
+    import torch
+    c = Case(19, 24, 4, 256, kind=O.F16, indirect_lengths=[900, 300, 77], shuffle=True, duplicates=5)
+    attended = np.zeros(c.capacity, dtype=bool)
+    for cells in c.oracle_cells:
+        attended[cells[cells >= 0]] = True
+    nan16 = np.float16(np.nan).view(np.uint16)
+    c.kc[~attended] = nan16
+    c.vc[~attended] = nan16
+    p = c.plan(K, tiles_per_split=1)
+    ws = K.workspace(p)
+    ws.view(torch.float32)[64:] = float("nan")  # tickets (first bytes) stay zero
+    assert 64 * 4 >= 4 * c.n_slots * c.hkv
+    out, lse = c.run(K, plan=p, ws=ws)
+    check(out, lse, *c.oracle())
+
+
+def test_workspace_reuse_across_plans(K):
+    """One workspace serves consecutive calls with different plans; tickets
+    are back at zero after every call."""
+    import torch
+    c1 = Case(21, 32, 8, 128, occupied=[6000])
+    c2 = Case(22, 32, 8, 128, occupied=[300, 9000])
+    p1, p2 = c1.plan(K, tiles_per_split=1), c2.plan(K, tiles_per_split=3)
+    ws = K.workspace(p1) if p1.workspace_bytes >= p2.workspace_bytes else K.workspace(p2)
+    for _ in range(2):
+        check(*c1.run(K, plan=p1, ws=ws), *c1.oracle())
+        check(*c2.run(K, plan=p2, ws=ws), *c2.oracle())
+    tick = ws[:4 * 2 * 8].view(torch.int32)
+    assert int(tick.abs().sum()) == 0

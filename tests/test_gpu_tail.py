@@ -1,0 +1,101 @@
+"""GPU parity of the resident-window + pinned-host-tail path: the tail is
+streamed through the staging ring in the workspace and merged with the
+window by log-sum-exp; the result must match the float64 oracle over the
+union of cells and the all-resident GPU result over the same cells."""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from gpu_cases import Case, check, dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    import torch
+    assert torch.cuda.is_available()
+    from long_context_decode_kv_amd import kvdec
+    return kvdec
+
+
+def pinned(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    t = torch.empty(a.shape, dtype=torch.from_numpy(a[:0]).dtype, pin_memory=True)
+    t.copy_(torch.from_numpy(a))
+    return t
+
+
+def run_tail(K, c, window, tail, chunk, depth, copy_stream=None):
+    """window: per slot (begin, n) resident cells; tail: per slot (begin, n)
+    cells of the host tail, which holds rows [0, tail_capacity) of the cache."""
+    import torch
+    tail_cap = max(b + n for b, n in tail)
+    p = K.plan(c.hq, c.hkv, c.d, c.n_slots, c.capacity, k_type=c.kind, v_type=c.kind, scale=c.scale,
+               n_occupied=[n for _, n in window], cell_begin=[b for b, _ in window], n_tail=[n for _, n in tail],
+               tail_begin=[b for b, _ in tail], tail_capacity_cells=tail_cap, tail_chunk_cells=chunk,
+               tail_ring_depth=depth)
+    c.upload()
+    hk, hv = pinned(c.kc[:tail_cap]), pinned(c.vc[:tail_cap])
+    hks = None if c.ks is None else pinned(c.ks[:tail_cap])
+    hvs = None if c.vs is None else pinned(c.vs[:tail_cap])
+    ws = K.workspace(p)
+    out = torch.full((c.n_slots, c.hq, c.d), float("nan"), device="cuda")
+    lse = torch.full((c.n_slots, c.hq), float("nan"), device="cuda")
+    K.attend(p, c.q_d, c.kc_d, c.vc_d, ws, out=out, lse=lse, k_scales=c.ks_d, v_scales=c.vs_d, k_tail=hk, v_tail=hv,
+             k_tail_scales=hks, v_tail_scales=hvs, copy_stream=copy_stream)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy(), p
+
+
+@pytest.mark.parametrize("chunk,depth", [(128, 2), (512, 2), (512, 4), (2048, 4)])
+def test_window_plus_tail_equals_resident(K, chunk, depth):
+    import torch
+    ctx = 5000
+    c = Case(51, 32, 8, 128, occupied=[ctx])
+    res_out, res_lse = c.run(K)
+    t = 3217  # oldest cells in the host tail; not a multiple of 128
+    cs = torch.cuda.Stream()
+    out, lse, p = run_tail(K, c, window=[(t, ctx - t)], tail=[(0, t)], chunk=chunk, depth=depth, copy_stream=cs)
+    assert p.info()["n_tail_chunks"] == -(-t // chunk)
+    check(out, lse, *c.oracle())
+    check(out, lse, res_out, res_lse, tol=1e-4)
+
+
+def test_tail_multi_slot_same_stream(K):
+    """Slots with tails of different length, one with no tail and one with an
+    empty window; copies on the compute stream itself."""
+    c = Case(52, 16, 4, 128, occupied=[3000, 2500, 1000, 700], begins=[0, 3000, 5500, 6500])
+    window = [(1000, 2000), (3000, 2500), (6000, 500), (6500, 0)]
+    tail = [(0, 1000), (0, 0), (5500, 500), (6500, 700)]
+    out, lse, _ = run_tail(K, c, window, tail, chunk=256, depth=3)
+    # oracle over the union: window cells + tail cells (same cache rows)
+    cells = [np.concatenate([np.arange(wb, wb + wn), np.arange(tb, tb + tn)]) for (wb, wn), (tb, tn) in zip(window, tail)]
+    wo, wl = O.decode_attention(c.q, [((O.F16, c.kc, None), (O.F16, c.vc, None), cells)], c.hkv, c.scale)
+    check(out, lse, wo, wl)
+
+
+@pytest.mark.parametrize("kind", [O.Q8_B32, O.Q4_B32])
+def test_quantized_tail(K, kind):
+    c = Case(53 + kind, 24, 4, 256, kind=kind, occupied=[3000])
+    out, lse, _ = run_tail(K, c, window=[(1100, 1900)], tail=[(0, 1100)], chunk=384, depth=2)
+    check(out, lse, *c.oracle())
+
+
+def test_tail_call_repeated_on_one_workspace(K):
+    """Back-to-back calls reuse the ring; each must see its own tail."""
+    import torch
+    c1 = Case(54, 32, 8, 128, occupied=[4000])
+    c2 = Case(55, 32, 8, 128, occupied=[4000])
+    outs = []
+    for c in (c1, c2, c1):
+        out, lse, _ = run_tail(K, c, window=[(2500, 1500)], tail=[(0, 2500)], chunk=512, depth=2,
+                               copy_stream=torch.cuda.Stream())
+        outs.append((out, lse))
+    check(*outs[0], *c1.oracle())
+    check(*outs[1], *c2.oracle())
+    assert np.array_equal(outs[0][0], outs[2][0])

@@ -1,0 +1,198 @@
+"""CPU tests of libkvdec's host side: the library loads and exports every
+function include/kvdec.h declares, the planner's compact plan is bit-exact
+against the oracle, the split table covers every tile exactly once, and every
+error path returns its status before any device work (no GPU needed)."""
+
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from long_context_decode_kv_amd import kvdec as K
+from long_context_decode_kv_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "kvdec.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(kvdec_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function():
+    names = _declared_functions()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(K.lib, name), name
+    assert set(names) == set(K.EXPORTED)
+    assert K.version() == 10000
+
+
+def test_strerror_codes():
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert K.lib.kvdec_strerror(code).decode() not in ("", "unknown status")
+    assert K.lib.kvdec_strerror(17).decode() == "unknown status"
+
+
+# ---------------------------------------------------------------- planner
+
+def _plan_cells(lists, capacity, **kw):
+    p = K.plan(24, 4, 256, len(lists), capacity, k_type=K.Q8_B32, v_type=K.Q8_B32, cells=lists, n_cu=256, **kw)
+    return p, p.cells()
+
+
+def test_compact_plan_matches_oracle_hand_cases():
+    lists = [[5, 130, 5, 7, -1, 129], [300, 0, 1, 2, 257], [639, 128, -1, -1, 639], [], [-1, -1]]
+    _, (e, off) = _plan_cells(lists, 640)
+    we, woff = O.compact_plan(lists, 640)
+    assert np.array_equal(e, we) and np.array_equal(off, woff)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_compact_plan_matches_oracle_random(seed):
+    r = synth.rng(100 + seed)
+    lengths = [int(x) for x in r.integers(0, 3000, 5)] + [0, 1, 128]
+    lists, cap = synth.interleaved_record_lists(lengths, r, shuffle=True, duplicates=40)
+    cap += 384  # spare records past the last one
+    p, (e, off) = _plan_cells(lists, cap)
+    we, woff = O.compact_plan(lists, cap)
+    assert np.array_equal(e, we) and np.array_equal(off, woff)
+    info = p.info()
+    assert info["n_entries"] == len(we)
+
+
+def test_compact_plan_gqa6_workload_shape():
+    lists, cap = synth.interleaved_record_lists([131072, 65536, 20000, 777])
+    p, (e, off) = _plan_cells(lists, cap)
+    assert cap == 217600 and len(e) == 217600 and int((e == -1).sum()) == 215
+    assert list(np.diff(off) // 128) == [1024, 512, 157, 7]
+
+
+def _coverage(p, tiles_per_slot, n_kv):
+    sp = p.splits()
+    seen = {}
+    for s, g, t0, nt in sp:
+        for t in range(t0, t0 + nt):
+            key = (int(s), int(g), int(t))
+            assert key not in seen
+            seen[key] = 1
+    want = {(s, g, t) for s, T in enumerate(tiles_per_slot) for g in range(n_kv) for t in range(T)}
+    assert set(seen) == want
+    return sp
+
+
+@pytest.mark.parametrize("tps", [0, 1, 3, 1000])
+def test_split_table_covers_every_tile_once(tps):
+    occ = [13100, 0, 1, 128, 129, 40000]
+    p = K.plan(32, 8, 128, len(occ), 50000, n_occupied=occ, tiles_per_split=tps, n_cu=256)
+    tiles = [-(-n // 128) for n in occ]
+    sp = _coverage(p, tiles, 8)
+    # splits of one (slot, head) differ by at most one tile
+    for s in range(len(occ)):
+        for g in range(8):
+            counts = [int(r[3]) for r in sp if r[0] == s and r[1] == g]
+            assert max(counts) - min(counts) <= 1
+            if tps:
+                assert max(counts) <= max(tps, 1) or tiles[s] == 0
+    info = p.info()
+    assert info["n_workgroups"] == len(sp)
+    assert info["n_tiles"] == sum(tiles) * 8
+
+
+def test_auto_split_fills_device():
+    p = K.plan(32, 8, 128, 1, 16384, n_occupied=[13100], n_cu=256)
+    info = p.info()
+    assert 256 <= info["n_workgroups"] <= 1024
+    p = K.plan(40, 8, 128, 1, 524288, n_occupied=[524288], n_cu=256)
+    info = p.info()
+    assert info["n_workgroups"] == 512 and info["tiles_per_split"] == 64
+
+
+def test_tail_plan_chunks_and_workspace():
+    p = K.plan(32, 8, 128, 1, 40960, n_occupied=[14000], cell_begin=[26960], n_tail=[26960],
+               tail_capacity_cells=26960, tail_chunk_cells=2048, tail_ring_depth=4, n_cu=256)
+    info = p.info()
+    assert info["n_tail_chunks"] == math.ceil(26960 / 2048)
+    # ring of 4 slots x 2048 cells x 8 heads x 256 B for each of K and V
+    assert info["workspace_bytes"] >= 4 * 2 * 2048 * 8 * 256
+
+
+# ---------------------------------------------------------------- errors
+
+def _status(fn):
+    with pytest.raises(K.KvdecError) as ei:
+        fn()
+    return ei.value.status
+
+
+def test_plan_errors():
+    base = dict(n_occupied=[10], n_cu=256)
+    assert _status(lambda: K.plan(32, 7, 128, 1, 100, **base)) == K.E_INVALID          # not a multiple
+    assert _status(lambda: K.plan(34, 2, 128, 1, 100, **base)) == K.E_INVALID          # G = 17
+    assert _status(lambda: K.plan(32, 8, 96, 1, 100, **base)) == K.E_INVALID           # head_dim
+    assert _status(lambda: K.plan(32, 8, 128, 0, 100, **base)) == K.E_INVALID          # no slots
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, k_type=5, **base)) == K.E_INVALID
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, scale=float("nan"), **base)) == K.E_INVALID
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, n_occupied=[101], n_cu=256)) == K.E_RANGE
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, n_occupied=[10], cell_begin=[95], n_cu=256)) == K.E_RANGE
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, cells=[[3, 100]], n_cu=256)) == K.E_RANGE
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, cells=[[3, -2]], n_cu=256)) == K.E_RANGE
+    assert _status(lambda: K.plan(32, 2, 128, 1, 100, **base)) == K.E_UNSUPPORTED      # G = 16
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, k_type=K.Q8_B32, v_type=K.F16, **base)) == K.E_UNSUPPORTED
+    assert _status(lambda: K.plan(32, 8, 128, 65, 100, n_occupied=[1] * 65, n_cu=256)) == K.E_UNSUPPORTED
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, cells=[[1]], n_tail=[1], tail_capacity_cells=1,
+                                  n_cu=256)) == K.E_UNSUPPORTED
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, n_occupied=[1], n_tail=[5], tail_capacity_cells=4,
+                                  n_cu=256)) == K.E_RANGE
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, n_occupied=[1], n_tail=[5], tail_capacity_cells=8,
+                                  tail_chunk_cells=100, n_cu=256)) == K.E_INVALID
+    # the library keeps the message of the last failure
+    assert "tail_chunk_cells" in K.lib.kvdec_last_error().decode()
+
+
+FAKE = 1 << 20  # an aligned address that is never dereferenced: validation fails first
+
+
+def test_attend_validation_before_device_work():
+    p = K.plan(32, 8, 128, 1, 4096, n_occupied=[4096], n_cu=256)
+    ws = (FAKE, p.workspace_bytes)
+    args = dict(out=FAKE, stream=0)
+    assert _status(lambda: K.attend(p, FAKE, FAKE, FAKE, (0, p.workspace_bytes), **args)) == K.E_WORKSPACE
+    assert _status(lambda: K.attend(p, FAKE, FAKE, FAKE, (FAKE, p.workspace_bytes - 1), **args)) == K.E_WORKSPACE
+    assert _status(lambda: K.attend(p, FAKE, FAKE, FAKE, (FAKE + 16, p.workspace_bytes), **args)) == K.E_INVALID
+    assert _status(lambda: K.attend(p, 0, FAKE, FAKE, ws, **args)) == K.E_INVALID            # no q
+    assert _status(lambda: K.attend(p, FAKE, FAKE + 8, FAKE, ws, **args)) == K.E_INVALID     # misaligned k
+    assert _status(lambda: K.attend(p, FAKE, FAKE, FAKE, ws, k_cell_stride=24, **args)) == K.E_INVALID
+    assert _status(lambda: K.attend(p, FAKE, FAKE, FAKE, ws, stream=0)) == K.E_INVALID       # no output
+    assert _status(lambda: K.attend(p, FAKE, FAKE, FAKE, ws, part=(FAKE, FAKE, 0), stream=0)) == K.E_INVALID
+    pq = K.plan(24, 4, 256, 1, 4096, k_type=K.Q8_B32, v_type=K.Q8_B32, n_occupied=[10], n_cu=256)
+    wsq = (FAKE, pq.workspace_bytes)
+    assert _status(lambda: K.attend(pq, FAKE, FAKE, FAKE, wsq, out=FAKE, k_scales=FAKE, stream=0)) == K.E_INVALID
+    pi = K.plan(24, 4, 256, 1, 4096, k_type=K.Q4_B32, v_type=K.Q4_B32, cells=[[1, 2]], n_cu=256)
+    wsi = (FAKE, pi.workspace_bytes)
+    assert _status(lambda: K.attend(pi, FAKE, FAKE, FAKE, wsi, out=FAKE, k_scales=FAKE, v_scales=FAKE, stream=0)) == K.E_INVALID
+    pt = K.plan(32, 8, 128, 1, 4096, n_occupied=[10], n_tail=[10], tail_capacity_cells=10, n_cu=256)
+    wst = (FAKE, pt.workspace_bytes)
+    assert _status(lambda: K.attend(pt, FAKE, FAKE, FAKE, wst, out=FAKE, stream=0)) == K.E_INVALID      # tail arrays missing
+
+
+def test_merge_validation():
+    import ctypes
+    arr = (K.PartialC * 1)()
+    arr[0].m, arr[0].l, arr[0].o = FAKE, FAKE, FAKE
+    f = K.lib.kvdec_merge
+    assert f(0, arr, 4, 128, FAKE, None, None, None, None, None) == K.E_INVALID
+    assert f(65, arr, 4, 128, FAKE, None, None, None, None, None) == K.E_INVALID
+    assert f(1, arr, 4, 0, FAKE, None, None, None, None, None) == K.E_INVALID
+    assert f(1, arr, 4, 128, None, None, None, None, None, None) == K.E_INVALID
+    assert f(1, arr, 4, 128, None, None, FAKE, FAKE, None, None) == K.E_INVALID
+    bad = (K.PartialC * 1)()
+    bad[0].m, bad[0].l, bad[0].o = FAKE, None, FAKE
+    assert f(1, bad, 4, 128, FAKE, None, None, None, None, None) == K.E_INVALID
+    # zero rows: nothing to do, nothing launched
+    assert f(1, arr, 0, 128, FAKE, None, None, None, None, None) == K.OK
+    del ctypes
