@@ -229,7 +229,7 @@ typedef struct kvdec_plan_info {
 
 int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info);
 
-/* Split table: for each workgroup of the resident launch, 4 int64 values
+/* Split table: for each workgroup of the resident launch, in launch order, 4 int64 values
  * (slot, kv head, first tile, tile count).  With splits_out == NULL only
  * *n_splits is written. */
 int kvdec_plan_splits(const kvdec_plan_t* plan, int64_t* splits_out, int64_t* n_splits);

@@ -123,8 +123,8 @@ int kvdec_plan_splits(const kvdec_plan_t* plan, int64_t* splits_out, int64_t* n_
     int64_t i = 0;
     for (int s = 0; s < plan->n_slots; ++s) {
         const kvdec::SlotArg& sa = plan->slots[s];
-        for (int g = 0; g < plan->n_kv_heads; ++g)
-            for (int sp = 0; sp < sa.n_splits; ++sp) {
+        for (int sp = 0; sp < sa.n_splits; ++sp)  // workgroup order: split-major
+            for (int g = 0; g < plan->n_kv_heads; ++g) {
                 const int64_t t0 = (int64_t)sp * sa.n_tiles / sa.n_splits;
                 const int64_t t1 = (int64_t)(sp + 1) * sa.n_tiles / sa.n_splits;
                 splits_out[4 * i + 0] = s;
@@ -169,6 +169,9 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
     const bool all_part = io->part_m && io->part_l && io->part_o;
     if (any_part && !all_part) return fail(KVDEC_E_INVALID, "part_m, part_l and part_o go together");
     if (!io->out && !all_part) return fail(KVDEC_E_INVALID, "give out or the partial triple");
+    if (!aligned(io->out, 16) || !aligned(io->part_o, 16) || !aligned(io->lse, 4) || !aligned(io->part_m, 4) ||
+        !aligned(io->part_l, 4))
+        return fail(KVDEC_E_INVALID, "out and part_o must be 16-byte aligned, lse / part_m / part_l 4-byte aligned");
     if (p.has_tail) {
         if (!io->k_tail || !io->v_tail) return fail(KVDEC_E_INVALID, "the plan has a tail: k_tail and v_tail needed");
         if ((kvdec::is_scaled(p.k_type) && !io->k_tail_scales) || (kvdec::is_scaled(p.v_type) && !io->v_tail_scales))
@@ -190,7 +193,10 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
     a.v_hs = v_hs;
     a.plan = p.indirect ? io->plan_cells : nullptr;
     a.capacity = p.capacity;
-    a.part = reinterpret_cast<float*>(ws + p.off_parts);
+    a.part_o = reinterpret_cast<float*>(ws + p.off_parts);
+    a.part_m = reinterpret_cast<float*>(ws + p.off_parts_m);
+    a.part_l = reinterpret_cast<float*>(ws + p.off_parts_l);
+    a.part_o_bytes = (int64_t)p.parts_o_bytes;
     a.tickets = reinterpret_cast<uint32_t*>(ws + p.off_tickets);
     a.n_slots = p.n_slots;
     a.slot_base = 0;
@@ -291,7 +297,10 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
             t.v_cs = vrow_b;
             t.plan = nullptr;
             t.capacity = nc;
-            t.part = a.part;
+            t.part_o = a.part_o;
+            t.part_m = a.part_m;
+            t.part_l = a.part_l;
+            t.part_o_bytes = a.part_o_bytes;
             t.tickets = a.tickets;
             t.n_slots = 1;
             t.slot_base = s;

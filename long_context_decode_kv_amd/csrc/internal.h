@@ -49,7 +49,10 @@ struct SplitArgs {
     int64_t v_cs, v_hs;
     const int32_t* plan;     // indirect entries, or null for contiguous cells
     int64_t capacity;        // cells addressable through k / v (indirect bound check)
-    float* part;             // partial records [part][G][D + 2]: m2[G], l[G], o[G][D]
+    float* part_o;           // split partial records: o [record][G][D]
+    float* part_m;           //   running max in log2 units [record][G]
+    float* part_l;           //   sum [record][G]
+    int64_t part_o_bytes;    // bytes of the o region (bound of its buffer resource)
     uint32_t* tickets;       // one per (slot, KV head)
     float* out;              // [slots][Hq][D] or null
     float* lse;              // [slots][Hq] or null
@@ -120,6 +123,7 @@ struct kvdec_plan {
     // acc0 / acc1: running partials (ping-pong) of the window + tail chain.
     size_t off_tickets = 0, off_parts = 0, off_acc0 = 0, off_acc1 = 0, off_ring = 0;
     int32_t n_part_capacity = 0;     // partial records the parts region holds
+    size_t off_parts_m = 0, off_parts_l = 0, parts_o_bytes = 0;
     size_t ring_slot_bytes = 0, ring_k = 0, ring_v = 0, ring_ks = 0, ring_vs = 0;
     size_t workspace_bytes = 0;
 };

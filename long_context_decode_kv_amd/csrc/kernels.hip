@@ -29,6 +29,7 @@
 
 #include "internal.h"
 
+
 namespace kvdec {
 namespace {
 
@@ -62,7 +63,36 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Max / sum over the whole wave; every lane receives the result.
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp<0xB1>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    x = fmaxf(x, dpp<0x141>(x));
+    x = fmaxf(x, dpp<0x140>(x));
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Cross-workgroup records.  A split's partial record is read by the last
+// workgroup of its (slot, KV head), which may run on another XCD.  The record
+// is written and read with device-scope relaxed atomic accesses, which the
+// hardware keeps coherent across the XCDs' L2 caches without the whole-L2
+// write-back / invalidate that a device-scope fence costs; the writer waits
+// for its stores to complete before the ticket increment that publishes them.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Storage formats: a lane reads its d-slice of a row in chunks of at most 16
 // bytes; EPC elements per chunk (a divisor of the 32-element scale block).
@@ -174,38 +204,200 @@ struct Geo {
     static_assert(R >= 4 && R <= 32, "lane geometry");
 };
 
-// Final or running-partial output of one (row, d) after the merge.
-__device__ __forceinline__ void emit(const SplitArgs& a, int to_acc, int64_t row, int d, int D, float M2, float L,
-                                     float O) {
+// Merge of two log2-domain partials (M, L, O) <- (mb, lb, ob), 4 columns.
+__device__ __forceinline__ void merge4(float& M, float& L, float4& O, float mb, float lb, float4 ob) {
+    const float mn = fmaxf(M, mb);
+    const float fa = (M == kNegInf) ? 0.f : exp2_fast(M - mn);
+    const float fb = (mb == kNegInf) ? 0.f : exp2_fast(mb - mn);
+    L = L * fa + lb * fb;
+    O.x = O.x * fa + ob.x * fb;
+    O.y = O.y * fa + ob.y * fb;
+    O.z = O.z * fa + ob.z * fb;
+    O.w = O.w * fa + ob.w * fb;
+    M = mn;
+}
+
+// Output of one row's columns d0 .. d0+3 after the merge: the final out /
+// lse / partial triple, or the running partial when more partials follow.
+__device__ __forceinline__ void emit4(const SplitArgs& a, int to_acc, int64_t row, int d0, int D, float M2, float L,
+                                      float4 O) {
     if (to_acc) {
         float* acc = a.acc_out;
-        if (d == 0) {
+        if (d0 == 0) {
             acc[row] = M2;
             acc[a.acc_rows + row] = L;
         }
-        acc[2 * (int64_t)a.acc_rows + row * D + d] = O;
+        *reinterpret_cast<float4*>(acc + 2 * (int64_t)a.acc_rows + row * D + d0) = O;
         return;
     }
     const bool empty = !(L > 0.f);
-    if (a.out) a.out[row * D + d] = empty ? 0.f : O / L;
-    if (d == 0) {
+    if (a.out) {
+        const float4 r = empty ? make_float4(0.f, 0.f, 0.f, 0.f) : make_float4(O.x / L, O.y / L, O.z / L, O.w / L);
+        *reinterpret_cast<float4*>(a.out + row * D + d0) = r;
+    }
+    if (d0 == 0) {
         if (a.lse) a.lse[row] = empty ? kNegInf : (M2 + log2f(L)) * kLn2;
         if (a.pm) {
             a.pm[row] = empty ? kNegInf : M2 * kLn2;
             a.pl[row] = L;
         }
     }
-    if (a.po) a.po[row * D + d] = O;
+    if (a.po) *reinterpret_cast<float4*>(a.po + row * D + d0) = O;
 }
 
-// Merge of two log2-domain partials (M2a, La, Oa) and (M2b, Lb, Ob).
-__device__ __forceinline__ void merge2(float& M, float& L, float& O, float mb, float lb, float ob) {
-    const float mn = fmaxf(M, mb);
-    const float fa = (M == kNegInf) ? 0.f : exp2_fast(M - mn);
-    const float fb = (mb == kNegInf) ? 0.f : exp2_fast(mb - mn);
-    L = L * fa + lb * fb;
-    O = O * fa + ob * fb;
-    M = mn;
+// Running partial handed in from an earlier launch (window + tail chain).
+__device__ __forceinline__ void merge_acc_in(const SplitArgs& a, int64_t row, int d0, int D, float& M, float& L,
+                                             float4& O) {
+    if (!a.acc_in) return;
+    const float4 ob = *reinterpret_cast<const float4*>(a.acc_in + 2 * (int64_t)a.acc_rows + row * D + d0);
+    merge4(M, L, O, a.acc_in[row], a.acc_in[a.acc_rows + row], ob);
+}
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const SplitArgs& a) {
+    return __builtin_amdgcn_make_buffer_rsrc(a.part_o, (short)0, (int)a.part_o_bytes, 0x00020000);
+}
+// Device-coherent (sc1) 16-byte store / load of a split record's o columns.
+__device__ __forceinline__ void st_dev4(__amdgpu_buffer_rsrc_t r, int64_t off_bytes, float4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(f4v{v.x, v.y, v.z, v.w}, r, (int)off_bytes, 0, 0x10);
+}
+__device__ __forceinline__ float4 ld_dev4(__amdgpu_buffer_rsrc_t r, int64_t off_bytes) {
+    const f4v v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off_bytes, 0, 0x10);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+// Last-workgroup merge of the n_splits partial records of one (slot, KV
+// head).  The records were written by workgroups that may sit on other
+// XCDs, so every load here goes out to memory; the merge is organised so
+// that each chunk of splits costs one round trip: a thread first issues the
+// loads of all its o columns for the chunk, then the (m, l) loads, and only
+// then waits.  Thread -> (float4 column, split residue class); the running
+// maximum and sums per head are kept in LDS across chunks.
+template <int D, int G>
+__device__ void merge_splits(const SplitArgs& a, const SlotArg& sa, int s, int g, int64_t row0, int n_splits) {
+    constexpr int NV = G * D / 4;                           // float4 columns of o
+    constexpr int TS = NV >= kThreads ? 1 : kThreads / NV;  // threads per column
+    constexpr int COLS = (NV + kThreads - 1) / kThreads;    // columns per thread
+    constexpr int UB = 16 / COLS;                           // splits per thread per chunk
+    constexpr int SPC = 64 < UB * TS ? 64 : UB * TS;        // splits per chunk (one per lane)
+    __shared__ float f_m[64 * G];
+    __shared__ float run_m[G], run_l[G], scale_old[G];
+    __shared__ float4 red[TS > 1 ? kThreads : 1];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = tid % (NV < kThreads ? NV : kThreads);
+    const int cls = tid / (NV < kThreads ? NV : kThreads);  // threads with cls >= TS idle
+    const __amdgpu_buffer_rsrc_t rs = part_rsrc(a);
+    const int64_t rec0 = sa.part_begin + (int64_t)g * n_splits;
+
+    float4 acc[COLS];
+#pragma unroll
+    for (int c = 0; c < COLS; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (tid < G) {
+        run_m[tid] = kNegInf;
+        run_l[tid] = 0.f;
+    }
+    for (int sp0 = 0; sp0 < n_splits; sp0 += SPC) {
+        const int nsp = (n_splits - sp0) < SPC ? (n_splits - sp0) : SPC;
+        float4 x[COLS][UB];
+#pragma unroll
+        for (int c = 0; c < COLS; ++c) {
+            const int v = col + c * kThreads;
+#pragma unroll
+            for (int u = 0; u < UB; ++u) {
+                const int sp = cls + u * TS;
+                x[c][u] = (cls < TS && v < NV && sp < nsp)
+                              ? ld_dev4(rs, ((rec0 + sp0 + sp) * (G * D) + 4 * v) * 4)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+        // (m, l) of the chunk: wave w takes heads w and w + 4, one split per lane.
+        float mv[2], lv[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int h = wave + 4 * hh;
+            mv[hh] = kNegInf;
+            lv[hh] = 0.f;
+            if (h < G && lane < nsp) {
+                mv[hh] = ld_dev(a.part_m + (rec0 + sp0 + lane) * G + h);
+                lv[hh] = ld_dev(a.part_l + (rec0 + sp0 + lane) * G + h);
+            }
+        }
+        __syncthreads();  // the previous chunk is done with f_m / scale_old
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int h = wave + 4 * hh;
+            if (h >= G) continue;  // uniform over the wave
+            const float mo = run_m[h];
+            const float mn = fmaxf(mo, wave_max(mv[hh]));
+            const float f = (mv[hh] == kNegInf) ? 0.f : exp2_fast(mv[hh] - mn);
+            const float so = (mo == kNegInf) ? 0.f : exp2_fast(mo - mn);
+            const float ls = wave_sum(lv[hh] * f);
+            if (lane < nsp) f_m[lane * G + h] = f;
+            if (lane == 0) {
+                scale_old[h] = so;
+                run_l[h] = run_l[h] * so + ls;
+                run_m[h] = mn;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < COLS; ++c) {
+            const int v = col + c * kThreads;
+            if (cls >= TS || v >= NV) continue;
+            const int h = (4 * v) / D;
+            const float so = scale_old[h];
+            float4 o = acc[c];
+            o.x *= so;
+            o.y *= so;
+            o.z *= so;
+            o.w *= so;
+#pragma unroll
+            for (int u = 0; u < UB; ++u) {
+                const int sp = cls + u * TS;
+                const float f = sp < nsp ? f_m[sp * G + h] : 0.f;
+                o.x = fmaf(x[c][u].x, f, o.x);
+                o.y = fmaf(x[c][u].y, f, o.y);
+                o.z = fmaf(x[c][u].z, f, o.z);
+                o.w = fmaf(x[c][u].w, f, o.w);
+            }
+            acc[c] = o;
+        }
+    }
+    // combine the TS residue classes of each column
+    if constexpr (TS > 1) {
+        red[tid] = acc[0];
+        __syncthreads();
+        if (cls == 0) {
+            float4 o = acc[0];
+            for (int t = 1; t < TS; ++t) {
+                const float4 y = red[t * NV + col];
+                o.x += y.x;
+                o.y += y.y;
+                o.z += y.z;
+                o.w += y.w;
+            }
+            acc[0] = o;
+        }
+    }
+    if (cls == 0) {
+#pragma unroll
+        for (int c = 0; c < COLS; ++c) {
+            const int v = col + c * kThreads;
+            if (v >= NV) continue;
+            const int h = (4 * v) / D;
+            const int d0 = 4 * v - h * D;
+            float M = run_m[h], L = run_l[h];
+            float4 O = acc[c];
+            merge_acc_in(a, row0 + h, d0, D, M, L, O);
+            emit4(a, sa.to_acc, row0 + h, d0, D, M, L, O);
+        }
+    }
+    if (tid == 0)
+        __hip_atomic_store(a.tickets + (int64_t)(a.slot_base + s) * a.n_kv_heads + g, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int G, int KT, int VT>
@@ -218,10 +410,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     constexpr int NCV = DL / FV::EPC;  // V chunks per lane per cell
     static_assert(NCK >= 1 && NCV >= 1 && NCK * FK::EPC == DL && NCV * FV::EPC == DL, "chunking");
     constexpr int NB = D / kBlock;     // scales per row
+    // Cell streams per wave left after the in-register (DPP) merge step.
+    constexpr bool kDppStep = R <= 8;
+    constexpr int NSW = kDppStep ? CPW / 2 : CPW;
+    constexpr int NS = 4 * NSW;        // streams per workgroup merged through LDS
 
-    __shared__ float sm_m[4][G];
-    __shared__ float sm_l[4][G];
-    __shared__ float sm_o[4][G][D];
+    __shared__ float sm_m[NS][G];
+    __shared__ float sm_l[NS][G];
+    __shared__ __align__(16) float sm_o[NS][G][D];
     __shared__ int sm_last;
 
     const int tid = threadIdx.x;
@@ -236,8 +432,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     while (s + 1 < a.n_slots && a.slot[s + 1].wg_begin <= wg) ++s;
     const SlotArg sa = a.slot[s];
     const int local = wg - sa.wg_begin;
-    const int g = local / sa.n_splits;
-    const int split = local - g * sa.n_splits;
+    // Consecutive workgroups take the same cell range of different KV heads,
+    // so the workgroups resident together read neighbouring bytes of each
+    // cell row.
+    const int split = local / a.n_kv_heads;
+    const int g = local - split * a.n_kv_heads;
     const int t0 = (int)(((int64_t)split * sa.n_tiles) / sa.n_splits);
     const int t1 = (int)(((int64_t)(split + 1) * sa.n_tiles) / sa.n_splits);
     const int hq0 = g * G;  // first query head of the group
@@ -273,58 +472,62 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const uint8_t* kbase = a.k + (int64_t)g * a.k_hs;
     const uint8_t* vbase = a.v + (int64_t)g * a.v_hs;
     const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-
     const int64_t tile_end = (int64_t)t1 * kTile;
     const int64_t pos_end = tile_end < sa.n ? tile_end : sa.n;
-    for (int64_t base = (int64_t)t0 * kTile; base < pos_end; base += STEP) {
-        // Cells of this lane in the step.
-        int64_t cell[NCW];
+
+    // One step: NCW cells per lane.  Buffers of a step in flight.
+    struct Step {
         bool valid[NCW];
+        Chunk<FK::CB> kc[NCW][NCK];
+        Chunk<FV::CB> vc[NCW][NCV];
+        float kd[NCW][NCK], vd[NCW][NCV];
+    };
+
+    // Issue the loads of the step starting at slot position `base`.
+    auto load_step = [&](int64_t base, Step& st) {
+        int64_t cell[NCW];
 #pragma unroll
         for (int j = 0; j < NCW; ++j) {
             const int64_t pos = base + (wave * NCW + j) * CPW + cl;  // position in the slot
             if (a.plan) {
                 const bool in = pos < pos_end;
                 const int64_t c = in ? (int64_t)a.plan[sa.first + pos] : -1;
-                valid[j] = c >= 0 && c < a.capacity;
-                cell[j] = valid[j] ? c : 0;
+                st.valid[j] = c >= 0 && c < a.capacity;
+                cell[j] = st.valid[j] ? c : 0;
             } else {
-                valid[j] = pos < pos_end;
-                cell[j] = sa.first + (valid[j] ? pos : 0);
+                st.valid[j] = pos < pos_end;
+                cell[j] = sa.first + (st.valid[j] ? pos : 0);
             }
         }
-
-        // Loads: K and V chunks (and scales) of all NCW cells, issued together.
-        Chunk<FK::CB> kc[NCW][NCK];
-        Chunk<FV::CB> vc[NCW][NCV];
-        float kd[NCW][NCK], vd[NCW][NCV];
 #pragma unroll
         for (int j = 0; j < NCW; ++j) {
             const uint8_t* kr = kbase + cell[j] * a.k_cs;
             const uint8_t* vr = vbase + cell[j] * a.v_cs;
 #pragma unroll
             for (int c = 0; c < NCK; ++c)
-                kc[j][c] = valid[j] ? load_chunk<FK::CB>(kr + (c * R + sub) * FK::CB) : zero_chunk<FK::CB>();
+                st.kc[j][c] = st.valid[j] ? load_chunk<FK::CB>(kr + (c * R + sub) * FK::CB) : zero_chunk<FK::CB>();
 #pragma unroll
             for (int c = 0; c < NCV; ++c)
-                vc[j][c] = valid[j] ? load_chunk<FV::CB>(vr + (c * R + sub) * FV::CB) : zero_chunk<FV::CB>();
+                st.vc[j][c] = st.valid[j] ? load_chunk<FV::CB>(vr + (c * R + sub) * FV::CB) : zero_chunk<FV::CB>();
             if constexpr (FK::scaled) {
 #pragma unroll
                 for (int c = 0; c < NCK; ++c) {
                     const int blk = ((c * R + sub) * FK::EPC) / kBlock;
-                    kd[j][c] = valid[j] ? half_bits_to_float(a.ks[(cell[j] * a.n_kv_heads + g) * NB + blk]) : 0.f;
+                    st.kd[j][c] = st.valid[j] ? half_bits_to_float(a.ks[(cell[j] * a.n_kv_heads + g) * NB + blk]) : 0.f;
                 }
             }
             if constexpr (FV::scaled) {
 #pragma unroll
                 for (int c = 0; c < NCV; ++c) {
                     const int blk = ((c * R + sub) * FV::EPC) / kBlock;
-                    vd[j][c] = valid[j] ? half_bits_to_float(a.vs[(cell[j] * a.n_kv_heads + g) * NB + blk]) : 0.f;
+                    st.vd[j][c] = st.valid[j] ? half_bits_to_float(a.vs[(cell[j] * a.n_kv_heads + g) * NB + blk]) : 0.f;
                 }
             }
         }
+    };
 
-        // Scores (log2 units).
+    // Scores, online-softmax update and P.V of one loaded step.
+    auto compute_step = [&](const Step& st) {
         float sc[NCW][G];
 #pragma unroll
         for (int j = 0; j < NCW; ++j) {
@@ -334,7 +537,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
             for (int c = 0; c < NCK; ++c) {
                 h2 kp[FK::EPC / 2];
-                to_pairs<KT>(kc[j][c], kp);
+                to_pairs<KT>(st.kc[j][c], kp);
                 if constexpr (FK::scaled) {
                     float part[G];
 #pragma unroll
@@ -345,7 +548,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                         for (int h = 0; h < G; ++h)
                             part[h] = __builtin_amdgcn_fdot2(kp[i], qh[h][c * (FK::EPC / 2) + i], part[h], false);
 #pragma unroll
-                    for (int h = 0; h < G; ++h) acc[h] = fmaf(part[h], kd[j][c], acc[h]);
+                    for (int h = 0; h < G; ++h) acc[h] = fmaf(part[h], st.kd[j][c], acc[h]);
                 } else {
 #pragma unroll
                     for (int i = 0; i < FK::EPC / 2; ++i)
@@ -357,11 +560,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 const float full = group_sum<R>(acc[h]);
-                sc[j][h] = valid[j] ? full * a.scale_log2 : kNegInf;
+                sc[j][h] = st.valid[j] ? full * a.scale_log2 : kNegInf;
             }
         }
 
-        // Online softmax update for the tile.
         float p[NCW][G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -378,7 +580,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
             for (int j = 0; j < NCW; ++j) p[j][h] = (sc[j][h] == kNegInf) ? 0.f : exp2_fast(sc[j][h] - mn + kPOff);
         }
 
-        // P.V
         if constexpr (VT == KVDEC_F16) {
             // Pairs of cells: (V[A][d], V[B][d]) . (pA, pB) in one packed dot.
 #pragma unroll
@@ -394,8 +595,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 for (int c = 0; c < NCV; ++c) {
 #pragma unroll
                     for (int i = 0; i < FV::CB / 4; ++i) {
-                        const h2 lo = as_h2(__builtin_amdgcn_perm(vc[B][c].w[i], vc[A][c].w[i], 0x05040100u));
-                        const h2 hi = as_h2(__builtin_amdgcn_perm(vc[B][c].w[i], vc[A][c].w[i], 0x07060302u));
+                        const h2 lo = as_h2(__builtin_amdgcn_perm(st.vc[B][c].w[i], st.vc[A][c].w[i], 0x05040100u));
+                        const h2 hi = as_h2(__builtin_amdgcn_perm(st.vc[B][c].w[i], st.vc[A][c].w[i], 0x07060302u));
                         const int dd = c * FV::EPC + 2 * i;
 #pragma unroll
                         for (int h = 0; h < G; ++h) {
@@ -413,10 +614,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
                 for (int c = 0; c < NCV; ++c) {
                     h2 vp[FV::EPC / 2];
-                    to_pairs<VT>(vc[j][c], vp);
+                    to_pairs<VT>(st.vc[j][c], vp);
 #pragma unroll
                     for (int h = 0; h < G; ++h) {
-                        const float pd = p[j][h] * vd[j][c];
+                        const float pd = p[j][h] * st.vd[j][c];
 #pragma unroll
                         for (int i = 0; i < FV::EPC / 2; ++i) {
                             o[h][c * FV::EPC + 2 * i] = fmaf((float)vp[i].x, pd, o[h][c * FV::EPC + 2 * i]);
@@ -426,90 +627,101 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 }
             }
         }
+    };
+
+    for (int64_t base = (int64_t)t0 * kTile; base < pos_end; base += STEP) {
+        Step st;
+        load_step(base, st);
+        compute_step(st);
     }
 
-    // Merge the cell streams of the wave (lanes with the same sub).
-#pragma unroll
-    for (int mask = R; mask < 64; mask <<= 1) {
+    // Merge the cell streams.  Lanes with the same sub own the same d-slice
+    // for different cells.  One in-register step pairs lane i with lane i ^ 8
+    // (DPP row rotate by 8) when that partner holds the same slice; the
+    // remaining NSW streams per wave go through LDS.
+    if constexpr (kDppStep) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const float mo = __shfl_xor(m[h], mask);
-            const float lo = __shfl_xor(l[h], mask);
+            const float mo = dpp<0x128>(m[h]);
+            const float lo = dpp<0x128>(l[h]);
             const float mn = fmaxf(m[h], mo);
             const float fa = (m[h] == kNegInf) ? 0.f : exp2_fast(m[h] - mn);
             const float fb = (mo == kNegInf) ? 0.f : exp2_fast(mo - mn);
             l[h] = l[h] * fa + lo * fb;
 #pragma unroll
-            for (int i = 0; i < DL; ++i) o[h][i] = o[h][i] * fa + __shfl_xor(o[h][i], mask) * fb;
+            for (int i = 0; i < DL; ++i) o[h][i] = o[h][i] * fa + dpp<0x128>(o[h][i]) * fb;
             m[h] = mn;
         }
     }
-    if (cl == 0) {
+    const bool rep = kDppStep ? ((lane & 8) == 0) : true;
+    const int kl = kDppStep ? (((lane & 7) | ((lane >> 4) << 3)) / R) : cl;
+    if (rep) {
+        const int k = wave * NSW + kl;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             if (sub == 0) {
-                sm_m[wave][h] = m[h];
-                sm_l[wave][h] = l[h] * kPOffInv;
+                sm_m[k][h] = m[h];
+                sm_l[k][h] = l[h] * kPOffInv;
             }
 #pragma unroll
             for (int c = 0; c < NCV; ++c)
 #pragma unroll
-                for (int i = 0; i < FV::EPC; ++i) sm_o[wave][h][(c * R + sub) * FV::EPC + i] = o[h][c * FV::EPC + i] * kPOffInv;
+                for (int i = 0; i < FV::EPC; i += 4)
+                    *reinterpret_cast<float4*>(&sm_o[k][h][(c * R + sub) * FV::EPC + i]) =
+                        make_float4(o[h][c * FV::EPC + i] * kPOffInv, o[h][c * FV::EPC + i + 1] * kPOffInv,
+                                    o[h][c * FV::EPC + i + 2] * kPOffInv, o[h][c * FV::EPC + i + 3] * kPOffInv);
         }
     }
     __syncthreads();
 
-    // Merge the 4 waves: thread -> (h, d).  Result of this split in log2 units.
+    // Merge the NS streams: thread -> float4 column.  Result of this split in log2 units.
+    constexpr int NV = G * D / 4;
     const int n_splits = sa.n_splits;
     const bool single = (n_splits == 1);
-    float* rec = a.part + (int64_t)(sa.part_begin + g * n_splits + split) * G * (D + 2);
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-        const int h = idx / D, d = idx - h * D;
-        float M = sm_m[0][h], L = sm_l[0][h], O = sm_o[0][h][d];
+    const int64_t rec = sa.part_begin + (int64_t)g * n_splits + split;
+    const __amdgpu_buffer_rsrc_t rs = part_rsrc(a);
+    for (int v = tid; v < NV; v += kThreads) {
+        const int h = (4 * v) / D, d0 = 4 * v - h * D;
+        float M = kNegInf;
 #pragma unroll
-        for (int w = 1; w < 4; ++w) merge2(M, L, O, sm_m[w][h], sm_l[w][h], sm_o[w][h][d]);
+        for (int k = 0; k < NS; ++k) M = fmaxf(M, sm_m[k][h]);
+        float L = 0.f;
+        float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            const float mk = sm_m[k][h];
+            const float f = (mk == kNegInf) ? 0.f : exp2_fast(mk - M);
+            const float4 ok = *reinterpret_cast<const float4*>(&sm_o[k][h][d0]);
+            L = fmaf(sm_l[k][h], f, L);
+            O.x = fmaf(ok.x, f, O.x);
+            O.y = fmaf(ok.y, f, O.y);
+            O.z = fmaf(ok.z, f, O.z);
+            O.w = fmaf(ok.w, f, O.w);
+        }
         if (single) {
-            if (a.acc_in) {
-                const int64_t row = row0 + h;
-                merge2(M, L, O, a.acc_in[row], a.acc_in[a.acc_rows + row], a.acc_in[2 * (int64_t)a.acc_rows + row * D + d]);
-            }
-            emit(a, sa.to_acc, row0 + h, d, D, M, L, O);
+            merge_acc_in(a, row0 + h, d0, D, M, L, O);
+            emit4(a, sa.to_acc, row0 + h, d0, D, M, L, O);
         } else {
-            if (d == 0) {
-                rec[h] = M;
-                rec[G + h] = L;
+            st_dev4(rs, (rec * (G * D) + 4 * v) * 4, O);
+            if (d0 == 0) {
+                st_dev(a.part_m + rec * G + h, M);
+                st_dev(a.part_l + rec * G + h, L);
             }
-            rec[2 * G + h * D + d] = O;
         }
     }
     if (single) return;
 
     // Last workgroup of the (slot, KV head) merges every split.
-    __threadfence();
+    wait_stores();
     __syncthreads();
     uint32_t* ticket = a.tickets + (int64_t)(a.slot_base + s) * a.n_kv_heads + g;
     if (tid == 0) {
-        const uint32_t prev = atomicAdd(ticket, 1u);
+        const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sm_last = (prev == (uint32_t)(n_splits - 1));
     }
     __syncthreads();
     if (!sm_last) return;
-    __threadfence();
-    const float* base = a.part + (int64_t)(sa.part_begin + g * n_splits) * G * (D + 2);
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-        const int h = idx / D, d = idx - h * D;
-        float M = kNegInf, L = 0.f, O = 0.f;
-        for (int sp = 0; sp < n_splits; ++sp) {
-            const float* r = base + (int64_t)sp * G * (D + 2);
-            merge2(M, L, O, r[h], r[G + h], r[2 * G + h * D + d]);
-        }
-        if (a.acc_in) {
-            const int64_t row = row0 + h;
-            merge2(M, L, O, a.acc_in[row], a.acc_in[a.acc_rows + row], a.acc_in[2 * (int64_t)a.acc_rows + row * D + d]);
-        }
-        emit(a, sa.to_acc, row0 + h, d, D, M, L, O);
-    }
-    if (tid == 0) atomicExch(ticket, 0u);
+    merge_splits<D, G>(a, sa, s, g, row0, n_splits);
 }
 
 // kvdec_merge: one workgroup per row, one thread per element of head_dim.

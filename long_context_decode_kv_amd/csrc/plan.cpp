@@ -241,7 +241,16 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
     plan.off_tickets = off;
     off = align_up(off + sizeof(uint32_t) * (size_t)p.n_slots * p.n_kv_heads, 256);
     plan.off_parts = off;
-    off = align_up(off + sizeof(float) * (size_t)part_capacity * group * (D + 2), 256);
+    plan.parts_o_bytes = sizeof(float) * (size_t)part_capacity * group * D;
+    if (plan.parts_o_bytes >= (1ull << 31)) {
+        err = "too many split records";
+        return KVDEC_E_UNSUPPORTED;
+    }
+    off = align_up(off + plan.parts_o_bytes, 256);
+    plan.off_parts_m = off;
+    off = align_up(off + sizeof(float) * (size_t)part_capacity * group, 256);
+    plan.off_parts_l = off;
+    off = align_up(off + sizeof(float) * (size_t)part_capacity * group, 256);
     if (has_tail) {
         const size_t rows = (size_t)p.n_slots * p.n_q_heads;
         plan.off_acc0 = off;
