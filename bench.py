@@ -33,6 +33,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+KIND = {0: "f16", 1: "q8", 2: "q4"}
+
+
+def measure_h2d(torch, nbytes=256 << 20, reps=5):
+    """Pinned host -> device copy rate (GB/s) of one large hipMemcpyAsync."""
+    h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    d.copy_(h, non_blocking=True)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        d.copy_(h, non_blocking=True)
+    b.record()
+    torch.cuda.synchronize()
+    return round(nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9, 2)
 
 
 def log(*a):
@@ -121,9 +137,129 @@ class ContiguousModel(Workload):
                                  f"{self.hkv} KV heads x {self.hq} q heads)"
 
 
+class Gqa6Quant(Workload):
+    """One launch over four slots (131072 / 65536 / 20000 / 777 cells) whose
+    128-cell records are interleaved in one cache, block-scaled K and V.
+    ``copies`` independent caches are rotated so repeated steps cannot be
+    served from the 256 MB MALL."""
+
+    cycle = 4  # steps per captured cycle (one launch per step, caches rotated)
+
+    def __init__(self, name, kind, copies=4):
+        self.name, self.kind, self.layers = name, kind, copies
+        self.hq, self.hkv, self.d = 24, 4, 256
+        self.lengths = [131072, 65536, 20000, 777]
+
+    def config(self):
+        return {"workload": self.name, "q_heads": 24, "kv_heads": 4, "head_dim": 256, "slots": 4,
+                "cells_per_slot": self.lengths, "kv_dtype": {1: "int8+f16 scale/32", 2: "4-bit+f16 scale/32"}[self.kind],
+                "indirect_plan": "128-cell records interleaved round-robin across slots, -1 holes",
+                "rotated_cache_copies": self.layers}
+
+    def algorithmic_bytes_per_launch(self):
+        return algorithmic_bytes(sum(self.lengths), self.hkv, self.d, self.kind, 4, self.hq, self.n_entries)
+
+    def setup(self, K, torch, seed0):
+        from long_context_decode_kv_amd import synth
+        lists, cap = synth.interleaved_record_lists(self.lengths)
+        self.plan = K.plan(24, 4, 256, 4, cap, k_type=self.kind, v_type=self.kind, cells=lists)
+        entries, _ = self.plan.cells()
+        self.n_entries = len(entries)
+        self.plan_cells = torch.from_numpy(entries).cuda()
+        self.k, self.v, self.q, self.out, self.lse = [], [], [], [], []
+        for c in range(self.layers):
+            s = seed0 * 100 + c
+            self.k.append(synth.device_quant_cache(3 * s, self.kind, cap, 4, 256))
+            self.v.append(synth.device_quant_cache(3 * s + 1, self.kind, cap, 4, 256))
+            self.q.append(synth.device_q(3 * s + 2, 4, 24, 256))
+            self.out.append(torch.empty(4, 24, 256, device="cuda"))
+            self.lse.append(torch.empty(4, 24, device="cuda"))
+        self.ws = K.workspace(self.plan)
+
+    def launch(self, K, i):
+        K.attend(self.plan, self.q[i], self.k[i][0], self.v[i][0], self.ws, out=self.out[i], lse=self.lse[i],
+                 k_scales=self.k[i][1], v_scales=self.v[i][1], plan_cells=self.plan_cells)
+
+    def oracle_sample(self, budget_s):
+        import numpy as np
+        import oracle as O
+        from long_context_decode_kv_amd import synth
+        r = synth.rng(98)
+        n = self.lengths[2]  # the 20000-cell slot, all four KV heads
+        q = synth.gen_q(r, 1, 24, 256)
+        kc, ks = synth.gen_quant_cache(r, self.kind, n, 4, 256)
+        vc, vs = synth.gen_quant_cache(r, self.kind, n, 4, 256)
+        t0 = time.perf_counter()
+        done = 0
+        while True:
+            O.decode_attention(q, [((self.kind, kc, ks), (self.kind, vc, vs), [np.arange(n)])], 4, 1 / 16)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or done >= 4:
+                break
+        per_cell = el / (done * n)
+        total = per_cell * sum(self.lengths)
+        return 1, total, f"slot of {n} cells x 4 KV heads x 24 q heads timed {done}x ({el:.1f} s), scaled by " \
+                         f"cell count to all {sum(self.lengths)} attended cells"
+
+
+class RollingWindow(ContiguousModel):
+    eager_only = True  # host-tail copies and events are enqueued per call
+    """Qwen3-8B shape at ctx 40960: per layer the newest 14000 cells are
+    resident and the oldest 26960 stream from pinned host memory through the
+    workspace ring (copy stream + events), merged by log-sum-exp."""
+
+    def __init__(self):
+        super().__init__("rolling-ctx40960", 36, 32, 8, 128, 40960, 40960)
+        self.window, self.tail = 14000, 26960
+
+    def config(self):
+        c = super().config()
+        c.update({"cells_resident_window": self.window, "cells_host_tail": self.tail, "tail_chunk_cells": 2048,
+                  "ring_depth": 4})
+        return c
+
+    def algorithmic_bytes_per_launch(self):
+        return algorithmic_bytes(self.occupied, self.hkv, self.d, 0, 1, self.hq)
+
+    def pcie_bytes_per_launch(self):
+        return 2 * self.tail * self.hkv * self.d * 2
+
+    def setup(self, K, torch, seed0):
+        from long_context_decode_kv_amd import synth
+        self.k, self.v, self.q, self.out, self.lse, self.hk, self.hv = [], [], [], [], [], [], []
+        for layer in range(self.layers):
+            s = seed0 * 100 + layer
+            kd = synth.device_f16_cache(3 * s, self.capacity, self.hkv, self.d)
+            vd = synth.device_f16_cache(3 * s + 1, self.capacity, self.hkv, self.d)
+            hk = torch.empty((self.tail, self.hkv, self.d), dtype=torch.float16, pin_memory=True)
+            hv = torch.empty((self.tail, self.hkv, self.d), dtype=torch.float16, pin_memory=True)
+            hk.copy_(kd[:self.tail])
+            hv.copy_(vd[:self.tail])
+            self.k.append(kd)
+            self.v.append(vd)
+            self.hk.append(hk)
+            self.hv.append(hv)
+            self.q.append(synth.device_q(3 * s + 2, 1, self.hq, self.d))
+            self.out.append(torch.empty(1, self.hq, self.d, device="cuda"))
+            self.lse.append(torch.empty(1, self.hq, device="cuda"))
+        self.plan = K.plan(self.hq, self.hkv, self.d, 1, self.capacity, n_occupied=[self.window],
+                           cell_begin=[self.tail], n_tail=[self.tail], tail_capacity_cells=self.tail,
+                           tail_chunk_cells=2048, tail_ring_depth=4)
+        self.ws = K.workspace(self.plan)
+        self.copy_stream = torch.cuda.Stream()
+
+    def launch(self, K, layer):
+        K.attend(self.plan, self.q[layer], self.k[layer], self.v[layer], self.ws, out=self.out[layer],
+                 lse=self.lse[layer], k_tail=self.hk[layer], v_tail=self.hv[layer], copy_stream=self.copy_stream)
+
+
 WORKLOADS = {
     "qwen3-8b-ctx16k": lambda: ContiguousModel("qwen3-8b-ctx16k", 36, 32, 8, 128, 16384, 13100),
     "qwen2.5-14b-1m": lambda: ContiguousModel("qwen2.5-14b-1m", 48, 40, 8, 128, 524288, 524288),
+    "gqa6-q8": lambda: Gqa6Quant("gqa6-q8", 1),
+    "gqa6-q4": lambda: Gqa6Quant("gqa6-q4", 2),
+    "rolling-ctx40960": lambda: RollingWindow(),
 }
 
 
@@ -180,62 +316,69 @@ def main():
     log(f"[bench] plan: {info}")
     stream = torch.cuda.current_stream()
 
-    def step():
+    cycle = getattr(wl, "cycle", 1)          # steps covered by one pass over the launch list
+    launches_per_step = wl.layers // cycle
+    mode = "eager" if getattr(wl, "eager_only", False) else args.mode
+
+    def one_cycle():
         for layer in range(wl.layers):
             wl.launch(K, layer)
 
-    # warm-up (eager), then optional graph capture of one step
-    for _ in range(max(1, args.warmup)):
-        step()
+    # warm-up (eager), then optional graph capture of one cycle
+    for _ in range(max(1, args.warmup // cycle)):
+        one_cycle()
     torch.cuda.synchronize()
     graph = None
-    if args.mode == "graph":
+    if mode == "graph":
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step()
+            one_cycle()
         torch.cuda.synchronize()
-        for _ in range(max(1, args.warmup)):
+        for _ in range(max(1, args.warmup // cycle)):
             graph.replay()
         torch.cuda.synchronize()
 
     # timed region 1: whole steps
-    log(f"[bench] timing {args.steps} steps ({args.mode})")
+    n_cycles = max(1, args.steps // cycle)
+    steps = n_cycles * cycle
+    log(f"[bench] timing {steps} steps ({mode})")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
+    for _ in range(n_cycles):
         if graph is not None:
             graph.replay()
         else:
-            step()
+            one_cycle()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = ev0.elapsed_time(ev1) / steps
 
-    # timed region 2: every split-kernel launch bracketed by its own events on
-    # its stream (adds the dispatch overhead of an isolated launch)
-    n_ev = min(args.steps, 20) * wl.layers
+    # timed region 2: every launch bracketed by its own events on its stream
+    # (adds the dispatch overhead of an isolated launch)
+    reps = max(1, min(n_cycles, 20 // cycle if cycle > 1 else 20))
+    n_ev = reps * wl.layers
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     torch.cuda.synchronize()
     i = 0
-    for _ in range(min(args.steps, 20)):
+    for _ in range(reps):
         for layer in range(wl.layers):
             starts[i].record(stream)
             wl.launch(K, layer)
             ends[i].record(stream)
             i += 1
     torch.cuda.synchronize()
-    durs = sorted(s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends))  # microseconds
+    durs = sorted(s_.elapsed_time(e_) * 1e3 for s_, e_ in zip(starts, ends))  # microseconds
     bracketed_us = sum(durs) / len(durs)
-    # average launch duration over timed region 1: the step is nothing but
-    # back-to-back split-kernel launches on one stream
-    avg_us = ms_per_step * 1e3 / wl.layers
+    # average launch duration over timed region 1: a step is nothing but
+    # back-to-back launches on one stream
+    avg_us = ms_per_step * 1e3 / launches_per_step
 
     bytes_launch = wl.algorithmic_bytes_per_launch()
-    bytes_step = bytes_launch * wl.layers
+    bytes_step = bytes_launch * launches_per_step
     gbs = bytes_step / (ms_per_step * 1e-3) / 1e9
     achieved = bytes_launch / (avg_us * 1e-6) / 1e9
     traffic = committed_traffic(wl.name)
@@ -254,7 +397,7 @@ def main():
         "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
@@ -262,19 +405,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 KV, fp32 accumulate",
-        "data": "synthetic: q, K, V ~ N(0,1), K/V rounded to f16, seeded on-device generator",
-        "config": dict(wl.config(), mode=args.mode, workgroups_per_launch=info["n_workgroups"],
+        "dtype": {0: "f16 KV, fp32 accumulate", 1: "int8 KV (f16 scale per 32), fp32 accumulate",
+                  2: "4-bit KV (f16 scale per 32), fp32 accumulate"}[wl.kind],
+        "data": "synthetic: q ~ N(0,1); K, V ~ N(0,1) rounded to f16 or block-encoded; seeded on-device generator",
+        "config": dict(wl.config(), mode=mode, workgroups_per_launch=info["n_workgroups"],
                        tiles_per_split=info["tiles_per_split"]),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "split_kernel<128,%d,f16,f16>" % (wl.hq // wl.hkv),
-                     "algorithmic_bytes_per_launch": bytes_launch, "launches_per_step": wl.layers,
+                     "kernel": "split_kernel<%d,%d,%s,%s>" % (wl.d, wl.hq // wl.hkv, KIND[wl.kind], KIND[wl.kind]),
+                     "algorithmic_bytes_per_launch": bytes_launch, "launches_per_step": launches_per_step,
                      "avg_launch_us": round(avg_us, 3), "isolated_launch_event_us": round(bracketed_us, 3)},
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall_s, 4),
         "kernel_source_sha256_16": kernel_source_hash(),
     }
+    if hasattr(wl, "pcie_bytes_per_launch"):
+        pb = wl.pcie_bytes_per_launch() * launches_per_step
+        res["pcie"] = {"h2d_bytes_per_step": pb, "h2d_gbs_effective": round(pb / (ms_per_step * 1e-3) / 1e9, 2),
+                       "link_gbs_measured": measure_h2d(torch)}
     print(json.dumps(res), flush=True)
 
 
