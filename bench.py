@@ -297,6 +297,8 @@ def main():
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device-to-device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -308,6 +310,13 @@ def main():
     import torch
     from long_context_decode_kv_amd import kvdec as K
     torch.cuda.set_device(0)
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wl = WORKLOADS[args.workload]()
     log(f"[bench] workload {wl.name}: generating inputs on the device")
     wl.setup(K, torch, 1001)
