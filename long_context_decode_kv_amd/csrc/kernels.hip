@@ -400,6 +400,66 @@ __device__ void merge_splits(const SplitArgs& a, const SlotArg& sa, int s, int g
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// End of a split: merge the NS cell streams left in LDS (m2, l, o per
+// stream and head) into the split's result; a single-split group writes its
+// output directly, otherwise the split's record is published and the last
+// workgroup of the (slot, KV head) merges all records.
+template <int D, int G, int NS>
+__device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& sa, int s, int g, int split,
+                                             int64_t row0, const float (*sm_m)[G], const float (*sm_l)[G],
+                                             const float (*sm_o)[G][D], int& sm_last) {
+    const int tid = threadIdx.x;
+    // Merge the NS streams: thread -> float4 column.  Result of this split in log2 units.
+    constexpr int NV = G * D / 4;
+    const int n_splits = sa.n_splits;
+    const bool single = (n_splits == 1);
+    const int64_t rec = sa.part_begin + (int64_t)g * n_splits + split;
+    const __amdgpu_buffer_rsrc_t rs = part_rsrc(a);
+    for (int v = tid; v < NV; v += kThreads) {
+        const int h = (4 * v) / D, d0 = 4 * v - h * D;
+        float M = kNegInf;
+#pragma unroll
+        for (int k = 0; k < NS; ++k) M = fmaxf(M, sm_m[k][h]);
+        float L = 0.f;
+        float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            const float mk = sm_m[k][h];
+            const float f = (mk == kNegInf) ? 0.f : exp2_fast(mk - M);
+            const float4 ok = *reinterpret_cast<const float4*>(&sm_o[k][h][d0]);
+            L = fmaf(sm_l[k][h], f, L);
+            O.x = fmaf(ok.x, f, O.x);
+            O.y = fmaf(ok.y, f, O.y);
+            O.z = fmaf(ok.z, f, O.z);
+            O.w = fmaf(ok.w, f, O.w);
+        }
+        if (single) {
+            merge_acc_in(a, row0 + h, d0, D, M, L, O);
+            emit4(a, sa.to_acc, row0 + h, d0, D, M, L, O);
+        } else {
+            st_dev4(rs, (rec * (G * D) + 4 * v) * 4, O);
+            if (d0 == 0) {
+                st_dev(a.part_m + rec * G + h, M);
+                st_dev(a.part_l + rec * G + h, L);
+            }
+        }
+    }
+    if (single) return;
+
+    // Last workgroup of the (slot, KV head) merges every split.
+    wait_stores();
+    __syncthreads();
+    uint32_t* ticket = a.tickets + (int64_t)(a.slot_base + s) * a.n_kv_heads + g;
+    if (tid == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm_last = (prev == (uint32_t)(n_splits - 1));
+    }
+    __syncthreads();
+    if (!sm_last) return;
+    merge_splits<D, G>(a, sa, s, g, row0, n_splits);
+}
+
+
 template <int D, int G, int KT, int VT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void split_kernel(const SplitArgs a) {
     using Gm = Geo<D, G>;
@@ -674,54 +734,279 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     __syncthreads();
 
-    // Merge the NS streams: thread -> float4 column.  Result of this split in log2 units.
-    constexpr int NV = G * D / 4;
-    const int n_splits = sa.n_splits;
-    const bool single = (n_splits == 1);
-    const int64_t rec = sa.part_begin + (int64_t)g * n_splits + split;
-    const __amdgpu_buffer_rsrc_t rs = part_rsrc(a);
-    for (int v = tid; v < NV; v += kThreads) {
-        const int h = (4 * v) / D, d0 = 4 * v - h * D;
-        float M = kNegInf;
+    finish_split<D, G, NS>(a, sa, s, g, split, row0, sm_m, sm_l, sm_o, sm_last);
+}
+
+// ---------------------------------------------------------------------------
+// Wide-group kernel (G = 6..8 query heads per KV head): matrix-core path.
+//
+// With six or more query rows per KV head the VALU path runs out of issue
+// slots before HBM does (int8 / 4-bit rows also need dequantisation), so the
+// two contractions of a 32-cell step go to v_mfma_f32_16x16x32_f16, the G
+// query rows padded to 16 with zero rows:
+//   S^T[cell][head] = K^[cell][:] . q[head][:]   (A = K^ rows, B = q^T)
+//   O[head][d]     += P[head][cell] . V^[cell][d] (A = P, B = V^)
+// Operand layouts (measured on gfx950): A[i][k] sits in lane i + 16*(k/8),
+// element k%8; B[k][j] in lane j + 16*(k/8); D[i][j] in lane j + 16*(i/4),
+// element i%4.  The order of the contraction index is free, so
+//  * for S, lane group q of a 16-cell block reads 16-byte chunks q, q+4, ...
+//    of its cell's row and q is loaded in the same permuted element order,
+//    so every chunk feeds whole MFMAs without any shuffle;
+//  * for P.V, the 8 contraction slots of lane group q are cells 4q..4q+3 of
+//    the step's two 16-cell blocks -- exactly the scores that lane holds
+//    after the S product -- so P never moves between lanes.
+// V^ is dequantised (d * code rounded to f16) into a per-wave LDS tile of 32
+// rows and read back column-wise with ds_read_b64_tr_b16, whose 16-lane 4x4
+// transpose delivers the B operand.  Each wave is one online-softmax stream;
+// the four waves are merged at the end like the VALU path's streams.
+// ---------------------------------------------------------------------------
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+
+// Elements per 16-byte chunk of a stored row.
+template <int T>
+struct Row16 {
+    static constexpr int EPC = T == KVDEC_F16 ? 8 : T == KVDEC_Q8_B32 ? 16 : 32;
+};
+
+// One 16-byte chunk -> its EPC values as f16 pairs (block-scaled kinds: d * code,
+// rounded to f16).
+template <int T>
+__device__ __forceinline__ void dequant16(const Chunk<16>& c, uint16_t scale_bits, h2 (&out)[Row16<T>::EPC / 2]) {
+    to_pairs<T>(c, out);
+    if constexpr (T != KVDEC_F16) {
+        const _Float16 d = __builtin_bit_cast(_Float16, scale_bits);
+        const h2 dd = {d, d};
 #pragma unroll
-        for (int k = 0; k < NS; ++k) M = fmaxf(M, sm_m[k][h]);
-        float L = 0.f;
-        float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int i = 0; i < Row16<T>::EPC / 2; ++i) out[i] = out[i] * dd;
+    }
+}
+
+template <int D, int G, int KT, int VT>
+__global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a) {
+    static_assert(G >= 1 && G <= 16, "heads padded to one 16-row tile");
+    constexpr int EK = Row16<KT>::EPC, EV = Row16<VT>::EPC;
+    constexpr int JK = D / EK / 4, JV = D / EV / 4;  // chunks per lane per row
+    static_assert(JK >= 1 && JV >= 1 && JK * 4 * EK == D && JV * 4 * EV == D, "row chunking");
+    constexpr int NKB = D / 32;                    // S MFMAs per 16-cell block
+    constexpr int NNB = D / 16;                    // P.V MFMAs (16-column blocks of O)
+    constexpr int NB = D / kBlock;                 // scales per row
+    constexpr int VSTR = 2 * D + 32;               // bytes per staged V row (padded)
+    constexpr int STAGE = 4 * 32 * VSTR;           // V staging of the 4 waves
+    constexpr int MERGE = 4 * G * 4 * 2 + 4 * G * D * 4;
+    constexpr int SMEM = STAGE > MERGE ? STAGE : MERGE;
+    __shared__ __align__(16) unsigned char smem[SMEM];
+    __shared__ int sm_last;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int li = lane & 15;  // row / column index inside a 16-lane group
+    const int lq = lane >> 4;  // lane group
+
+    const int wg = blockIdx.x;
+    int s = 0;
+    while (s + 1 < a.n_slots && a.slot[s + 1].wg_begin <= wg) ++s;
+    const SlotArg sa = a.slot[s];
+    const int local = wg - sa.wg_begin;
+    const int split = local / a.n_kv_heads;
+    const int g = local - split * a.n_kv_heads;
+    const int t0 = (int)(((int64_t)split * sa.n_tiles) / sa.n_splits);
+    const int t1 = (int)(((int64_t)(split + 1) * sa.n_tiles) / sa.n_splits);
+    const int64_t row0 = (int64_t)(a.slot_base + s) * a.n_q_heads + g * G;
+
+    // B operand of S: q rows (zero rows for heads >= G) in the permuted order
+    // of the K chunks this lane group reads.
+    h8 qb[NKB];
 #pragma unroll
-        for (int k = 0; k < NS; ++k) {
-            const float mk = sm_m[k][h];
-            const float f = (mk == kNegInf) ? 0.f : exp2_fast(mk - M);
-            const float4 ok = *reinterpret_cast<const float4*>(&sm_o[k][h][d0]);
-            L = fmaf(sm_l[k][h], f, L);
-            O.x = fmaf(ok.x, f, O.x);
-            O.y = fmaf(ok.y, f, O.y);
-            O.z = fmaf(ok.z, f, O.z);
-            O.w = fmaf(ok.w, f, O.w);
+    for (int j = 0; j < JK; ++j) {
+#pragma unroll
+        for (int sub = 0; sub < EK / 8; ++sub) {
+            const int e0 = (lq + 4 * j) * EK + 8 * sub;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                qb[j * (EK / 8) + sub][e] = li < G ? (_Float16)a.q[(row0 + li) * D + e0 + e] : (_Float16)0.0f;
         }
-        if (single) {
-            merge_acc_in(a, row0 + h, d0, D, M, L, O);
-            emit4(a, sa.to_acc, row0 + h, d0, D, M, L, O);
-        } else {
-            st_dev4(rs, (rec * (G * D) + 4 * v) * 4, O);
-            if (d0 == 0) {
-                st_dev(a.part_m + rec * G + h, M);
-                st_dev(a.part_l + rec * G + h, L);
+    }
+
+    float m_h = kNegInf, l_h = 0.f;  // state of head li (identical over the 4 lane groups)
+    f4v oacc[NNB];
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb) oacc[nb] = f4v{0.f, 0.f, 0.f, 0.f};
+
+    const uint8_t* kbase = a.k + (int64_t)g * a.k_hs;
+    const uint8_t* vbase = a.v + (int64_t)g * a.v_hs;
+    unsigned char* vst = smem + wave * 32 * VSTR;
+    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    const int64_t tile_end = (int64_t)t1 * kTile;
+    const int64_t pos_end = tile_end < sa.n ? tile_end : sa.n;
+
+    for (int64_t base = (int64_t)t0 * kTile; base < pos_end; base += kTile) {
+        // The two 16-cell blocks of this wave: lane li owns cell li of each.
+        int64_t cell[2];
+        bool valid[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int64_t pos = base + 32 * wave + 16 * mb + li;
+            if (a.plan) {
+                const int64_t c = pos < pos_end ? (int64_t)a.plan[sa.first + pos] : -1;
+                valid[mb] = c >= 0 && c < a.capacity;
+                cell[mb] = valid[mb] ? c : 0;
+            } else {
+                valid[mb] = pos < pos_end;
+                cell[mb] = sa.first + (valid[mb] ? pos : 0);
             }
         }
-    }
-    if (single) return;
+        const uint64_t vm0 = __ballot(valid[0]), vm1 = __ballot(valid[1]);
+        if (((vm0 | vm1) & 0xFFFFull) == 0) continue;  // fully masked step (wave-uniform)
 
-    // Last workgroup of the (slot, KV head) merges every split.
-    wait_stores();
-    __syncthreads();
-    uint32_t* ticket = a.tickets + (int64_t)(a.slot_base + s) * a.n_kv_heads + g;
-    if (tid == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sm_last = (prev == (uint32_t)(n_splits - 1));
+        Chunk<16> kc[2][JK], vc[2][JV];
+        uint16_t kd[2][JK], vd[2][JV];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const uint8_t* kr = kbase + cell[mb] * a.k_cs;
+            const uint8_t* vr = vbase + cell[mb] * a.v_cs;
+#pragma unroll
+            for (int j = 0; j < JK; ++j) {
+                const int c = lq + 4 * j;
+                kc[mb][j] = valid[mb] ? load_chunk<16>(kr + c * 16) : zero_chunk<16>();
+                if constexpr (KT != KVDEC_F16)
+                    kd[mb][j] = valid[mb] ? a.ks[(cell[mb] * a.n_kv_heads + g) * NB + (c * EK) / kBlock] : 0;
+            }
+#pragma unroll
+            for (int j = 0; j < JV; ++j) {
+                const int c = lq + 4 * j;
+                vc[mb][j] = valid[mb] ? load_chunk<16>(vr + c * 16) : zero_chunk<16>();
+                if constexpr (VT != KVDEC_F16)
+                    vd[mb][j] = valid[mb] ? a.vs[(cell[mb] * a.n_kv_heads + g) * NB + (c * EV) / kBlock] : 0;
+            }
+        }
+
+        // S^T for the two blocks.
+        f4v sacc[2] = {f4v{0.f, 0.f, 0.f, 0.f}, f4v{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+            for (int j = 0; j < JK; ++j) {
+                h2 kp[EK / 2];
+                dequant16<KT>(kc[mb][j], KT == KVDEC_F16 ? 0 : kd[mb][j], kp);
+#pragma unroll
+                for (int sub = 0; sub < EK / 8; ++sub) {
+                    h8 av;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        av[2 * e] = kp[4 * sub + e].x;
+                        av[2 * e + 1] = kp[4 * sub + e].y;
+                    }
+                    sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[j * (EK / 8) + sub], sacc[mb], 0, 0, 0);
+                }
+            }
+        }
+
+        // Scores of head li for cells 4*lq + e of each block (log2 units).
+        float sc[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = 4 * lq + e;
+            sc[e] = ((vm0 >> c) & 1) ? sacc[0][e] * a.scale_log2 : kNegInf;
+            sc[4 + e] = ((vm1 >> c) & 1) ? sacc[1][e] * a.scale_log2 : kNegInf;
+        }
+        float mt = sc[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sc[e]);
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(m_h, mt);
+        const float alpha = (mn == kNegInf) ? 1.f : exp2_fast(m_h - mn);
+        m_h = mn;
+        h8 pa;
+        float lsum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const float p0 = (sc[e] == kNegInf) ? 0.f : exp2_fast(sc[e] - mn + kPOff);
+            const float p1 = (sc[e + 1] == kNegInf) ? 0.f : exp2_fast(sc[e + 1] - mn + kPOff);
+            const h2 pp = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+            pa[e] = pp.x;
+            pa[e + 1] = pp.y;
+            lsum = __builtin_amdgcn_fdot2(pp, ones, lsum, false);
+        }
+        lsum += __shfl_xor(lsum, 16);
+        lsum += __shfl_xor(lsum, 32);
+        l_h = l_h * alpha + lsum;
+        // O rows held by this lane are heads 4*lq + e: rescale with their alphas.
+        if (__ballot(alpha != 1.f) != 0) {
+            float ae[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ae[e] = __shfl(alpha, 4 * lq + e);
+#pragma unroll
+            for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) oacc[nb][e] *= ae[e];
+        }
+
+        // V^ rows of the step -> LDS (row = 16*block + cell), f16.
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+            for (int j = 0; j < JV; ++j) {
+                const int c = lq + 4 * j;
+                h2 vp[EV / 2];
+                dequant16<VT>(vc[mb][j], VT == KVDEC_F16 ? 0 : vd[mb][j], vp);
+                uint4* dst = reinterpret_cast<uint4*>(vst + (16 * mb + li) * VSTR + c * EV * 2);
+#pragma unroll
+                for (int w = 0; w < EV / 8; ++w)
+                    dst[w] = make_uint4(__builtin_bit_cast(uint32_t, vp[4 * w]), __builtin_bit_cast(uint32_t, vp[4 * w + 1]),
+                                        __builtin_bit_cast(uint32_t, vp[4 * w + 2]),
+                                        __builtin_bit_cast(uint32_t, vp[4 * w + 3]));
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // O += P . V^: B operand by transposing 16-lane reads of the staged rows.
+        typedef __attribute__((address_space(3))) fp16x4_t lds_h4;
+        const int r_lo = 4 * lq + (li >> 2);  // staged row of block 0 read by this lane
+        const int col = 4 * (li & 3);
+#pragma unroll
+        for (int nb = 0; nb < NNB; ++nb) {
+            const int cb = (16 * nb + col) * 2;
+            // generic -> LDS address space (C-style cast: the pointer is in smem)
+            lds_h4* p0 = (lds_h4*)(vst + r_lo * VSTR + cb);
+            lds_h4* p1 = (lds_h4*)(vst + (16 + r_lo) * VSTR + cb);
+            const fp16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16(p0);
+            const fp16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16(p1);
+            h8 vb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vb[e] = (_Float16)v0[e];
+                vb[4 + e] = (_Float16)v1[e];
+            }
+            oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, oacc[nb], 0, 0, 0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+
+    // Each wave is one stream: (m2, l, o) of heads < G -> LDS, then merge.
+    __syncthreads();  // the V staging area is reused for the merge arrays
+    float (*sm_m)[G] = reinterpret_cast<float (*)[G]>(smem);
+    float (*sm_l)[G] = reinterpret_cast<float (*)[G]>(smem + 4 * G * 4);
+    float (*sm_o)[G][D] = reinterpret_cast<float (*)[G][D]>(smem + 4 * G * 4 * 2);
+    if (lq == 0 && li < G) {
+        sm_m[wave][li] = m_h;
+        sm_l[wave][li] = l_h * kPOffInv;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int h = 4 * lq + e;
+            if (h < G) sm_o[wave][h][16 * nb + li] = oacc[nb][e] * kPOffInv;
+        }
     __syncthreads();
-    if (!sm_last) return;
-    merge_splits<D, G>(a, sa, s, g, row0, n_splits);
+    finish_split<D, G, 4>(a, sa, s, g, split, row0, sm_m, sm_l, sm_o, sm_last);
 }
 
 // kvdec_merge: one workgroup per row, one thread per element of head_dim.
@@ -753,9 +1038,21 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
     }
 }
 
+// Groups of up to 5 query heads per KV head run on the VALU kernel; wider
+// groups (with head_dim 128 or 256) on the matrix-core kernel.
+template <int D, int G>
+constexpr bool use_mfma() {
+    return G >= 6 && D >= 128;
+}
+
 template <int D, int G, int KT, int VT>
 int launch_one(const SplitArgs& a, void* stream) {
-    hipLaunchKernelGGL((split_kernel<D, G, KT, VT>), dim3(a.n_workgroups), dim3(kThreads), 0, (hipStream_t)stream, a);
+    if constexpr (use_mfma<D, G>())
+        hipLaunchKernelGGL((split_mfma_kernel<D, G, KT, VT>), dim3(a.n_workgroups), dim3(kThreads), 0,
+                           (hipStream_t)stream, a);
+    else
+        hipLaunchKernelGGL((split_kernel<D, G, KT, VT>), dim3(a.n_workgroups), dim3(kThreads), 0,
+                           (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
 
