@@ -421,7 +421,9 @@ def main():
                        tiles_per_split=info["tiles_per_split"]),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "split_kernel<%d,%d,%s,%s>" % (wl.d, wl.hq // wl.hkv, KIND[wl.kind], KIND[wl.kind]),
+                     "kernel": "%s<%d,%d,%s,%s>" % ("split_mfma_kernel" if wl.hq // wl.hkv >= 6 and wl.d >= 128
+                                                    else "split_kernel", wl.d, wl.hq // wl.hkv, KIND[wl.kind],
+                                                    KIND[wl.kind]),
                      "algorithmic_bytes_per_launch": bytes_launch, "launches_per_step": launches_per_step,
                      "avg_launch_us": round(avg_us, 3), "isolated_launch_event_us": round(bracketed_us, 3)},
         "cpu_baseline": cpu,

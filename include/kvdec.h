@@ -152,7 +152,8 @@ typedef struct kvdec_plan kvdec_plan_t;
  *   means the dense layout [cell][kv head][row].  Base pointers and strides
  *   must be multiples of 16 bytes (of 8 bytes for 4-bit rows).
  * k_scales, v_scales: device f16 scales, dense [cell][kv head][head_dim/32],
- *   required for the block-scaled kinds and ignored for f16.
+ *   required for the block-scaled kinds and ignored for f16; aligned to one
+ *   row of scales, min(16, head_dim / 16) bytes.
  * plan_cells: device int32 copy of the plan's entries (kvdec_plan_cells) in
  *   indirect mode, else NULL.  Entries outside [0, capacity_cells) are read
  *   as holes.

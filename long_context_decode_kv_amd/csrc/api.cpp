@@ -160,10 +160,12 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
         return fail(KVDEC_E_INVALID, "k pointer and strides must be non-negative multiples of the row load size");
     if (!aligned(io->v, val) || v_cs % (int64_t)val || v_hs % (int64_t)val || v_cs < 0 || v_hs < 0)
         return fail(KVDEC_E_INVALID, "v pointer and strides must be non-negative multiples of the row load size");
-    if (kvdec::is_scaled(p.k_type) && (!io->k_scales || !aligned(io->k_scales, 2)))
-        return fail(KVDEC_E_INVALID, "k_scales required (2-byte aligned) for block-scaled K");
-    if (kvdec::is_scaled(p.v_type) && (!io->v_scales || !aligned(io->v_scales, 2)))
-        return fail(KVDEC_E_INVALID, "v_scales required (2-byte aligned) for block-scaled V");
+    // one row of scales (head_dim/32 f16 values) is read with one load
+    const size_t sal = std::min<size_t>(16, (size_t)p.head_dim / 16);
+    if (kvdec::is_scaled(p.k_type) && (!io->k_scales || !aligned(io->k_scales, sal)))
+        return fail(KVDEC_E_INVALID, "k_scales required for block-scaled K, aligned to min(16, head_dim/16) bytes");
+    if (kvdec::is_scaled(p.v_type) && (!io->v_scales || !aligned(io->v_scales, sal)))
+        return fail(KVDEC_E_INVALID, "v_scales required for block-scaled V, aligned to min(16, head_dim/16) bytes");
     if (p.indirect && !io->plan_cells) return fail(KVDEC_E_INVALID, "indirect plan needs plan_cells on the device");
     const bool any_part = io->part_m || io->part_l || io->part_o;
     const bool all_part = io->part_m && io->part_l && io->part_o;

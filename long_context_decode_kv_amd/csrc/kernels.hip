@@ -279,7 +279,7 @@ __device__ void merge_splits(const SplitArgs& a, const SlotArg& sa, int s, int g
     constexpr int NV = G * D / 4;                           // float4 columns of o
     constexpr int TS = NV >= kThreads ? 1 : kThreads / NV;  // threads per column
     constexpr int COLS = (NV + kThreads - 1) / kThreads;    // columns per thread
-    constexpr int UB = 16 / COLS;                           // splits per thread per chunk
+    constexpr int UB = COLS == 1 ? 32 : 16 / COLS;          // splits per thread per chunk
     constexpr int SPC = 64 < UB * TS ? 64 : UB * TS;        // splits per chunk (one per lane)
     __shared__ float f_m[64 * G];
     __shared__ float run_m[G], run_l[G], scale_old[G];
@@ -404,10 +404,10 @@ __device__ void merge_splits(const SplitArgs& a, const SlotArg& sa, int s, int g
 // stream and head) into the split's result; a single-split group writes its
 // output directly, otherwise the split's record is published and the last
 // workgroup of the (slot, KV head) merges all records.
-template <int D, int G, int NS>
+template <int D, int G, int NS, int DP>
 __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& sa, int s, int g, int split,
                                              int64_t row0, const float (*sm_m)[G], const float (*sm_l)[G],
-                                             const float (*sm_o)[G][D], int& sm_last) {
+                                             const float (*sm_o)[G][DP], int& sm_last) {
     const int tid = threadIdx.x;
     // Merge the NS streams: thread -> float4 column.  Result of this split in log2 units.
     constexpr int NV = G * D / 4;
@@ -477,7 +477,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     __shared__ float sm_m[NS][G];
     __shared__ float sm_l[NS][G];
-    __shared__ __align__(16) float sm_o[NS][G][D];
+    // stream stride padded by 16 floats: streams written by one instruction land in different banks
+    __shared__ __align__(16) float sm_o[NS][G][D + 16];
     __shared__ int sm_last;
 
     const int tid = threadIdx.x;
@@ -734,7 +735,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     __syncthreads();
 
-    finish_split<D, G, NS>(a, sa, s, g, split, row0, sm_m, sm_l, sm_o, sm_last);
+    finish_split<D, G, NS, D + 16>(a, sa, s, g, split, row0, sm_m, sm_l, sm_o, sm_last);
 }
 
 // ---------------------------------------------------------------------------
@@ -782,7 +783,24 @@ __device__ __forceinline__ void dequant16(const Chunk<16>& c, uint16_t scale_bit
     }
 }
 
-template <int D, int G, int KT, int VT>
+// Scale of the 32-element block holding chunk lq + 4j of a row, taken from
+// the row's SB bytes of scales.  int8: 16 elements per chunk, so the block is
+// 2j + lq/2 (dword j); 4-bit: 32 per chunk, block lq + 4j (half lq of dwords 2j, 2j+1).
+template <int T, int SB>
+__device__ __forceinline__ uint16_t scale_of(const Chunk<SB>& r, int j, int lq) {
+    if constexpr (T == KVDEC_Q8_B32) {
+        return (uint16_t)(r.w[j] >> (16 * (lq >> 1)));
+    } else if constexpr (T == KVDEC_Q4_B32) {
+        // halves 4j..4j+3 of the row as one 64-bit value (no lane-dependent
+        // register index, which would go through scratch memory)
+        const uint64_t x = (uint64_t)r.w[2 * j] | ((uint64_t)r.w[2 * j + 1] << 32);
+        return (uint16_t)(x >> (16 * lq));
+    } else {
+        return 0;
+    }
+}
+
+template <int D, int G, int KT, int VT, bool IND>
 __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a) {
     static_assert(G >= 1 && G <= 16, "heads padded to one 16-row tile");
     constexpr int EK = Row16<KT>::EPC, EV = Row16<VT>::EPC;
@@ -791,6 +809,7 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
     constexpr int NKB = D / 32;                    // S MFMAs per 16-cell block
     constexpr int NNB = D / 16;                    // P.V MFMAs (16-column blocks of O)
     constexpr int NB = D / kBlock;                 // scales per row
+    constexpr int SB = NB * 2;                     // bytes of one row of scales
     constexpr int VSTR = 2 * D + 32;               // bytes per staged V row (padded)
     constexpr int STAGE = 4 * 32 * VSTR;           // V staging of the 4 waves
     constexpr int MERGE = 4 * G * 4 * 2 + 4 * G * D * 4;
@@ -816,20 +835,37 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
     const int64_t row0 = (int64_t)(a.slot_base + s) * a.n_q_heads + g * G;
 
     // B operand of S: q rows (zero rows for heads >= G) in the permuted order
-    // of the K chunks this lane group reads.
+    // of the K chunks this lane group reads.  Loads are unconditional (row
+    // clamped) so that they all leave before the first wait.
     h8 qb[NKB];
+    {
+        const float* qr = a.q + (row0 + (li < G ? li : 0)) * D;
 #pragma unroll
-    for (int j = 0; j < JK; ++j) {
+        for (int j = 0; j < JK; ++j) {
 #pragma unroll
-        for (int sub = 0; sub < EK / 8; ++sub) {
-            const int e0 = (lq + 4 * j) * EK + 8 * sub;
+            for (int sub = 0; sub < EK / 8; ++sub) {
+                const int e0 = (lq + 4 * j) * EK + 8 * sub;
+                float x[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                qb[j * (EK / 8) + sub][e] = li < G ? (_Float16)a.q[(row0 + li) * D + e0 + e] : (_Float16)0.0f;
+                for (int e = 0; e < 8; e += 2) {
+                    const float2 v = *reinterpret_cast<const float2*>(qr + e0 + e);
+                    x[e] = v.x;
+                    x[e + 1] = v.y;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qb[j * (EK / 8) + sub][e] = li < G ? (_Float16)x[e] : (_Float16)0.0f;
+            }
         }
     }
 
-    float m_h = kNegInf, l_h = 0.f;  // state of head li (identical over the 4 lane groups)
+    // Online softmax of head li (identical over the 4 lane groups).  The
+    // reference m_h moves only when a score exceeds it by more than kLazy,
+    // so the O tile is rarely rescaled; weights 2^(s - m_h + kMPOff) then stay
+    // below 2^15 and remain normal f16 numbers far below the maximum.
+    constexpr float kLazy = 6.0f;
+    constexpr float kMPOff = 9.0f;
+    constexpr float kMPOffInv = 1.0f / 512.0f;
+    float m_h = kNegInf, l_h = 0.f;
     f4v oacc[NNB];
 #pragma unroll
     for (int nb = 0; nb < NNB; ++nb) oacc[nb] = f4v{0.f, 0.f, 0.f, 0.f};
@@ -840,46 +876,92 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
     const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     const int64_t tile_end = (int64_t)t1 * kTile;
     const int64_t pos_end = tile_end < sa.n ? tile_end : sa.n;
+    const int64_t base0 = (int64_t)t0 * kTile;
+    const int n_steps = t1 - t0;  // one 32-cell step of every tile per wave
 
-    for (int64_t base = (int64_t)t0 * kTile; base < pos_end; base += kTile) {
-        // The two 16-cell blocks of this wave: lane li owns cell li of each.
-        int64_t cell[2];
-        bool valid[2];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+    // Cells of a step: lane li owns cell li of the wave's two 16-cell blocks.
+    // Loads never branch: an invalid cell reads row 0 of the cache instead,
+    // its score is masked and its V row is zeroed where it is consumed.  Raw
+    // plan entries are fetched two steps ahead and left untouched until the
+    // step before their use, and the K / V loads of step i+1 leave while
+    // step i computes, so no wait falls on data that is not needed yet.
+    const int32_t* plan_s = IND ? a.plan + sa.first : nullptr;
+    auto fetch = [&](int64_t base, int mb) -> int32_t {
+        if constexpr (IND) {
             const int64_t pos = base + 32 * wave + 16 * mb + li;
-            if (a.plan) {
-                const int64_t c = pos < pos_end ? (int64_t)a.plan[sa.first + pos] : -1;
-                valid[mb] = c >= 0 && c < a.capacity;
-                cell[mb] = valid[mb] ? c : 0;
-            } else {
-                valid[mb] = pos < pos_end;
-                cell[mb] = sa.first + (valid[mb] ? pos : 0);
-            }
+            return plan_s[pos < pos_end ? pos : pos_end - 1];
+        } else {
+            return 0;
         }
-        const uint64_t vm0 = __ballot(valid[0]), vm1 = __ballot(valid[1]);
-        if (((vm0 | vm1) & 0xFFFFull) == 0) continue;  // fully masked step (wave-uniform)
-
-        Chunk<16> kc[2][JK], vc[2][JV];
-        uint16_t kd[2][JK], vd[2][JV];
+    };
+    auto resolve = [&](int64_t base, int mb, int32_t raw, int64_t& cell, bool& valid) {
+        const int64_t pos = base + 32 * wave + 16 * mb + li;
+        if constexpr (IND) {
+            valid = pos < pos_end && raw >= 0 && raw < a.capacity;
+            cell = valid ? raw : 0;
+        } else {
+            valid = pos < pos_end;
+            cell = valid ? sa.first + pos : 0;
+        }
+    };
+    Chunk<16> kc[2][JK], vc[2][JV];
+    Chunk<SB> kr_s[2], vr_s[2];  // scale rows of the two cells (block-scaled kinds)
+    auto load_k = [&](const int64_t (&cell)[2]) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             const uint8_t* kr = kbase + cell[mb] * a.k_cs;
+#pragma unroll
+            for (int j = 0; j < JK; ++j) kc[mb][j] = load_chunk<16>(kr + (lq + 4 * j) * 16);
+            if constexpr (KT != KVDEC_F16)
+                kr_s[mb] = load_chunk<SB>(reinterpret_cast<const uint8_t*>(a.ks) + (cell[mb] * a.n_kv_heads + g) * SB);
+        }
+    };
+    auto load_v = [&](const int64_t (&cell)[2]) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
             const uint8_t* vr = vbase + cell[mb] * a.v_cs;
 #pragma unroll
-            for (int j = 0; j < JK; ++j) {
-                const int c = lq + 4 * j;
-                kc[mb][j] = valid[mb] ? load_chunk<16>(kr + c * 16) : zero_chunk<16>();
-                if constexpr (KT != KVDEC_F16)
-                    kd[mb][j] = valid[mb] ? a.ks[(cell[mb] * a.n_kv_heads + g) * NB + (c * EK) / kBlock] : 0;
-            }
+            for (int j = 0; j < JV; ++j) vc[mb][j] = load_chunk<16>(vr + (lq + 4 * j) * 16);
+            if constexpr (VT != KVDEC_F16)
+                vr_s[mb] = load_chunk<SB>(reinterpret_cast<const uint8_t*>(a.vs) + (cell[mb] * a.n_kv_heads + g) * SB);
+        }
+    };
+
+    int32_t raw_next[2] = {0, 0};
+    int64_t cell[2] = {0, 0};
+    bool valid[2] = {false, false};
+    if (n_steps > 0) {
 #pragma unroll
-            for (int j = 0; j < JV; ++j) {
-                const int c = lq + 4 * j;
-                vc[mb][j] = valid[mb] ? load_chunk<16>(vr + c * 16) : zero_chunk<16>();
-                if constexpr (VT != KVDEC_F16)
-                    vd[mb][j] = valid[mb] ? a.vs[(cell[mb] * a.n_kv_heads + g) * NB + (c * EV) / kBlock] : 0;
+        for (int mb = 0; mb < 2; ++mb) {
+            resolve(base0, mb, fetch(base0, mb), cell[mb], valid[mb]);
+            raw_next[mb] = fetch(base0 + kTile, mb);
+        }
+        load_k(cell);
+        __builtin_amdgcn_sched_barrier(0);  // same issue order as in the loop: K, then V
+        load_v(cell);
+        if constexpr (IND) {
+            // Land the step-1 entries here, behind an opaque copy: entering the
+            // loop with a load still pending on them would make the compiler
+            // wait for every prefetched K / V load at the top of each step.
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                int32_t t;
+                asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(raw_next[mb]));
+                raw_next[mb] = t;
             }
+        }
+    }
+
+    for (int st = 0; st < n_steps; ++st) {
+        const int64_t base = base0 + (int64_t)st * kTile;
+        const uint64_t vm0 = __ballot(valid[0]), vm1 = __ballot(valid[1]);
+        int32_t raw2[2];
+        int64_t ncell[2];
+        bool nvalid[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            raw2[mb] = fetch(base + 2 * kTile, mb);
+            resolve(base + kTile, mb, raw_next[mb], ncell[mb], nvalid[mb]);
         }
 
         // S^T for the two blocks.
@@ -889,7 +971,7 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
 #pragma unroll
             for (int j = 0; j < JK; ++j) {
                 h2 kp[EK / 2];
-                dequant16<KT>(kc[mb][j], KT == KVDEC_F16 ? 0 : kd[mb][j], kp);
+                dequant16<KT>(kc[mb][j], scale_of<KT, SB>(kr_s[mb], j, lq), kp);
 #pragma unroll
                 for (int sub = 0; sub < EK / 8; ++sub) {
                     h8 av;
@@ -902,6 +984,9 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
                 }
             }
         }
+        load_k(ncell);  // K of the next step (its registers are free now)
+        // phase fence for the scheduler: V data is consumed only below
+        __builtin_amdgcn_sched_barrier(0);
 
         // Scores of head li for cells 4*lq + e of each block (log2 units).
         float sc[8];
@@ -916,15 +1001,17 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
         for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sc[e]);
         mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float mn = fmaxf(m_h, mt);
-        const float alpha = (mn == kNegInf) ? 1.f : exp2_fast(m_h - mn);
+        const bool bump = mt > m_h + kLazy;  // also the first finite score
+        const float mn = bump ? mt : m_h;
+        const float alpha = bump ? exp2_fast(m_h - mn) : 1.f;
+        const bool rescale = bump && m_h != kNegInf;
         m_h = mn;
         h8 pa;
         float lsum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-            const float p0 = (sc[e] == kNegInf) ? 0.f : exp2_fast(sc[e] - mn + kPOff);
-            const float p1 = (sc[e + 1] == kNegInf) ? 0.f : exp2_fast(sc[e + 1] - mn + kPOff);
+            const float p0 = (sc[e] == kNegInf) ? 0.f : exp2_fast(sc[e] - mn + kMPOff);
+            const float p1 = (sc[e + 1] == kNegInf) ? 0.f : exp2_fast(sc[e + 1] - mn + kMPOff);
             const h2 pp = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
             pa[e] = pp.x;
             pa[e + 1] = pp.y;
@@ -934,7 +1021,7 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
         lsum += __shfl_xor(lsum, 32);
         l_h = l_h * alpha + lsum;
         // O rows held by this lane are heads 4*lq + e: rescale with their alphas.
-        if (__ballot(alpha != 1.f) != 0) {
+        if (__ballot(rescale) != 0) {
             float ae[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) ae[e] = __shfl(alpha, 4 * lq + e);
@@ -944,6 +1031,7 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
                 for (int e = 0; e < 4; ++e) oacc[nb][e] *= ae[e];
         }
 
+        __builtin_amdgcn_sched_barrier(0);
         // V^ rows of the step -> LDS (row = 16*block + cell), f16.
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
@@ -951,7 +1039,14 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
             for (int j = 0; j < JV; ++j) {
                 const int c = lq + 4 * j;
                 h2 vp[EV / 2];
-                dequant16<VT>(vc[mb][j], VT == KVDEC_F16 ? 0 : vd[mb][j], vp);
+                if constexpr (VT == KVDEC_F16) {
+                    Chunk<16> x = vc[mb][j];
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) x.w[w] = valid[mb] ? x.w[w] : 0u;
+                    dequant16<VT>(x, 0, vp);
+                } else {
+                    dequant16<VT>(vc[mb][j], valid[mb] ? scale_of<VT, SB>(vr_s[mb], j, lq) : (uint16_t)0, vp);
+                }
                 uint4* dst = reinterpret_cast<uint4*>(vst + (16 * mb + li) * VSTR + c * EV * 2);
 #pragma unroll
                 for (int w = 0; w < EV / 8; ++w)
@@ -960,6 +1055,7 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
                                         __builtin_bit_cast(uint32_t, vp[4 * w + 3]));
             }
         }
+        load_v(ncell);  // V of the next step
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -987,6 +1083,13 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            raw_next[mb] = raw2[mb];
+            cell[mb] = ncell[mb];
+            valid[mb] = nvalid[mb];
+        }
     }
 
     // Each wave is one stream: (m2, l, o) of heads < G -> LDS, then merge.
@@ -996,17 +1099,17 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
     float (*sm_o)[G][D] = reinterpret_cast<float (*)[G][D]>(smem + 4 * G * 4 * 2);
     if (lq == 0 && li < G) {
         sm_m[wave][li] = m_h;
-        sm_l[wave][li] = l_h * kPOffInv;
+        sm_l[wave][li] = l_h * kMPOffInv;
     }
 #pragma unroll
     for (int nb = 0; nb < NNB; ++nb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int h = 4 * lq + e;
-            if (h < G) sm_o[wave][h][16 * nb + li] = oacc[nb][e] * kPOffInv;
+            if (h < G) sm_o[wave][h][16 * nb + li] = oacc[nb][e] * kMPOffInv;
         }
     __syncthreads();
-    finish_split<D, G, 4>(a, sa, s, g, split, row0, sm_m, sm_l, sm_o, sm_last);
+    finish_split<D, G, 4, D>(a, sa, s, g, split, row0, sm_m, sm_l, sm_o, sm_last);
 }
 
 // kvdec_merge: one workgroup per row, one thread per element of head_dim.
@@ -1047,10 +1150,14 @@ constexpr bool use_mfma() {
 
 template <int D, int G, int KT, int VT>
 int launch_one(const SplitArgs& a, void* stream) {
-    if constexpr (use_mfma<D, G>())
-        hipLaunchKernelGGL((split_mfma_kernel<D, G, KT, VT>), dim3(a.n_workgroups), dim3(kThreads), 0,
-                           (hipStream_t)stream, a);
-    else
+    if constexpr (use_mfma<D, G>()) {
+        if (a.plan)
+            hipLaunchKernelGGL((split_mfma_kernel<D, G, KT, VT, true>), dim3(a.n_workgroups), dim3(kThreads), 0,
+                               (hipStream_t)stream, a);
+        else
+            hipLaunchKernelGGL((split_mfma_kernel<D, G, KT, VT, false>), dim3(a.n_workgroups), dim3(kThreads), 0,
+                               (hipStream_t)stream, a);
+    } else
         hipLaunchKernelGGL((split_kernel<D, G, KT, VT>), dim3(a.n_workgroups), dim3(kThreads), 0,
                            (hipStream_t)stream, a);
     return (int)hipGetLastError();
