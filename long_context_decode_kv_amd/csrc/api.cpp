@@ -200,6 +200,8 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
     a.part_l = reinterpret_cast<float*>(ws + p.off_parts_l);
     a.part_o_bytes = (int64_t)p.parts_o_bytes;
     a.tickets = reinterpret_cast<uint32_t*>(ws + p.off_tickets);
+    a.ctickets = a.tickets + (size_t)p.n_slots * p.n_kv_heads;
+    a.crec_base = p.crec_base;
     a.n_slots = p.n_slots;
     a.slot_base = 0;
     a.n_workgroups = p.n_workgroups;
@@ -304,6 +306,8 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
             t.part_l = a.part_l;
             t.part_o_bytes = a.part_o_bytes;
             t.tickets = a.tickets;
+            t.ctickets = a.ctickets;
+            t.crec_base = a.crec_base;
             t.n_slots = 1;
             t.slot_base = s;
             const int32_t tiles = (int32_t)((nc + kvdec::kTile - 1) / kvdec::kTile);
@@ -315,6 +319,8 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
             t.slot[0].wg_begin = 0;
             t.slot[0].part_begin = 0;
             t.slot[0].to_acc = (c + 1 < n_chunks) ? 1 : 0;
+            t.slot[0].n_clusters = kvdec::merge_clusters(splits, kvdec::merge_chunk(D, p.group));
+            t.slot[0].cl_begin = 0;
             t.n_workgroups = splits * p.n_kv_heads;
             t.acc_in = acc[c % 2];
             t.acc_out = acc[(c + 1) % 2];

@@ -26,15 +26,34 @@ inline constexpr int64_t row_bytes(int type, int head_dim) {
 }
 inline constexpr bool is_scaled(int type) { return type != KVDEC_F16; }
 
+// Split records one merge round reads: a merging workgroup issues the loads
+// of this many records before it waits (UB records per thread and float4
+// column, TS threads per column).
+constexpr int merge_chunk(int head_dim, int group) {
+    const int nv = group * head_dim / 4;  // float4 columns of a record's o
+    const int ts = nv >= kThreads ? 1 : kThreads / nv;
+    const int cols = (nv + kThreads - 1) / kThreads;
+    const int ub = cols == 1 ? 32 : 32 / cols;
+    return ub * ts < 64 ? ub * ts : 64;
+}
+// Clusters per (slot, KV head): one level of merging while it takes at most
+// two rounds, else clusters of merge_chunk splits merged first, each into a
+// cluster record, and the cluster records merged last.
+constexpr int merge_clusters(int n_splits, int chunk) {
+    return n_splits <= 2 * chunk ? 1 : (n_splits + chunk - 1) / chunk;
+}
+
 // Per-slot launch description, passed to the split kernel by value.
 struct SlotArg {
-    int64_t first;     // contiguous: first cell; indirect: first plan entry
-    int64_t n;         // contiguous: occupied cells; indirect: plan entries
-    int32_t n_tiles;   // ceil(n / 128)
-    int32_t n_splits;  // splits per KV head (>= 1)
-    int32_t wg_begin;  // first workgroup of this slot (n_kv_heads * n_splits of them)
+    int64_t first;       // contiguous: first cell; indirect: first plan entry
+    int64_t n;           // contiguous: occupied cells; indirect: plan entries
+    int32_t n_tiles;     // ceil(n / 128)
+    int32_t n_splits;    // splits per KV head (>= 1)
+    int32_t wg_begin;    // first workgroup of this slot (n_kv_heads * n_splits of them)
     int32_t part_begin;  // first partial record of this slot
-    int32_t to_acc;    // 1: the slot's result goes to acc_out (more partials follow)
+    int32_t to_acc;      // 1: the slot's result goes to acc_out (more partials follow)
+    int32_t n_clusters;  // merge_clusters(n_splits, merge_chunk(D, G))
+    int32_t cl_begin;    // first cluster (ticket and record) of this slot
     int32_t pad;
 };
 
@@ -54,6 +73,9 @@ struct SplitArgs {
     float* part_l;           //   sum [record][G]
     int64_t part_o_bytes;    // bytes of the o region (bound of its buffer resource)
     uint32_t* tickets;       // one per (slot, KV head)
+    uint32_t* ctickets;      // one per cluster of splits
+    int32_t crec_base;       // record index of cluster 0's record
+    int32_t pad1;
     float* out;              // [slots][Hq][D] or null
     float* lse;              // [slots][Hq] or null
     float* pm;               // whole-call partial (m natural units, l, o) or null
@@ -123,6 +145,8 @@ struct kvdec_plan {
     // acc0 / acc1: running partials (ping-pong) of the window + tail chain.
     size_t off_tickets = 0, off_parts = 0, off_acc0 = 0, off_acc1 = 0, off_ring = 0;
     int32_t n_part_capacity = 0;     // partial records the parts region holds
+    int32_t crec_base = 0;           // record index of the first cluster record
+    int32_t n_cluster_capacity = 0;  // cluster tickets / records reserved
     size_t off_parts_m = 0, off_parts_l = 0, parts_o_bytes = 0;
     size_t ring_slot_bytes = 0, ring_k = 0, ring_v = 0, ring_ks = 0, ring_vs = 0;
     size_t workspace_bytes = 0;

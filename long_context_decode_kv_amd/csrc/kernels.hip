@@ -267,20 +267,25 @@ __device__ __forceinline__ float4 ld_dev4(__amdgpu_buffer_rsrc_t r, int64_t off_
     return make_float4(v.x, v.y, v.z, v.w);
 }
 
-// Last-workgroup merge of the n_splits partial records of one (slot, KV
-// head).  The records were written by workgroups that may sit on other
+// Merge of `count` consecutive partial records of one (slot, KV head),
+// starting at record rec0, by the last workgroup to finish among those that
+// wrote them.  The records were written by workgroups that may sit on other
 // XCDs, so every load here goes out to memory; the merge is organised so
-// that each chunk of splits costs one round trip: a thread first issues the
-// loads of all its o columns for the chunk, then the (m, l) loads, and only
-// then waits.  Thread -> (float4 column, split residue class); the running
-// maximum and sums per head are kept in LDS across chunks.
+// that each chunk of merge_chunk(D, G) records costs one round trip: a
+// thread first issues the loads of all its o columns for the chunk, then
+// the (m, l) loads, and only then waits.  Thread -> (float4 column, record
+// residue class); the running maximum and sums per head are kept in LDS
+// across chunks.  The result goes to the outputs (dest < 0) or, merged but
+// not normalised, to record `dest` (a cluster record).
 template <int D, int G>
-__device__ void merge_splits(const SplitArgs& a, const SlotArg& sa, int s, int g, int64_t row0, int n_splits) {
+__device__ void merge_records(const SplitArgs& a, const SlotArg& sa, int64_t row0, int64_t rec0, int count,
+                              int64_t dest) {
     constexpr int NV = G * D / 4;                           // float4 columns of o
     constexpr int TS = NV >= kThreads ? 1 : kThreads / NV;  // threads per column
     constexpr int COLS = (NV + kThreads - 1) / kThreads;    // columns per thread
-    constexpr int UB = COLS == 1 ? 32 : 16 / COLS;          // splits per thread per chunk
-    constexpr int SPC = 64 < UB * TS ? 64 : UB * TS;        // splits per chunk (one per lane)
+    constexpr int UB = COLS == 1 ? 32 : 32 / COLS;          // records per thread per chunk
+    constexpr int SPC = merge_chunk(D, G);                  // records per chunk (one per lane)
+    static_assert(SPC == (64 < UB * TS ? 64 : UB * TS), "merge chunk");
     __shared__ float f_m[64 * G];
     __shared__ float run_m[G], run_l[G], scale_old[G];
     __shared__ float4 red[TS > 1 ? kThreads : 1];
@@ -290,7 +295,7 @@ __device__ void merge_splits(const SplitArgs& a, const SlotArg& sa, int s, int g
     const int col = tid % (NV < kThreads ? NV : kThreads);
     const int cls = tid / (NV < kThreads ? NV : kThreads);  // threads with cls >= TS idle
     const __amdgpu_buffer_rsrc_t rs = part_rsrc(a);
-    const int64_t rec0 = sa.part_begin + (int64_t)g * n_splits;
+    const int n_splits = count;
 
     float4 acc[COLS];
 #pragma unroll
@@ -391,13 +396,31 @@ __device__ void merge_splits(const SplitArgs& a, const SlotArg& sa, int s, int g
             const int d0 = 4 * v - h * D;
             float M = run_m[h], L = run_l[h];
             float4 O = acc[c];
-            merge_acc_in(a, row0 + h, d0, D, M, L, O);
-            emit4(a, sa.to_acc, row0 + h, d0, D, M, L, O);
+            if (dest < 0) {
+                merge_acc_in(a, row0 + h, d0, D, M, L, O);
+                emit4(a, sa.to_acc, row0 + h, d0, D, M, L, O);
+            } else {
+                st_dev4(rs, (dest * (G * D) + 4 * v) * 4, O);
+                if (d0 == 0) {
+                    st_dev(a.part_m + dest * G + h, M);
+                    st_dev(a.part_l + dest * G + h, L);
+                }
+            }
         }
     }
-    if (tid == 0)
-        __hip_atomic_store(a.tickets + (int64_t)(a.slot_base + s) * a.n_kv_heads + g, 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One arrival at a ticket that counts `expected` arrivals; true (for the
+// whole workgroup) in the last one to arrive, which also resets the ticket.
+__device__ __forceinline__ bool last_arrival(uint32_t* ticket, int expected, int& sm_last) {
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = prev == (uint32_t)(expected - 1);
+        if (last) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm_last = last;
+    }
+    __syncthreads();
+    return sm_last != 0;
 }
 
 // End of a split: merge the NS cell streams left in LDS (m2, l, o per
@@ -446,17 +469,31 @@ __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& 
     }
     if (single) return;
 
-    // Last workgroup of the (slot, KV head) merges every split.
+    // Records are published (stores complete) before the arrival is counted.
     wait_stores();
     __syncthreads();
-    uint32_t* ticket = a.tickets + (int64_t)(a.slot_base + s) * a.n_kv_heads + g;
-    if (tid == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sm_last = (prev == (uint32_t)(n_splits - 1));
+    uint32_t* gticket = a.tickets + (int64_t)(a.slot_base + s) * a.n_kv_heads + g;
+    const int64_t srec0 = sa.part_begin + (int64_t)g * n_splits;
+    const int ncl = sa.n_clusters;
+    if (ncl <= 1) {
+        // the last workgroup of the (slot, KV head) merges every split
+        if (!last_arrival(gticket, n_splits, sm_last)) return;
+        merge_records<D, G>(a, sa, row0, srec0, n_splits, -1);
+        return;
     }
+    // two levels: the last of each cluster of splits merges the cluster into
+    // a cluster record; the last cluster merger merges the cluster records
+    constexpr int CH = merge_chunk(D, G);
+    const int cid = split / CH;
+    const int c0 = cid * CH;
+    const int cn = (n_splits - c0) < CH ? (n_splits - c0) : CH;
+    const int64_t cidx = sa.cl_begin + (int64_t)g * ncl + cid;
+    if (!last_arrival(a.ctickets + cidx, cn, sm_last)) return;
+    merge_records<D, G>(a, sa, row0, srec0 + c0, cn, a.crec_base + cidx);
+    wait_stores();
     __syncthreads();
-    if (!sm_last) return;
-    merge_splits<D, G>(a, sa, s, g, row0, n_splits);
+    if (!last_arrival(gticket, ncl, sm_last)) return;
+    merge_records<D, G>(a, sa, row0, a.crec_base + sa.cl_begin + (int64_t)g * ncl, ncl, -1);
 }
 
 

@@ -198,6 +198,13 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
     }
     plan.n_workgroups = (int32_t)wgs;
     plan.n_part_records = (int32_t)wgs;
+    const int chunk = merge_chunk(p.head_dim, group);
+    int64_t clusters = 0;
+    for (auto& sa : plan.slots) {
+        sa.n_clusters = merge_clusters(sa.n_splits, chunk);
+        sa.cl_begin = (int32_t)clusters;
+        if (sa.n_clusters > 1) clusters += (int64_t)sa.n_clusters * p.n_kv_heads;
+    }
 
     // ---- host tail
     plan.has_tail = has_tail;
@@ -232,14 +239,20 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
         plan.chunk_tiles_per_split = (int32_t)ctps;
         plan.chunk_splits = (int32_t)std::max<int64_t>(1, ceil_div(chunk_tiles, ctps));
         part_capacity = std::max<int64_t>(part_capacity, (int64_t)plan.chunk_splits * p.n_kv_heads);
+        const int cc = merge_clusters(plan.chunk_splits, chunk);
+        if (cc > 1) clusters = std::max<int64_t>(clusters, (int64_t)cc * p.n_kv_heads);
     }
+    // cluster records follow the split records
+    plan.crec_base = (int32_t)part_capacity;
+    plan.n_cluster_capacity = (int32_t)clusters;
+    part_capacity += clusters;
     plan.n_part_capacity = (int32_t)part_capacity;
 
     // ---- workspace layout
     const size_t D = (size_t)p.head_dim;
     size_t off = 0;
     plan.off_tickets = off;
-    off = align_up(off + sizeof(uint32_t) * (size_t)p.n_slots * p.n_kv_heads, 256);
+    off = align_up(off + sizeof(uint32_t) * ((size_t)p.n_slots * p.n_kv_heads + (size_t)clusters), 256);
     plan.off_parts = off;
     plan.parts_o_bytes = sizeof(float) * (size_t)part_capacity * group * D;
     if (plan.parts_o_bytes >= (1ull << 31)) {

@@ -205,3 +205,18 @@ def test_workspace_reuse_across_plans(K):
         check(*c2.run(K, plan=p2, ws=ws), *c2.oracle())
     tick = ws[:4 * 2 * 8].view(torch.int32)
     assert int(tick.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("kind,d,g,occ", [(O.Q8_B32, 256, 6, [9000, 300]), (O.F16, 128, 4, [20000]),
+                                          (O.F16, 128, 8, [9000, 1]), (O.Q4_B32, 256, 8, [6000])])
+def test_two_level_merge(K, kind, d, g, occ):
+    """One-tile splits: more splits per KV head than two merge rounds hold,
+    so clusters of splits are merged first and the cluster records last."""
+    c = Case(60 + d + g + kind, 2 * g, 2, d, kind=kind, occupied=occ)
+    out, lse = c.run(K, tiles_per_split=1)
+    check(out, lse, *c.oracle())
+    # close to a plan whose splits merge in one level (f16 softmax weights
+    # are rounded against each stream's own reference maximum, so different
+    # split boundaries round differently)
+    out1, lse1 = c.run(K, tiles_per_split=max(1, -(-max(occ) // 128) // 8))
+    check(out, lse, out1, lse1, tol=1e-3)

@@ -99,3 +99,12 @@ def test_tail_call_repeated_on_one_workspace(K):
     check(*outs[0], *c1.oracle())
     check(*outs[1], *c2.oracle())
     assert np.array_equal(outs[0][0], outs[2][0])
+
+
+def test_quantized_tail_two_level_merge(K):
+    """GQA-6, head_dim 256: a full 8192-cell tail chunk is cut into one-tile
+    splits per KV head, merged in two levels."""
+    c = Case(57, 24, 4, 256, kind=O.Q8_B32, occupied=[11000])
+    out, lse, p = run_tail(K, c, window=[(9000, 2000)], tail=[(0, 9000)], chunk=8192, depth=2)
+    assert p.info()["n_tail_chunks"] == 2
+    check(out, lse, *c.oracle())
