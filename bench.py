@@ -18,6 +18,10 @@ Workloads (synthetic N(0, 1) data of the named model's attention shape):
                     records, block-scaled int8 / 4-bit K and V
   rolling-ctx40960  qwen3-8b shape at ctx 40960: newest 14000 cells resident,
                     oldest 26960 streamed from pinned host memory per layer
+  qwen3-8b-ctx16k-1launch
+                    secondary figure for the qwen3-8b-ctx16k data: all 36
+                    layers as 36 slots of ONE kvdec_attend call (ignores the
+                    layer-to-layer dependency of a real decode step)
 """
 
 import argparse
@@ -49,6 +53,50 @@ def measure_h2d(torch, nbytes=256 << 20, reps=5):
     b.record()
     torch.cuda.synchronize()
     return round(nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9, 2)
+
+
+def measure_read_ceiling(torch, nbytes, launches):
+    """Streaming-read ceiling for the same bytes per launch and launches per
+    step: `launches` back-to-back reads (kvprobe_read, 16-byte loads) of
+    distinct buffers of `nbytes` each, rotated over >= 1 GiB so the 256 MB
+    MALL cannot serve repeats; the best over a few launch shapes.  Returns
+    (GB/s, us per launch, shape)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "long_context_decode_kv_amd", "libkvprobe.so"))
+    f = lib.kvprobe_read
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    nb = -(-nbytes // 16) * 16
+    copies = max(2, -(-(1 << 30) // nb))
+    reps = max(2, -(-(20 << 30) // (nb * launches)))
+    bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    shapes = [(wgs, u) for wgs in (512, 1024, 2048) for u in (4, 8, 16)]
+    sink = torch.empty(max(w for w, _ in shapes) * 256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = None
+    for wgs, u in shapes:
+        def run(n):
+            k = 0
+            for _ in range(n):
+                for _ in range(launches):
+                    rc = f(bufs[k % copies].data_ptr(), nb, wgs, u, sink.data_ptr(), stream.cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError(f"kvprobe_read failed: {rc}")
+                    k += 1
+            return k
+        run(1)
+        torch.cuda.synchronize()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        k = run(reps)
+        e.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(e) * 1e3 / k
+        if best is None or us < best[1]:
+            best = (round(nb / (us * 1e-6) / 1e9, 1), round(us, 3), f"{wgs} workgroups x 256 threads, {u} loads "
+                                                                     f"of 16 B in flight per thread")
+    del bufs
+    return best
 
 
 def log(*a):
@@ -254,12 +302,54 @@ class RollingWindow(ContiguousModel):
                  lse=self.lse[layer], k_tail=self.hk[layer], v_tail=self.hv[layer], copy_stream=self.copy_stream)
 
 
+class ContiguousModelOneLaunch(ContiguousModel):
+    """Secondary figure: every layer of a ContiguousModel as one slot of a
+    single launch (one cache allocation, layer l's cells at l * capacity)."""
+
+    def __init__(self, name, layers, hq, hkv, d, capacity, occupied):
+        super().__init__(name, layers, hq, hkv, d, capacity, occupied)
+        self.model_layers, self.layers = layers, 1
+
+    def config(self):
+        c = super().config()
+        c.update({"layers": self.model_layers, "launch": f"all {self.model_layers} layers as slots of one call",
+                  "figure": "secondary: ignores the layer-to-layer dependency of a real decode step"})
+        return c
+
+    def algorithmic_bytes_per_launch(self):
+        return algorithmic_bytes(self.occupied * self.model_layers, self.hkv, self.d, 0, self.model_layers, self.hq)
+
+    def setup(self, K, torch, seed0):
+        from long_context_decode_kv_amd import synth
+        L, cap = self.model_layers, self.capacity
+        kc = torch.empty((L * cap, self.hkv, self.d), dtype=torch.float16, device="cuda")
+        vc = torch.empty_like(kc)
+        q = torch.empty((L, self.hq, self.d), device="cuda")
+        for layer in range(L):
+            s = seed0 * 100 + layer
+            synth.device_f16_cache(3 * s, cap, self.hkv, self.d, out=kc[layer * cap:(layer + 1) * cap])
+            synth.device_f16_cache(3 * s + 1, cap, self.hkv, self.d, out=vc[layer * cap:(layer + 1) * cap])
+            q[layer] = synth.device_q(3 * s + 2, 1, self.hq, self.d)[0]
+        self.k, self.v, self.q = [kc], [vc], [q]
+        self.out = [torch.empty(L, self.hq, self.d, device="cuda")]
+        self.lse = [torch.empty(L, self.hq, device="cuda")]
+        self.plan = K.plan(self.hq, self.hkv, self.d, L, L * cap, n_occupied=[self.occupied] * L,
+                           cell_begin=[layer * cap for layer in range(L)])
+        self.ws = K.workspace(self.plan)
+
+    def oracle_sample(self, budget_s):
+        done, el, sample = super().oracle_sample(budget_s)
+        return done / self.model_layers, el, sample
+
+
 WORKLOADS = {
     "qwen3-8b-ctx16k": lambda: ContiguousModel("qwen3-8b-ctx16k", 36, 32, 8, 128, 16384, 13100),
     "qwen2.5-14b-1m": lambda: ContiguousModel("qwen2.5-14b-1m", 48, 40, 8, 128, 524288, 524288),
     "gqa6-q8": lambda: Gqa6Quant("gqa6-q8", 1),
     "gqa6-q4": lambda: Gqa6Quant("gqa6-q4", 2),
     "rolling-ctx40960": lambda: RollingWindow(),
+    "qwen3-8b-ctx16k-1launch": lambda: ContiguousModelOneLaunch("qwen3-8b-ctx16k-1launch", 36, 32, 8, 128, 16384,
+                                                                13100),
 }
 
 
@@ -351,19 +441,23 @@ def main():
     n_cycles = max(1, args.steps // cycle)
     steps = n_cycles * cycle
     log(f"[bench] timing {steps} steps ({mode})")
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_cycles + 1)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(n_cycles):
+    evs[0].record(stream)
+    for c in range(n_cycles):
         if graph is not None:
             graph.replay()
         else:
             one_cycle()
-    ev1.record(stream)
+        evs[c + 1].record(stream)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
-    ms_per_step = ev0.elapsed_time(ev1) / steps
+    ms_per_step = evs[0].elapsed_time(evs[-1]) / steps
+    per_cycle = sorted(evs[c].elapsed_time(evs[c + 1]) * 1e3 / cycle for c in range(n_cycles))  # us per step
+
+    def pct(p):
+        return round(per_cycle[min(len(per_cycle) - 1, int(p * len(per_cycle)))], 2)
 
     # timed region 2: every launch bracketed by its own events on its stream
     # (adds the dispatch overhead of an isolated launch)
@@ -391,6 +485,7 @@ def main():
     gbs = bytes_step / (ms_per_step * 1e-3) / 1e9
     achieved = bytes_launch / (avg_us * 1e-6) / 1e9
     traffic = committed_traffic(wl.name)
+    ceiling_gbs, ceiling_us, ceiling_shape = measure_read_ceiling(torch, bytes_launch, launches_per_step)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -410,6 +505,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "us_per_step_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
         "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -425,7 +521,11 @@ def main():
                                                     else "split_kernel", wl.d, wl.hq // wl.hkv, KIND[wl.kind],
                                                     KIND[wl.kind]),
                      "algorithmic_bytes_per_launch": bytes_launch, "launches_per_step": launches_per_step,
-                     "avg_launch_us": round(avg_us, 3), "isolated_launch_event_us": round(bracketed_us, 3)},
+                     "avg_launch_us": round(avg_us, 3), "isolated_launch_event_us": round(bracketed_us, 3),
+                     "read_ceiling": {"method": "kvprobe_read: plain 16-byte streaming read of the same bytes per "
+                                                "launch, same launches per step, best launch shape",
+                                      "shape": ceiling_shape, "gbs": ceiling_gbs, "us_per_launch": ceiling_us,
+                                      "frac_of_ceiling": round(achieved / ceiling_gbs, 4)}},
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall_s, 4),
         "kernel_source_sha256_16": kernel_source_hash(),

@@ -5,7 +5,8 @@
 Every translation unit is compiled for gfx950 with the packed-fp32 VALU
 operations switched off (hipcc's host pass warns that it does not know the
 feature; that is harmless).  The objects go to ``_build/`` at the repository
-root and the library to ``long_context_decode_kv_amd/libkvdec.so``.
+root, the library to ``long_context_decode_kv_amd/libkvdec.so`` and the
+streaming-read probe used by the benchmark to ``libkvprobe.so`` beside it.
 """
 
 import os
@@ -20,6 +21,9 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvdec.so")
 
 SOURCES = ["kernels.hip", "api.cpp", "plan.cpp"]
+# the streaming-read probe (bandwidth ceiling for the benchmark) is a library of its own
+PROBE_SOURCES = ["probe.hip"]
+PROBE_LIB = os.path.join(PKG, "libkvprobe.so")
 
 FLAGS = [
     "--offload-arch=gfx950",
@@ -53,19 +57,20 @@ def _compile(src, extra):
 
 def build(verbose=False, extra=()):
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        results = list(ex.map(lambda s: _compile(s, list(extra)), SOURCES))
-    objs = [o for o, _ in results]
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        results = dict(zip(srcs, ex.map(lambda s: _compile(s, list(extra)), srcs)))
     if verbose:
-        for _, log in results:
+        for _, log in results.values():
             if log.strip():
                 print(log, file=sys.stderr)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    for lib, names in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+        tmp = lib + ".tmp"
+        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [results[n][0] for n in names]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -32,6 +32,26 @@ def test_exports_every_declared_function():
     assert K.version() == 10000
 
 
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """The streaming-read probe (include/kvprobe.h) loads, exports what its
+    header declares, and rejects invalid arguments before any launch."""
+    import ctypes
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "kvprobe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(kvprobe_\w+)\s*\(", text, flags=re.M)))
+    assert names == ["kvprobe_read"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "long_context_decode_kv_amd", "libkvprobe.so"))
+    f = lib.kvprobe_read
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    fake = 1 << 20
+    assert f(None, 1024, 4, 4, fake, None) == -1          # null buffer
+    assert f(fake, 1000, 4, 4, fake, None) == -1          # not a multiple of 16
+    assert f(fake + 8, 1024, 4, 4, fake, None) == -1      # misaligned
+    assert f(fake, 1024, 0, 4, fake, None) == -1          # no workgroups
+    assert f(fake, 1024, 4, 3, fake, None) == -1          # unsupported unroll
+    assert f(fake, 1024, 4, 4, None, None) == -1          # null sink
+
+
 def test_strerror_codes():
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert K.lib.kvdec_strerror(code).decode() not in ("", "unknown status")
