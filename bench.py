@@ -365,10 +365,11 @@ def kernel_source_hash():
 def committed_traffic(workload):
     """HBM bytes per dispatch from the committed rocprofv3 --pmc summary of
     this workload, if it was taken with the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"split_kernel_{workload}_pmc.txt")
-    if not os.path.exists(path):
+    import glob
+    paths = glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}_pmc.txt"))
+    if len(paths) != 1:
         return None
-    text = open(path).read()
+    text = open(paths[0]).read()
     m = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
     t = re.search(r"hbm_bytes_per_dispatch:\s*([0-9.]+)", text)
     if not m or not t or m.group(1) != kernel_source_hash():
@@ -387,6 +388,7 @@ def main():
     ap.add_argument("--mode", default="graph", choices=["graph", "eager"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true", help="skip the streaming-read ceiling (profiling runs)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -485,7 +487,12 @@ def main():
     gbs = bytes_step / (ms_per_step * 1e-3) / 1e9
     achieved = bytes_launch / (avg_us * 1e-6) / 1e9
     traffic = committed_traffic(wl.name)
-    ceiling_gbs, ceiling_us, ceiling_shape = measure_read_ceiling(torch, bytes_launch, launches_per_step)
+    ceiling = None
+    if not args.no_read_ceiling:
+        c_gbs, c_us, c_shape = measure_read_ceiling(torch, bytes_launch, launches_per_step)
+        ceiling = {"method": "kvprobe_read: plain 16-byte streaming read of the same bytes per launch, same "
+                             "launches per step, best launch shape",
+                   "shape": c_shape, "gbs": c_gbs, "us_per_launch": c_us, "frac_of_ceiling": round(achieved / c_gbs, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -522,10 +529,7 @@ def main():
                                                     KIND[wl.kind]),
                      "algorithmic_bytes_per_launch": bytes_launch, "launches_per_step": launches_per_step,
                      "avg_launch_us": round(avg_us, 3), "isolated_launch_event_us": round(bracketed_us, 3),
-                     "read_ceiling": {"method": "kvprobe_read: plain 16-byte streaming read of the same bytes per "
-                                                "launch, same launches per step, best launch shape",
-                                      "shape": ceiling_shape, "gbs": ceiling_gbs, "us_per_launch": ceiling_us,
-                                      "frac_of_ceiling": round(achieved / ceiling_gbs, 4)}},
+                     "read_ceiling": ceiling},
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall_s, 4),
         "kernel_source_sha256_16": kernel_source_hash(),

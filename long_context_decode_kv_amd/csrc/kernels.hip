@@ -820,6 +820,19 @@ __device__ __forceinline__ void dequant16(const Chunk<16>& c, uint16_t scale_bit
     }
 }
 
+// Workgroup order seen by the work decomposition.  The dispatcher hands
+// workgroups to the 8 XCDs round-robin (workgroup b to XCD b % 8), and each
+// XCD has its own L2.  Renumbering so that consecutive logical indices land
+// on the same XCD puts the KV heads of one split -- which share the cache
+// lines of the cells' block scales and plan entries -- behind one L2.  Only
+// a bijection of [0, n): correctness never depends on the placement.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_logical_index(int b, int n) {
+    const int per = n / kXcds, extra = n % kXcds;
+    const int x = b % kXcds, k = b / kXcds;
+    return (x < extra ? x * (per + 1) : extra * (per + 1) + (x - extra) * per) + k;
+}
+
 // Scale of the 32-element block holding chunk lq + 4j of a row, taken from
 // the row's SB bytes of scales.  int8: 16 elements per chunk, so the block is
 // 2j + lq/2 (dword j); 4-bit: 32 per chunk, block lq + 4j (half lq of dwords 2j, 2j+1).
@@ -860,7 +873,7 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
     const int li = lane & 15;  // row / column index inside a 16-lane group
     const int lq = lane >> 4;  // lane group
 
-    const int wg = blockIdx.x;
+    const int wg = xcd_logical_index(blockIdx.x, a.n_workgroups);
     int s = 0;
     while (s + 1 < a.n_slots && a.slot[s + 1].wg_begin <= wg) ++s;
     const SlotArg sa = a.slot[s];
