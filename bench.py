@@ -16,6 +16,7 @@ Workloads (synthetic N(0, 1) data of the named model's attention shape):
   gqa6-q8 / gqa6-q4 one layer, 24 q / 4 KV heads, head_dim 256, four slots of
                     131072 / 65536 / 20000 / 777 cells in interleaved 128-cell
                     records, block-scaled int8 / 4-bit K and V
+  gqa6-q8k-q4v      the same with int8 K and 4-bit V
   rolling-ctx40960  qwen3-8b shape at ctx 40960: newest 14000 cells resident,
                     oldest 26960 streamed from pinned host memory per layer
   qwen3-8b-ctx16k-1launch
@@ -38,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 KIND = {0: "f16", 1: "q8", 2: "q4"}
+KDESC = {0: "f16", 1: "int8+f16 scale/32", 2: "4-bit+f16 scale/32"}
 
 
 def measure_h2d(torch, nbytes=256 << 20, reps=5):
@@ -123,12 +125,14 @@ def scale_row_bytes(kind, d):
     return 0 if kind == 0 else 2 * (d // 32)
 
 
-def algorithmic_bytes(n_cells_attended, hkv, d, kind, n_slots, hq, plan_entries=0):
+def algorithmic_bytes(n_cells_attended, hkv, d, kind, n_slots, hq, plan_entries=0, v_kind=None):
     """Bytes the method must move for one evaluation: the attended cells' K
     and V codes and scales, the indirect plan (4 B per entry), q (fp32) and
     out (fp32).  Unoccupied cells, hole cells, partials and re-reads are not
     counted."""
-    kv = 2 * n_cells_attended * hkv * (kv_row_bytes(kind, d) + scale_row_bytes(kind, d))
+    vk = kind if v_kind is None else v_kind
+    kv = n_cells_attended * hkv * (kv_row_bytes(kind, d) + scale_row_bytes(kind, d) + kv_row_bytes(vk, d) +
+                                   scale_row_bytes(vk, d))
     return kv + 4 * plan_entries + 2 * 4 * n_slots * hq * d
 
 
@@ -193,24 +197,28 @@ class Gqa6Quant(Workload):
 
     cycle = 4  # steps per captured cycle (one launch per step, caches rotated)
 
-    def __init__(self, name, kind, copies=4):
+    def __init__(self, name, kind, copies=4, v_kind=None):
         self.name, self.kind, self.layers = name, kind, copies
+        self.v_kind = kind if v_kind is None else v_kind
         self.hq, self.hkv, self.d = 24, 4, 256
         self.lengths = [131072, 65536, 20000, 777]
 
     def config(self):
         return {"workload": self.name, "q_heads": 24, "kv_heads": 4, "head_dim": 256, "slots": 4,
-                "cells_per_slot": self.lengths, "kv_dtype": {1: "int8+f16 scale/32", 2: "4-bit+f16 scale/32"}[self.kind],
+                "cells_per_slot": self.lengths,
+                "kv_dtype": ("K " if self.v_kind != self.kind else "") + KDESC[self.kind] +
+                            (" / V " + KDESC[self.v_kind] if self.v_kind != self.kind else ""),
                 "indirect_plan": "128-cell records interleaved round-robin across slots, -1 holes",
                 "rotated_cache_copies": self.layers}
 
     def algorithmic_bytes_per_launch(self):
-        return algorithmic_bytes(sum(self.lengths), self.hkv, self.d, self.kind, 4, self.hq, self.n_entries)
+        return algorithmic_bytes(sum(self.lengths), self.hkv, self.d, self.kind, 4, self.hq, self.n_entries,
+                                 self.v_kind)
 
     def setup(self, K, torch, seed0):
         from long_context_decode_kv_amd import synth
         lists, cap = synth.interleaved_record_lists(self.lengths)
-        self.plan = K.plan(24, 4, 256, 4, cap, k_type=self.kind, v_type=self.kind, cells=lists)
+        self.plan = K.plan(24, 4, 256, 4, cap, k_type=self.kind, v_type=self.v_kind, cells=lists)
         entries, _ = self.plan.cells()
         self.n_entries = len(entries)
         self.plan_cells = torch.from_numpy(entries).cuda()
@@ -218,7 +226,7 @@ class Gqa6Quant(Workload):
         for c in range(self.layers):
             s = seed0 * 100 + c
             self.k.append(synth.device_quant_cache(3 * s, self.kind, cap, 4, 256))
-            self.v.append(synth.device_quant_cache(3 * s + 1, self.kind, cap, 4, 256))
+            self.v.append(synth.device_quant_cache(3 * s + 1, self.v_kind, cap, 4, 256))
             self.q.append(synth.device_q(3 * s + 2, 4, 24, 256))
             self.out.append(torch.empty(4, 24, 256, device="cuda"))
             self.lse.append(torch.empty(4, 24, device="cuda"))
@@ -236,11 +244,11 @@ class Gqa6Quant(Workload):
         n = self.lengths[2]  # the 20000-cell slot, all four KV heads
         q = synth.gen_q(r, 1, 24, 256)
         kc, ks = synth.gen_quant_cache(r, self.kind, n, 4, 256)
-        vc, vs = synth.gen_quant_cache(r, self.kind, n, 4, 256)
+        vc, vs = synth.gen_quant_cache(r, self.v_kind, n, 4, 256)
         t0 = time.perf_counter()
         done = 0
         while True:
-            O.decode_attention(q, [((self.kind, kc, ks), (self.kind, vc, vs), [np.arange(n)])], 4, 1 / 16)
+            O.decode_attention(q, [((self.kind, kc, ks), (self.v_kind, vc, vs), [np.arange(n)])], 4, 1 / 16)
             done += 1
             el = time.perf_counter() - t0
             if el >= budget_s or done >= 4:
@@ -347,6 +355,7 @@ WORKLOADS = {
     "qwen2.5-14b-1m": lambda: ContiguousModel("qwen2.5-14b-1m", 48, 40, 8, 128, 524288, 524288),
     "gqa6-q8": lambda: Gqa6Quant("gqa6-q8", 1),
     "gqa6-q4": lambda: Gqa6Quant("gqa6-q4", 2),
+    "gqa6-q8k-q4v": lambda: Gqa6Quant("gqa6-q8k-q4v", 1, v_kind=2),
     "rolling-ctx40960": lambda: RollingWindow(),
     "qwen3-8b-ctx16k-1launch": lambda: ContiguousModelOneLaunch("qwen3-8b-ctx16k-1launch", 36, 32, 8, 128, 16384,
                                                                 13100),
@@ -517,8 +526,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {0: "f16 KV, fp32 accumulate", 1: "int8 KV (f16 scale per 32), fp32 accumulate",
-                  2: "4-bit KV (f16 scale per 32), fp32 accumulate"}[wl.kind],
+        "dtype": ({0: "f16 KV", 1: "int8 KV (f16 scale per 32)", 2: "4-bit KV (f16 scale per 32)"}[wl.kind]
+                  if getattr(wl, "v_kind", wl.kind) == wl.kind else
+                  f"{KIND[wl.kind]} K / {KIND[wl.v_kind]} V (f16 scale per 32)") + ", fp32 accumulate",
         "data": "synthetic: q ~ N(0,1); K, V ~ N(0,1) rounded to f16 or block-encoded; seeded on-device generator",
         "config": dict(wl.config(), mode=mode, workgroups_per_launch=info["n_workgroups"],
                        tiles_per_split=info["tiles_per_split"]),
@@ -526,7 +536,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "%s<%d,%d,%s,%s>" % ("split_mfma_kernel" if wl.hq // wl.hkv >= 6 and wl.d >= 128
                                                     else "split_kernel", wl.d, wl.hq // wl.hkv, KIND[wl.kind],
-                                                    KIND[wl.kind]),
+                                                    KIND[getattr(wl, "v_kind", wl.kind)]),
                      "algorithmic_bytes_per_launch": bytes_launch, "launches_per_step": launches_per_step,
                      "avg_launch_us": round(avg_us, 3), "isolated_launch_event_us": round(bracketed_us, 3),
                      "read_ceiling": ceiling},

@@ -86,7 +86,12 @@ extern "C" {
  *   built for G <= 8, larger groups give KVDEC_E_UNSUPPORTED.
  * head_dim: 64, 128 or 256.
  * n_slots: 1..KVDEC_MAX_SLOTS (one query row per slot).
- * k_type, v_type: KVDEC_F16 / KVDEC_Q8_B32 / KVDEC_Q4_B32.
+ * k_type, v_type: KVDEC_F16 / KVDEC_Q8_B32 / KVDEC_Q4_B32.  Kernels exist for
+ *   K stored at least as finely as V: equal kinds, or (K, V) = (f16, int8),
+ *   (f16, 4-bit), (int8, 4-bit) -- int8 K with 4-bit V is the pair of the
+ *   resident-compression anchors ("Rolling-KV -- overflow throughput
+ *   evaluations (consolidated)", section 5); other pairs give
+ *   KVDEC_E_UNSUPPORTED.
  * scale: multiplies q.k before the softmax (usually 1/sqrt(head_dim)).
  * capacity_cells: number of device cells addressable through the K/V
  *   pointers of kvdec_attend; every attended cell must lie below it.

@@ -108,7 +108,16 @@ struct MergeArgs {
     float* mo;
 };
 
-// Kernel launchers (kernels.hip).  Return a hipError_t value.
+// Kernel launchers (kernels.hip, split_*.hip).  Return a hipError_t value.
+// Per pair of storage kinds, the launcher of the split-kernel instance for
+// (head_dim, group), or null.
+using SplitLaunchFn = int (*)(const SplitArgs&, void*);
+SplitLaunchFn pick_split_f16(int head_dim, int group);
+SplitLaunchFn pick_split_q8(int head_dim, int group);
+SplitLaunchFn pick_split_q4(int head_dim, int group);
+SplitLaunchFn pick_split_f16_q8(int head_dim, int group);
+SplitLaunchFn pick_split_f16_q4(int head_dim, int group);
+SplitLaunchFn pick_split_q8_q4(int head_dim, int group);
 int launch_split(int head_dim, int group, int k_type, int v_type, const SplitArgs& a, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
 bool split_instance_exists(int head_dim, int group, int k_type, int v_type);

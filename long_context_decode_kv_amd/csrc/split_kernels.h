@@ -1,0 +1,1219 @@
+// Split-KV decode kernels of libkvdec for gfx950 (MI355X), as templates over
+// head_dim, GQA group and K / V storage kinds.  Included by the split_*.hip
+// translation units, each of which instantiates one pair of storage kinds
+// (so the instances compile in parallel), and by kernels.hip for the shared
+// helpers.
+//
+// Split kernel.  One workgroup (4 waves) streams a contiguous range of
+// 128-cell tiles of one (slot, KV head), in steps where each lane holds 4
+// cells and each wave a contiguous run of cells.  R consecutive lanes share
+// one cell and split its head_dim
+// elements into R slices of D/R; every 16-byte (8-byte for 4-bit rows) load
+// of a wave covers whole 128-byte lines of consecutive cells, so the KV
+// stream is read with coalesced 128-bit loads.  The G query rows of the KV
+// head's group are held in every lane (f16-packed, its D/R slice only), so
+// each K row fetched once serves all G query heads ("KVARN KV Performance
+// optimizations", "What was implemented" item 6: decoded K/V reused across
+// query rows).  Scores are reduced over the R lanes of a cell with DPP
+// moves; each group of lanes that shares a cell stream keeps its own online
+// softmax state (m, l, o), and the states are merged at the end of the split
+// with the log-sum-exp rule, first across the wave, then across the 4 waves
+// through LDS.
+//
+// Partials are written as (m2 = running max in log2 units, l, o).  When a
+// (slot, KV head) has several splits, the last workgroup to finish (atomic
+// ticket in the workspace) merges all of them and writes the output, so one
+// launch does the whole evaluation -- the partials carry their max and sum
+// in the same pass and nothing is recomputed ("Rolling-KV -- overflow
+// throughput evaluations (consolidated)", section 3: the log-sum-exp channel
+// replaced a per-tile recompute).
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+
+namespace kvdec {
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kNegInf = -__builtin_inff();
+// Softmax weights are formed as 2^(s - m + kPOff) so that, when they are
+// rounded to f16 for packed dot products, weights down to 2^-29 of the
+// maximum stay normal f16 numbers; l and o carry the same factor, which is
+// removed when a partial leaves the workgroup.
+constexpr float kPOff = 15.0f;
+constexpr float kPOffInv = 1.0f / 32768.0f;
+
+__device__ __forceinline__ h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each group of R consecutive lanes; every lane receives its group's sum.
+template <int R>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (R >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+    if constexpr (R >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+    if constexpr (R >= 8) x += dpp<0x141>(x);  // row_half_mirror
+    if constexpr (R >= 16) x += dpp<0x140>(x); // row_mirror
+    if constexpr (R >= 32) x += __shfl_xor(x, 16);
+    if constexpr (R >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
+
+// Max / sum over the whole wave; every lane receives the result.
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp<0xB1>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    x = fmaxf(x, dpp<0x141>(x));
+    x = fmaxf(x, dpp<0x140>(x));
+    x = fmaxf(x, __shfl_xor(x, 16));
+    return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Cross-workgroup records.  A split's partial record is read by the last
+// workgroup of its (slot, KV head), which may run on another XCD.  The record
+// is written and read with device-scope relaxed atomic accesses, which the
+// hardware keeps coherent across the XCDs' L2 caches without the whole-L2
+// write-back / invalidate that a device-scope fence costs; the writer waits
+// for its stores to complete before the ticket increment that publishes them.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Storage formats: a lane reads its d-slice of a row in chunks of at most 16
+// bytes; EPC elements per chunk (a divisor of the 32-element scale block).
+template <int T, int DL>
+struct Fmt;
+template <int DL>
+struct Fmt<KVDEC_F16, DL> {
+    static constexpr int EPC = DL < 8 ? DL : 8;
+    static constexpr int CB = 2 * EPC;
+    static constexpr bool scaled = false;
+};
+template <int DL>
+struct Fmt<KVDEC_Q8_B32, DL> {
+    static constexpr int EPC = DL < 16 ? DL : 16;
+    static constexpr int CB = EPC;
+    static constexpr bool scaled = true;
+};
+template <int DL>
+struct Fmt<KVDEC_Q4_B32, DL> {
+    static constexpr int EPC = DL < 16 ? DL : 16;
+    static constexpr int CB = EPC / 2;
+    static constexpr bool scaled = true;
+};
+
+template <int CB>
+struct Chunk {
+    uint32_t w[CB / 4];
+};
+
+template <int CB>
+__device__ __forceinline__ Chunk<CB> load_chunk(const uint8_t* p) {
+    Chunk<CB> c;
+    if constexpr (CB == 16) {
+        const uint4 x = *reinterpret_cast<const uint4*>(p);
+        c.w[0] = x.x;
+        c.w[1] = x.y;
+        c.w[2] = x.z;
+        c.w[3] = x.w;
+    } else if constexpr (CB == 8) {
+        const uint2 x = *reinterpret_cast<const uint2*>(p);
+        c.w[0] = x.x;
+        c.w[1] = x.y;
+    } else {
+        static_assert(CB == 4, "chunk size");
+        c.w[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+    return c;
+}
+
+template <int CB>
+__device__ __forceinline__ Chunk<CB> zero_chunk() {
+    Chunk<CB> c;
+#pragma unroll
+    for (int i = 0; i < CB / 4; ++i) c.w[i] = 0;
+    return c;
+}
+
+// Stored codes of one chunk -> pairs (element 2i, element 2i+1) as f16, exactly.
+// int8 code x: the byte x ^ 0x80 = x + 128 becomes the low byte of the f16
+// 0x64__ = 1024 + (x + 128); subtracting 1152 leaves x.  4-bit code u: the
+// nibble becomes the low byte of 0x64__ = 1024 + u; subtracting 1032 leaves
+// u - 8.  Element 2i of a 4-bit row is the low nibble of byte i.
+template <int T, int CB, int NP>
+__device__ __forceinline__ void to_pairs(const Chunk<CB>& c, h2 (&p)[NP]) {
+    constexpr int NW = CB / 4;
+    if constexpr (T == KVDEC_F16) {
+        static_assert(NP == NW, "pairs");
+#pragma unroll
+        for (int i = 0; i < NW; ++i) p[i] = as_h2(c.w[i]);
+    } else if constexpr (T == KVDEC_Q8_B32) {
+        static_assert(NP == 2 * NW, "pairs");
+        const h2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const uint32_t x = c.w[i] ^ 0x80808080u;
+            p[2 * i] = as_h2(__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u)) - bias;
+            p[2 * i + 1] = as_h2(__builtin_amdgcn_perm(0x64646464u, x, 0x04030402u)) - bias;
+        }
+    } else {
+        static_assert(NP == 4 * NW, "pairs");
+        const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const uint32_t lo = c.w[i] & 0x0F0F0F0Fu;
+            const uint32_t hi = (c.w[i] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + b) << 16) | (uint32_t)b;
+                p[4 * i + b] = as_h2(__builtin_amdgcn_perm(hi, lo, sel) | 0x64006400u) - bias;
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// Lane geometry.  Per-lane d-slice DL: 16 elements for groups up to 5, 8
+// above (register budget).  R lanes per cell, CPW cells per wave per load,
+// NB cells per lane per step, so a workgroup step covers 4 * CPW * NB cells.
+template <int D, int G>
+struct Geo {
+    static constexpr int DL = (G <= 5) ? 16 : 8;
+    static constexpr int R = D / DL;
+    static constexpr int CPW = 64 / R;
+    static constexpr int NB = 4;
+    static constexpr int STEP = 4 * CPW * NB;
+    static_assert(R >= 4 && R <= 32, "lane geometry");
+};
+
+// Merge of two log2-domain partials (M, L, O) <- (mb, lb, ob), 4 columns.
+__device__ __forceinline__ void merge4(float& M, float& L, float4& O, float mb, float lb, float4 ob) {
+    const float mn = fmaxf(M, mb);
+    const float fa = (M == kNegInf) ? 0.f : exp2_fast(M - mn);
+    const float fb = (mb == kNegInf) ? 0.f : exp2_fast(mb - mn);
+    L = L * fa + lb * fb;
+    O.x = O.x * fa + ob.x * fb;
+    O.y = O.y * fa + ob.y * fb;
+    O.z = O.z * fa + ob.z * fb;
+    O.w = O.w * fa + ob.w * fb;
+    M = mn;
+}
+
+// Output of one row's columns d0 .. d0+3 after the merge: the final out /
+// lse / partial triple, or the running partial when more partials follow.
+__device__ __forceinline__ void emit4(const SplitArgs& a, int to_acc, int64_t row, int d0, int D, float M2, float L,
+                                      float4 O) {
+    if (to_acc) {
+        float* acc = a.acc_out;
+        if (d0 == 0) {
+            acc[row] = M2;
+            acc[a.acc_rows + row] = L;
+        }
+        *reinterpret_cast<float4*>(acc + 2 * (int64_t)a.acc_rows + row * D + d0) = O;
+        return;
+    }
+    const bool empty = !(L > 0.f);
+    if (a.out) {
+        const float4 r = empty ? make_float4(0.f, 0.f, 0.f, 0.f) : make_float4(O.x / L, O.y / L, O.z / L, O.w / L);
+        *reinterpret_cast<float4*>(a.out + row * D + d0) = r;
+    }
+    if (d0 == 0) {
+        if (a.lse) a.lse[row] = empty ? kNegInf : (M2 + log2f(L)) * kLn2;
+        if (a.pm) {
+            a.pm[row] = empty ? kNegInf : M2 * kLn2;
+            a.pl[row] = L;
+        }
+    }
+    if (a.po) *reinterpret_cast<float4*>(a.po + row * D + d0) = O;
+}
+
+// Running partial handed in from an earlier launch (window + tail chain).
+__device__ __forceinline__ void merge_acc_in(const SplitArgs& a, int64_t row, int d0, int D, float& M, float& L,
+                                             float4& O) {
+    if (!a.acc_in) return;
+    const float4 ob = *reinterpret_cast<const float4*>(a.acc_in + 2 * (int64_t)a.acc_rows + row * D + d0);
+    merge4(M, L, O, a.acc_in[row], a.acc_in[a.acc_rows + row], ob);
+}
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const SplitArgs& a) {
+    return __builtin_amdgcn_make_buffer_rsrc(a.part_o, (short)0, (int)a.part_o_bytes, 0x00020000);
+}
+// Device-coherent (sc1) 16-byte store / load of a split record's o columns.
+__device__ __forceinline__ void st_dev4(__amdgpu_buffer_rsrc_t r, int64_t off_bytes, float4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(f4v{v.x, v.y, v.z, v.w}, r, (int)off_bytes, 0, 0x10);
+}
+__device__ __forceinline__ float4 ld_dev4(__amdgpu_buffer_rsrc_t r, int64_t off_bytes) {
+    const f4v v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off_bytes, 0, 0x10);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+// Merge of `count` consecutive partial records of one (slot, KV head),
+// starting at record rec0, by the last workgroup to finish among those that
+// wrote them.  The records were written by workgroups that may sit on other
+// XCDs, so every load here goes out to memory; the merge is organised so
+// that each chunk of merge_chunk(D, G) records costs one round trip: a
+// thread first issues the loads of all its o columns for the chunk, then
+// the (m, l) loads, and only then waits.  Thread -> (float4 column, record
+// residue class); the running maximum and sums per head are kept in LDS
+// across chunks.  The result goes to the outputs (dest < 0) or, merged but
+// not normalised, to record `dest` (a cluster record).
+template <int D, int G>
+__device__ void merge_records(const SplitArgs& a, const SlotArg& sa, int64_t row0, int64_t rec0, int count,
+                              int64_t dest) {
+    constexpr int NV = G * D / 4;                           // float4 columns of o
+    constexpr int TS = NV >= kThreads ? 1 : kThreads / NV;  // threads per column
+    constexpr int COLS = (NV + kThreads - 1) / kThreads;    // columns per thread
+    constexpr int UB = COLS == 1 ? 32 : 32 / COLS;          // records per thread per chunk
+    constexpr int SPC = merge_chunk(D, G);                  // records per chunk (one per lane)
+    static_assert(SPC == (64 < UB * TS ? 64 : UB * TS), "merge chunk");
+    __shared__ float f_m[64 * G];
+    __shared__ float run_m[G], run_l[G], scale_old[G];
+    __shared__ float4 red[TS > 1 ? kThreads : 1];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = tid % (NV < kThreads ? NV : kThreads);
+    const int cls = tid / (NV < kThreads ? NV : kThreads);  // threads with cls >= TS idle
+    const __amdgpu_buffer_rsrc_t rs = part_rsrc(a);
+    const int n_splits = count;
+
+    float4 acc[COLS];
+#pragma unroll
+    for (int c = 0; c < COLS; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (tid < G) {
+        run_m[tid] = kNegInf;
+        run_l[tid] = 0.f;
+    }
+    for (int sp0 = 0; sp0 < n_splits; sp0 += SPC) {
+        const int nsp = (n_splits - sp0) < SPC ? (n_splits - sp0) : SPC;
+        float4 x[COLS][UB];
+#pragma unroll
+        for (int c = 0; c < COLS; ++c) {
+            const int v = col + c * kThreads;
+#pragma unroll
+            for (int u = 0; u < UB; ++u) {
+                const int sp = cls + u * TS;
+                x[c][u] = (cls < TS && v < NV && sp < nsp)
+                              ? ld_dev4(rs, ((rec0 + sp0 + sp) * (G * D) + 4 * v) * 4)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+        // (m, l) of the chunk: wave w takes heads w and w + 4, one split per lane.
+        float mv[2], lv[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int h = wave + 4 * hh;
+            mv[hh] = kNegInf;
+            lv[hh] = 0.f;
+            if (h < G && lane < nsp) {
+                mv[hh] = ld_dev(a.part_m + (rec0 + sp0 + lane) * G + h);
+                lv[hh] = ld_dev(a.part_l + (rec0 + sp0 + lane) * G + h);
+            }
+        }
+        __syncthreads();  // the previous chunk is done with f_m / scale_old
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int h = wave + 4 * hh;
+            if (h >= G) continue;  // uniform over the wave
+            const float mo = run_m[h];
+            const float mn = fmaxf(mo, wave_max(mv[hh]));
+            const float f = (mv[hh] == kNegInf) ? 0.f : exp2_fast(mv[hh] - mn);
+            const float so = (mo == kNegInf) ? 0.f : exp2_fast(mo - mn);
+            const float ls = wave_sum(lv[hh] * f);
+            if (lane < nsp) f_m[lane * G + h] = f;
+            if (lane == 0) {
+                scale_old[h] = so;
+                run_l[h] = run_l[h] * so + ls;
+                run_m[h] = mn;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < COLS; ++c) {
+            const int v = col + c * kThreads;
+            if (cls >= TS || v >= NV) continue;
+            const int h = (4 * v) / D;
+            const float so = scale_old[h];
+            float4 o = acc[c];
+            o.x *= so;
+            o.y *= so;
+            o.z *= so;
+            o.w *= so;
+#pragma unroll
+            for (int u = 0; u < UB; ++u) {
+                const int sp = cls + u * TS;
+                const float f = sp < nsp ? f_m[sp * G + h] : 0.f;
+                o.x = fmaf(x[c][u].x, f, o.x);
+                o.y = fmaf(x[c][u].y, f, o.y);
+                o.z = fmaf(x[c][u].z, f, o.z);
+                o.w = fmaf(x[c][u].w, f, o.w);
+            }
+            acc[c] = o;
+        }
+    }
+    // combine the TS residue classes of each column
+    if constexpr (TS > 1) {
+        red[tid] = acc[0];
+        __syncthreads();
+        if (cls == 0) {
+            float4 o = acc[0];
+            for (int t = 1; t < TS; ++t) {
+                const float4 y = red[t * NV + col];
+                o.x += y.x;
+                o.y += y.y;
+                o.z += y.z;
+                o.w += y.w;
+            }
+            acc[0] = o;
+        }
+    }
+    if (cls == 0) {
+#pragma unroll
+        for (int c = 0; c < COLS; ++c) {
+            const int v = col + c * kThreads;
+            if (v >= NV) continue;
+            const int h = (4 * v) / D;
+            const int d0 = 4 * v - h * D;
+            float M = run_m[h], L = run_l[h];
+            float4 O = acc[c];
+            if (dest < 0) {
+                merge_acc_in(a, row0 + h, d0, D, M, L, O);
+                emit4(a, sa.to_acc, row0 + h, d0, D, M, L, O);
+            } else {
+                st_dev4(rs, (dest * (G * D) + 4 * v) * 4, O);
+                if (d0 == 0) {
+                    st_dev(a.part_m + dest * G + h, M);
+                    st_dev(a.part_l + dest * G + h, L);
+                }
+            }
+        }
+    }
+}
+
+// One arrival at a ticket that counts `expected` arrivals; true (for the
+// whole workgroup) in the last one to arrive, which also resets the ticket.
+__device__ __forceinline__ bool last_arrival(uint32_t* ticket, int expected, int& sm_last) {
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = prev == (uint32_t)(expected - 1);
+        if (last) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sm_last = last;
+    }
+    __syncthreads();
+    return sm_last != 0;
+}
+
+// End of a split: merge the NS cell streams left in LDS (m2, l, o per
+// stream and head) into the split's result; a single-split group writes its
+// output directly, otherwise the split's record is published and the last
+// workgroup of the (slot, KV head) merges all records.
+template <int D, int G, int NS, int DP>
+__device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& sa, int s, int g, int split,
+                                             int64_t row0, const float (*sm_m)[G], const float (*sm_l)[G],
+                                             const float (*sm_o)[G][DP], int& sm_last) {
+    const int tid = threadIdx.x;
+    // Merge the NS streams: thread -> float4 column.  Result of this split in log2 units.
+    constexpr int NV = G * D / 4;
+    const int n_splits = sa.n_splits;
+    const bool single = (n_splits == 1);
+    const int64_t rec = sa.part_begin + (int64_t)g * n_splits + split;
+    const __amdgpu_buffer_rsrc_t rs = part_rsrc(a);
+    for (int v = tid; v < NV; v += kThreads) {
+        const int h = (4 * v) / D, d0 = 4 * v - h * D;
+        float M = kNegInf;
+#pragma unroll
+        for (int k = 0; k < NS; ++k) M = fmaxf(M, sm_m[k][h]);
+        float L = 0.f;
+        float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            const float mk = sm_m[k][h];
+            const float f = (mk == kNegInf) ? 0.f : exp2_fast(mk - M);
+            const float4 ok = *reinterpret_cast<const float4*>(&sm_o[k][h][d0]);
+            L = fmaf(sm_l[k][h], f, L);
+            O.x = fmaf(ok.x, f, O.x);
+            O.y = fmaf(ok.y, f, O.y);
+            O.z = fmaf(ok.z, f, O.z);
+            O.w = fmaf(ok.w, f, O.w);
+        }
+        if (single) {
+            merge_acc_in(a, row0 + h, d0, D, M, L, O);
+            emit4(a, sa.to_acc, row0 + h, d0, D, M, L, O);
+        } else {
+            st_dev4(rs, (rec * (G * D) + 4 * v) * 4, O);
+            if (d0 == 0) {
+                st_dev(a.part_m + rec * G + h, M);
+                st_dev(a.part_l + rec * G + h, L);
+            }
+        }
+    }
+    if (single) return;
+
+    // Records are published (stores complete) before the arrival is counted.
+    wait_stores();
+    __syncthreads();
+    uint32_t* gticket = a.tickets + (int64_t)(a.slot_base + s) * a.n_kv_heads + g;
+    const int64_t srec0 = sa.part_begin + (int64_t)g * n_splits;
+    const int ncl = sa.n_clusters;
+    if (ncl <= 1) {
+        // the last workgroup of the (slot, KV head) merges every split
+        if (!last_arrival(gticket, n_splits, sm_last)) return;
+        merge_records<D, G>(a, sa, row0, srec0, n_splits, -1);
+        return;
+    }
+    // two levels: the last of each cluster of splits merges the cluster into
+    // a cluster record; the last cluster merger merges the cluster records
+    constexpr int CH = merge_chunk(D, G);
+    const int cid = split / CH;
+    const int c0 = cid * CH;
+    const int cn = (n_splits - c0) < CH ? (n_splits - c0) : CH;
+    const int64_t cidx = sa.cl_begin + (int64_t)g * ncl + cid;
+    if (!last_arrival(a.ctickets + cidx, cn, sm_last)) return;
+    merge_records<D, G>(a, sa, row0, srec0 + c0, cn, a.crec_base + cidx);
+    wait_stores();
+    __syncthreads();
+    if (!last_arrival(gticket, ncl, sm_last)) return;
+    merge_records<D, G>(a, sa, row0, a.crec_base + sa.cl_begin + (int64_t)g * ncl, ncl, -1);
+}
+
+
+template <int D, int G, int KT, int VT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void split_kernel(const SplitArgs a) {
+    using Gm = Geo<D, G>;
+    constexpr int DL = Gm::DL, R = Gm::R, CPW = Gm::CPW, NCW = Gm::NB, STEP = Gm::STEP;
+    using FK = Fmt<KT, DL>;
+    using FV = Fmt<VT, DL>;
+    constexpr int NCK = DL / FK::EPC;  // K chunks per lane per cell
+    constexpr int NCV = DL / FV::EPC;  // V chunks per lane per cell
+    static_assert(NCK >= 1 && NCV >= 1 && NCK * FK::EPC == DL && NCV * FV::EPC == DL, "chunking");
+    constexpr int NB = D / kBlock;     // scales per row
+    // Cell streams per wave left after the in-register (DPP) merge step.
+    constexpr bool kDppStep = R <= 8;
+    constexpr int NSW = kDppStep ? CPW / 2 : CPW;
+    constexpr int NS = 4 * NSW;        // streams per workgroup merged through LDS
+
+    __shared__ float sm_m[NS][G];
+    __shared__ float sm_l[NS][G];
+    // stream stride padded by 16 floats: streams written by one instruction land in different banks
+    __shared__ __align__(16) float sm_o[NS][G][D + 16];
+    __shared__ int sm_last;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int sub = lane % R;
+    const int cl = lane / R;
+
+    // Which (slot, KV head, split) this workgroup owns.
+    const int wg = blockIdx.x;
+    int s = 0;
+    while (s + 1 < a.n_slots && a.slot[s + 1].wg_begin <= wg) ++s;
+    const SlotArg sa = a.slot[s];
+    const int local = wg - sa.wg_begin;
+    // Consecutive workgroups take the same cell range of different KV heads,
+    // so the workgroups resident together read neighbouring bytes of each
+    // cell row.
+    const int split = local / a.n_kv_heads;
+    const int g = local - split * a.n_kv_heads;
+    const int t0 = (int)(((int64_t)split * sa.n_tiles) / sa.n_splits);
+    const int t1 = (int)(((int64_t)(split + 1) * sa.n_tiles) / sa.n_splits);
+    const int hq0 = g * G;  // first query head of the group
+    const int64_t row0 = (int64_t)(a.slot_base + s) * a.n_q_heads + hq0;
+
+    // Query rows of the group, f16 pairs, this lane's K d-slice only.
+    h2 qh[G][DL / 2];
+    {
+        const float* qp = a.q + row0 * D;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+            for (int c = 0; c < NCK; ++c) {
+                const int e = (c * R + sub) * FK::EPC;
+#pragma unroll
+                for (int i = 0; i < FK::EPC / 2; ++i) {
+                    const float2 x = *reinterpret_cast<const float2*>(qp + h * D + e + 2 * i);
+                    qh[h][c * (FK::EPC / 2) + i] = h2{(_Float16)x.x, (_Float16)x.y};
+                }
+            }
+        }
+    }
+
+    float m[G], l[G], o[G][DL];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = kNegInf;
+        l[h] = 0.f;
+#pragma unroll
+        for (int i = 0; i < DL; ++i) o[h][i] = 0.f;
+    }
+
+    const uint8_t* kbase = a.k + (int64_t)g * a.k_hs;
+    const uint8_t* vbase = a.v + (int64_t)g * a.v_hs;
+    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    const int64_t tile_end = (int64_t)t1 * kTile;
+    const int64_t pos_end = tile_end < sa.n ? tile_end : sa.n;
+
+    // One step: NCW cells per lane.  Buffers of a step in flight.
+    struct Step {
+        bool valid[NCW];
+        Chunk<FK::CB> kc[NCW][NCK];
+        Chunk<FV::CB> vc[NCW][NCV];
+        float kd[NCW][NCK], vd[NCW][NCV];
+    };
+
+    // Issue the loads of the step starting at slot position `base`.
+    auto load_step = [&](int64_t base, Step& st) {
+        int64_t cell[NCW];
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) {
+            const int64_t pos = base + (wave * NCW + j) * CPW + cl;  // position in the slot
+            if (a.plan) {
+                const bool in = pos < pos_end;
+                const int64_t c = in ? (int64_t)a.plan[sa.first + pos] : -1;
+                st.valid[j] = c >= 0 && c < a.capacity;
+                cell[j] = st.valid[j] ? c : 0;
+            } else {
+                st.valid[j] = pos < pos_end;
+                cell[j] = sa.first + (st.valid[j] ? pos : 0);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) {
+            const uint8_t* kr = kbase + cell[j] * a.k_cs;
+            const uint8_t* vr = vbase + cell[j] * a.v_cs;
+#pragma unroll
+            for (int c = 0; c < NCK; ++c)
+                st.kc[j][c] = st.valid[j] ? load_chunk<FK::CB>(kr + (c * R + sub) * FK::CB) : zero_chunk<FK::CB>();
+#pragma unroll
+            for (int c = 0; c < NCV; ++c)
+                st.vc[j][c] = st.valid[j] ? load_chunk<FV::CB>(vr + (c * R + sub) * FV::CB) : zero_chunk<FV::CB>();
+            if constexpr (FK::scaled) {
+#pragma unroll
+                for (int c = 0; c < NCK; ++c) {
+                    const int blk = ((c * R + sub) * FK::EPC) / kBlock;
+                    st.kd[j][c] = st.valid[j] ? half_bits_to_float(a.ks[(cell[j] * a.n_kv_heads + g) * NB + blk]) : 0.f;
+                }
+            }
+            if constexpr (FV::scaled) {
+#pragma unroll
+                for (int c = 0; c < NCV; ++c) {
+                    const int blk = ((c * R + sub) * FV::EPC) / kBlock;
+                    st.vd[j][c] = st.valid[j] ? half_bits_to_float(a.vs[(cell[j] * a.n_kv_heads + g) * NB + blk]) : 0.f;
+                }
+            }
+        }
+    };
+
+    // Scores, online-softmax update and P.V of one loaded step.
+    auto compute_step = [&](const Step& st) {
+        float sc[NCW][G];
+#pragma unroll
+        for (int j = 0; j < NCW; ++j) {
+            float acc[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) acc[h] = 0.f;
+#pragma unroll
+            for (int c = 0; c < NCK; ++c) {
+                h2 kp[FK::EPC / 2];
+                to_pairs<KT>(st.kc[j][c], kp);
+                if constexpr (FK::scaled) {
+                    float part[G];
+#pragma unroll
+                    for (int h = 0; h < G; ++h) part[h] = 0.f;
+#pragma unroll
+                    for (int i = 0; i < FK::EPC / 2; ++i)
+#pragma unroll
+                        for (int h = 0; h < G; ++h)
+                            part[h] = __builtin_amdgcn_fdot2(kp[i], qh[h][c * (FK::EPC / 2) + i], part[h], false);
+#pragma unroll
+                    for (int h = 0; h < G; ++h) acc[h] = fmaf(part[h], st.kd[j][c], acc[h]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < FK::EPC / 2; ++i)
+#pragma unroll
+                        for (int h = 0; h < G; ++h)
+                            acc[h] = __builtin_amdgcn_fdot2(kp[i], qh[h][c * (FK::EPC / 2) + i], acc[h], false);
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float full = group_sum<R>(acc[h]);
+                sc[j][h] = st.valid[j] ? full * a.scale_log2 : kNegInf;
+            }
+        }
+
+        float p[NCW][G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float mt = sc[0][h];
+#pragma unroll
+            for (int j = 1; j < NCW; ++j) mt = fmaxf(mt, sc[j][h]);
+            const float mn = fmaxf(m[h], mt);
+            const float alpha = (mn == kNegInf) ? 1.f : exp2_fast(m[h] - mn);
+            l[h] *= alpha;
+#pragma unroll
+            for (int i = 0; i < DL; ++i) o[h][i] *= alpha;
+            m[h] = mn;
+#pragma unroll
+            for (int j = 0; j < NCW; ++j) p[j][h] = (sc[j][h] == kNegInf) ? 0.f : exp2_fast(sc[j][h] - mn + kPOff);
+        }
+
+        if constexpr (VT == KVDEC_F16) {
+            // Pairs of cells: (V[A][d], V[B][d]) . (pA, pB) in one packed dot.
+#pragma unroll
+            for (int jp = 0; jp < NCW / 2; ++jp) {
+                const int A = 2 * jp, B = 2 * jp + 1;
+                h2 pp[G];
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    pp[h] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p[A][h], p[B][h]));
+                    l[h] = __builtin_amdgcn_fdot2(pp[h], ones, l[h], false);
+                }
+#pragma unroll
+                for (int c = 0; c < NCV; ++c) {
+#pragma unroll
+                    for (int i = 0; i < FV::CB / 4; ++i) {
+                        const h2 lo = as_h2(__builtin_amdgcn_perm(st.vc[B][c].w[i], st.vc[A][c].w[i], 0x05040100u));
+                        const h2 hi = as_h2(__builtin_amdgcn_perm(st.vc[B][c].w[i], st.vc[A][c].w[i], 0x07060302u));
+                        const int dd = c * FV::EPC + 2 * i;
+#pragma unroll
+                        for (int h = 0; h < G; ++h) {
+                            o[h][dd] = __builtin_amdgcn_fdot2(lo, pp[h], o[h][dd], false);
+                            o[h][dd + 1] = __builtin_amdgcn_fdot2(hi, pp[h], o[h][dd + 1], false);
+                        }
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NCW; ++j) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) l[h] += p[j][h];
+#pragma unroll
+                for (int c = 0; c < NCV; ++c) {
+                    h2 vp[FV::EPC / 2];
+                    to_pairs<VT>(st.vc[j][c], vp);
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        const float pd = p[j][h] * st.vd[j][c];
+#pragma unroll
+                        for (int i = 0; i < FV::EPC / 2; ++i) {
+                            o[h][c * FV::EPC + 2 * i] = fmaf((float)vp[i].x, pd, o[h][c * FV::EPC + 2 * i]);
+                            o[h][c * FV::EPC + 2 * i + 1] = fmaf((float)vp[i].y, pd, o[h][c * FV::EPC + 2 * i + 1]);
+                        }
+                    }
+                }
+            }
+        }
+    };
+
+    for (int64_t base = (int64_t)t0 * kTile; base < pos_end; base += STEP) {
+        Step st;
+        load_step(base, st);
+        compute_step(st);
+    }
+
+    // Merge the cell streams.  Lanes with the same sub own the same d-slice
+    // for different cells.  One in-register step pairs lane i with lane i ^ 8
+    // (DPP row rotate by 8) when that partner holds the same slice; the
+    // remaining NSW streams per wave go through LDS.
+    if constexpr (kDppStep) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float mo = dpp<0x128>(m[h]);
+            const float lo = dpp<0x128>(l[h]);
+            const float mn = fmaxf(m[h], mo);
+            const float fa = (m[h] == kNegInf) ? 0.f : exp2_fast(m[h] - mn);
+            const float fb = (mo == kNegInf) ? 0.f : exp2_fast(mo - mn);
+            l[h] = l[h] * fa + lo * fb;
+#pragma unroll
+            for (int i = 0; i < DL; ++i) o[h][i] = o[h][i] * fa + dpp<0x128>(o[h][i]) * fb;
+            m[h] = mn;
+        }
+    }
+    const bool rep = kDppStep ? ((lane & 8) == 0) : true;
+    const int kl = kDppStep ? (((lane & 7) | ((lane >> 4) << 3)) / R) : cl;
+    if (rep) {
+        const int k = wave * NSW + kl;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            if (sub == 0) {
+                sm_m[k][h] = m[h];
+                sm_l[k][h] = l[h] * kPOffInv;
+            }
+#pragma unroll
+            for (int c = 0; c < NCV; ++c)
+#pragma unroll
+                for (int i = 0; i < FV::EPC; i += 4)
+                    *reinterpret_cast<float4*>(&sm_o[k][h][(c * R + sub) * FV::EPC + i]) =
+                        make_float4(o[h][c * FV::EPC + i] * kPOffInv, o[h][c * FV::EPC + i + 1] * kPOffInv,
+                                    o[h][c * FV::EPC + i + 2] * kPOffInv, o[h][c * FV::EPC + i + 3] * kPOffInv);
+        }
+    }
+    __syncthreads();
+
+    finish_split<D, G, NS, D + 16>(a, sa, s, g, split, row0, sm_m, sm_l, sm_o, sm_last);
+}
+
+// ---------------------------------------------------------------------------
+// Wide-group kernel (G = 6..8 query heads per KV head): matrix-core path.
+//
+// With six or more query rows per KV head the VALU path runs out of issue
+// slots before HBM does (int8 / 4-bit rows also need dequantisation), so the
+// two contractions of a 32-cell step go to v_mfma_f32_16x16x32_f16, the G
+// query rows padded to 16 with zero rows:
+//   S^T[cell][head] = K^[cell][:] . q[head][:]   (A = K^ rows, B = q^T)
+//   O[head][d]     += P[head][cell] . V^[cell][d] (A = P, B = V^)
+// Operand layouts (measured on gfx950): A[i][k] sits in lane i + 16*(k/8),
+// element k%8; B[k][j] in lane j + 16*(k/8); D[i][j] in lane j + 16*(i/4),
+// element i%4.  The order of the contraction index is free, so
+//  * for S, lane group q of a 16-cell block reads 16-byte chunks q, q+4, ...
+//    of its cell's row and q is loaded in the same permuted element order,
+//    so every chunk feeds whole MFMAs without any shuffle;
+//  * for P.V, the 8 contraction slots of lane group q are cells 4q..4q+3 of
+//    the step's two 16-cell blocks -- exactly the scores that lane holds
+//    after the S product -- so P never moves between lanes.
+// V^ is dequantised (d * code rounded to f16) into a per-wave LDS tile of 32
+// rows and read back column-wise with ds_read_b64_tr_b16, whose 16-lane 4x4
+// transpose delivers the B operand.  Each wave is one online-softmax stream;
+// the four waves are merged at the end like the VALU path's streams.
+// ---------------------------------------------------------------------------
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+
+// Elements per 16-byte chunk of a stored row.
+template <int T>
+struct Row16 {
+    static constexpr int EPC = T == KVDEC_F16 ? 8 : T == KVDEC_Q8_B32 ? 16 : 32;
+};
+
+// One 16-byte chunk -> its EPC values as f16 pairs (block-scaled kinds: d * code,
+// rounded to f16).
+template <int T>
+__device__ __forceinline__ void dequant16(const Chunk<16>& c, uint16_t scale_bits, h2 (&out)[Row16<T>::EPC / 2]) {
+    to_pairs<T>(c, out);
+    if constexpr (T != KVDEC_F16) {
+        const _Float16 d = __builtin_bit_cast(_Float16, scale_bits);
+        const h2 dd = {d, d};
+#pragma unroll
+        for (int i = 0; i < Row16<T>::EPC / 2; ++i) out[i] = out[i] * dd;
+    }
+}
+
+// Workgroup order seen by the work decomposition.  The dispatcher hands
+// workgroups to the 8 XCDs round-robin (workgroup b to XCD b % 8), and each
+// XCD has its own L2.  Renumbering so that consecutive logical indices land
+// on the same XCD puts the KV heads of one split -- which share the cache
+// lines of the cells' block scales and plan entries -- behind one L2.  Only
+// a bijection of [0, n): correctness never depends on the placement.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_logical_index(int b, int n) {
+    const int per = n / kXcds, extra = n % kXcds;
+    const int x = b % kXcds, k = b / kXcds;
+    return (x < extra ? x * (per + 1) : extra * (per + 1) + (x - extra) * per) + k;
+}
+
+// Scale of the 32-element block holding chunk lq + 4j of a row, taken from
+// the row's SB bytes of scales.  int8: 16 elements per chunk, so the block is
+// 2j + lq/2 (dword j); 4-bit: 32 per chunk, block lq + 4j (half lq of dwords 2j, 2j+1).
+template <int T, int SB>
+__device__ __forceinline__ uint16_t scale_of(const Chunk<SB>& r, int j, int lq) {
+    if constexpr (T == KVDEC_Q8_B32) {
+        return (uint16_t)(r.w[j] >> (16 * (lq >> 1)));
+    } else if constexpr (T == KVDEC_Q4_B32) {
+        // halves 4j..4j+3 of the row as one 64-bit value (no lane-dependent
+        // register index, which would go through scratch memory)
+        const uint64_t x = (uint64_t)r.w[2 * j] | ((uint64_t)r.w[2 * j + 1] << 32);
+        return (uint16_t)(x >> (16 * lq));
+    } else {
+        return 0;
+    }
+}
+
+template <int D, int G, int KT, int VT, bool IND>
+__global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a) {
+    static_assert(G >= 1 && G <= 16, "heads padded to one 16-row tile");
+    constexpr int EK = Row16<KT>::EPC, EV = Row16<VT>::EPC;
+    constexpr int JK = D / EK / 4, JV = D / EV / 4;  // chunks per lane per row
+    static_assert(JK >= 1 && JV >= 1 && JK * 4 * EK == D && JV * 4 * EV == D, "row chunking");
+    constexpr int NKB = D / 32;                    // S MFMAs per 16-cell block
+    constexpr int NNB = D / 16;                    // P.V MFMAs (16-column blocks of O)
+    constexpr int NB = D / kBlock;                 // scales per row
+    constexpr int SB = NB * 2;                     // bytes of one row of scales
+    constexpr int VSTR = 2 * D + 32;               // bytes per staged V row (padded)
+    constexpr int STAGE = 4 * 32 * VSTR;           // V staging of the 4 waves
+    constexpr int MERGE = 4 * G * 4 * 2 + 4 * G * D * 4;
+    constexpr int SMEM = STAGE > MERGE ? STAGE : MERGE;
+    __shared__ __align__(16) unsigned char smem[SMEM];
+    __shared__ int sm_last;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int li = lane & 15;  // row / column index inside a 16-lane group
+    const int lq = lane >> 4;  // lane group
+
+    const int wg = xcd_logical_index(blockIdx.x, a.n_workgroups);
+    int s = 0;
+    while (s + 1 < a.n_slots && a.slot[s + 1].wg_begin <= wg) ++s;
+    const SlotArg sa = a.slot[s];
+    const int local = wg - sa.wg_begin;
+    const int split = local / a.n_kv_heads;
+    const int g = local - split * a.n_kv_heads;
+    const int t0 = (int)(((int64_t)split * sa.n_tiles) / sa.n_splits);
+    const int t1 = (int)(((int64_t)(split + 1) * sa.n_tiles) / sa.n_splits);
+    const int64_t row0 = (int64_t)(a.slot_base + s) * a.n_q_heads + g * G;
+
+    // B operand of S: q rows (zero rows for heads >= G) in the permuted order
+    // of the K chunks this lane group reads.  Loads are unconditional (row
+    // clamped) so that they all leave before the first wait.
+    h8 qb[NKB];
+    {
+        const float* qr = a.q + (row0 + (li < G ? li : 0)) * D;
+#pragma unroll
+        for (int j = 0; j < JK; ++j) {
+#pragma unroll
+            for (int sub = 0; sub < EK / 8; ++sub) {
+                const int e0 = (lq + 4 * j) * EK + 8 * sub;
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const float2 v = *reinterpret_cast<const float2*>(qr + e0 + e);
+                    x[e] = v.x;
+                    x[e + 1] = v.y;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qb[j * (EK / 8) + sub][e] = li < G ? (_Float16)x[e] : (_Float16)0.0f;
+            }
+        }
+    }
+
+    // Online softmax of head li (identical over the 4 lane groups).  The
+    // reference m_h moves only when a score exceeds it by more than kLazy,
+    // so the O tile is rarely rescaled; weights 2^(s - m_h + kMPOff) then stay
+    // below 2^15 and remain normal f16 numbers far below the maximum.
+    constexpr float kLazy = 6.0f;
+    constexpr float kMPOff = 9.0f;
+    constexpr float kMPOffInv = 1.0f / 512.0f;
+    float m_h = kNegInf, l_h = 0.f;
+    f4v oacc[NNB];
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb) oacc[nb] = f4v{0.f, 0.f, 0.f, 0.f};
+
+    const uint8_t* kbase = a.k + (int64_t)g * a.k_hs;
+    const uint8_t* vbase = a.v + (int64_t)g * a.v_hs;
+    unsigned char* vst = smem + wave * 32 * VSTR;
+    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    const int64_t tile_end = (int64_t)t1 * kTile;
+    const int64_t pos_end = tile_end < sa.n ? tile_end : sa.n;
+    const int64_t base0 = (int64_t)t0 * kTile;
+    const int n_steps = t1 - t0;  // one 32-cell step of every tile per wave
+
+    // Cells of a step: lane li owns cell li of the wave's two 16-cell blocks.
+    // Loads never branch: an invalid cell reads row 0 of the cache instead,
+    // its score is masked and its V row is zeroed where it is consumed.  Raw
+    // plan entries are fetched two steps ahead and left untouched until the
+    // step before their use, and the K / V loads of step i+1 leave while
+    // step i computes, so no wait falls on data that is not needed yet.
+    const int32_t* plan_s = IND ? a.plan + sa.first : nullptr;
+    auto fetch = [&](int64_t base, int mb) -> int32_t {
+        if constexpr (IND) {
+            const int64_t pos = base + 32 * wave + 16 * mb + li;
+            return plan_s[pos < pos_end ? pos : pos_end - 1];
+        } else {
+            return 0;
+        }
+    };
+    auto resolve = [&](int64_t base, int mb, int32_t raw, int64_t& cell, bool& valid) {
+        const int64_t pos = base + 32 * wave + 16 * mb + li;
+        if constexpr (IND) {
+            valid = pos < pos_end && raw >= 0 && raw < a.capacity;
+            cell = valid ? raw : 0;
+        } else {
+            valid = pos < pos_end;
+            cell = valid ? sa.first + pos : 0;
+        }
+    };
+    Chunk<16> kc[2][JK], vc[2][JV];
+    Chunk<SB> kr_s[2], vr_s[2];  // scale rows of the two cells (block-scaled kinds)
+    auto load_k = [&](const int64_t (&cell)[2]) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const uint8_t* kr = kbase + cell[mb] * a.k_cs;
+#pragma unroll
+            for (int j = 0; j < JK; ++j) kc[mb][j] = load_chunk<16>(kr + (lq + 4 * j) * 16);
+            if constexpr (KT != KVDEC_F16)
+                kr_s[mb] = load_chunk<SB>(reinterpret_cast<const uint8_t*>(a.ks) + (cell[mb] * a.n_kv_heads + g) * SB);
+        }
+    };
+    auto load_v = [&](const int64_t (&cell)[2]) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const uint8_t* vr = vbase + cell[mb] * a.v_cs;
+#pragma unroll
+            for (int j = 0; j < JV; ++j) vc[mb][j] = load_chunk<16>(vr + (lq + 4 * j) * 16);
+            if constexpr (VT != KVDEC_F16)
+                vr_s[mb] = load_chunk<SB>(reinterpret_cast<const uint8_t*>(a.vs) + (cell[mb] * a.n_kv_heads + g) * SB);
+        }
+    };
+
+    int32_t raw_next[2] = {0, 0};
+    int64_t cell[2] = {0, 0};
+    bool valid[2] = {false, false};
+    if (n_steps > 0) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            resolve(base0, mb, fetch(base0, mb), cell[mb], valid[mb]);
+            raw_next[mb] = fetch(base0 + kTile, mb);
+        }
+        load_k(cell);
+        __builtin_amdgcn_sched_barrier(0);  // same issue order as in the loop: K, then V
+        load_v(cell);
+        if constexpr (IND) {
+            // Land the step-1 entries here, behind an opaque copy: entering the
+            // loop with a load still pending on them would make the compiler
+            // wait for every prefetched K / V load at the top of each step.
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                int32_t t;
+                asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(raw_next[mb]));
+                raw_next[mb] = t;
+            }
+        }
+    }
+
+    for (int st = 0; st < n_steps; ++st) {
+        const int64_t base = base0 + (int64_t)st * kTile;
+        const uint64_t vm0 = __ballot(valid[0]), vm1 = __ballot(valid[1]);
+        int32_t raw2[2];
+        int64_t ncell[2];
+        bool nvalid[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            raw2[mb] = fetch(base + 2 * kTile, mb);
+            resolve(base + kTile, mb, raw_next[mb], ncell[mb], nvalid[mb]);
+        }
+
+        // S^T for the two blocks.
+        f4v sacc[2] = {f4v{0.f, 0.f, 0.f, 0.f}, f4v{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+            for (int j = 0; j < JK; ++j) {
+                h2 kp[EK / 2];
+                dequant16<KT>(kc[mb][j], scale_of<KT, SB>(kr_s[mb], j, lq), kp);
+#pragma unroll
+                for (int sub = 0; sub < EK / 8; ++sub) {
+                    h8 av;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        av[2 * e] = kp[4 * sub + e].x;
+                        av[2 * e + 1] = kp[4 * sub + e].y;
+                    }
+                    sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qb[j * (EK / 8) + sub], sacc[mb], 0, 0, 0);
+                }
+            }
+        }
+        load_k(ncell);  // K of the next step (its registers are free now)
+        // phase fence for the scheduler: V data is consumed only below
+        __builtin_amdgcn_sched_barrier(0);
+
+        // Scores of head li for cells 4*lq + e of each block (log2 units).
+        float sc[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = 4 * lq + e;
+            sc[e] = ((vm0 >> c) & 1) ? sacc[0][e] * a.scale_log2 : kNegInf;
+            sc[4 + e] = ((vm1 >> c) & 1) ? sacc[1][e] * a.scale_log2 : kNegInf;
+        }
+        float mt = sc[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sc[e]);
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const bool bump = mt > m_h + kLazy;  // also the first finite score
+        const float mn = bump ? mt : m_h;
+        const float alpha = bump ? exp2_fast(m_h - mn) : 1.f;
+        const bool rescale = bump && m_h != kNegInf;
+        m_h = mn;
+        h8 pa;
+        float lsum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const float p0 = (sc[e] == kNegInf) ? 0.f : exp2_fast(sc[e] - mn + kMPOff);
+            const float p1 = (sc[e + 1] == kNegInf) ? 0.f : exp2_fast(sc[e + 1] - mn + kMPOff);
+            const h2 pp = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+            pa[e] = pp.x;
+            pa[e + 1] = pp.y;
+            lsum = __builtin_amdgcn_fdot2(pp, ones, lsum, false);
+        }
+        lsum += __shfl_xor(lsum, 16);
+        lsum += __shfl_xor(lsum, 32);
+        l_h = l_h * alpha + lsum;
+        // O rows held by this lane are heads 4*lq + e: rescale with their alphas.
+        if (__ballot(rescale) != 0) {
+            float ae[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ae[e] = __shfl(alpha, 4 * lq + e);
+#pragma unroll
+            for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) oacc[nb][e] *= ae[e];
+        }
+
+        __builtin_amdgcn_sched_barrier(0);
+        // V^ rows of the step -> LDS (row = 16*block + cell), f16.
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+            for (int j = 0; j < JV; ++j) {
+                const int c = lq + 4 * j;
+                h2 vp[EV / 2];
+                if constexpr (VT == KVDEC_F16) {
+                    Chunk<16> x = vc[mb][j];
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) x.w[w] = valid[mb] ? x.w[w] : 0u;
+                    dequant16<VT>(x, 0, vp);
+                } else {
+                    dequant16<VT>(vc[mb][j], valid[mb] ? scale_of<VT, SB>(vr_s[mb], j, lq) : (uint16_t)0, vp);
+                }
+                uint4* dst = reinterpret_cast<uint4*>(vst + (16 * mb + li) * VSTR + c * EV * 2);
+#pragma unroll
+                for (int w = 0; w < EV / 8; ++w)
+                    dst[w] = make_uint4(__builtin_bit_cast(uint32_t, vp[4 * w]), __builtin_bit_cast(uint32_t, vp[4 * w + 1]),
+                                        __builtin_bit_cast(uint32_t, vp[4 * w + 2]),
+                                        __builtin_bit_cast(uint32_t, vp[4 * w + 3]));
+            }
+        }
+        load_v(ncell);  // V of the next step
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // O += P . V^: B operand by transposing 16-lane reads of the staged rows.
+        typedef __attribute__((address_space(3))) fp16x4_t lds_h4;
+        const int r_lo = 4 * lq + (li >> 2);  // staged row of block 0 read by this lane
+        const int col = 4 * (li & 3);
+#pragma unroll
+        for (int nb = 0; nb < NNB; ++nb) {
+            const int cb = (16 * nb + col) * 2;
+            // generic -> LDS address space (C-style cast: the pointer is in smem)
+            lds_h4* p0 = (lds_h4*)(vst + r_lo * VSTR + cb);
+            lds_h4* p1 = (lds_h4*)(vst + (16 + r_lo) * VSTR + cb);
+            const fp16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16(p0);
+            const fp16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16(p1);
+            h8 vb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                vb[e] = (_Float16)v0[e];
+                vb[4 + e] = (_Float16)v1[e];
+            }
+            oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, oacc[nb], 0, 0, 0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            raw_next[mb] = raw2[mb];
+            cell[mb] = ncell[mb];
+            valid[mb] = nvalid[mb];
+        }
+    }
+
+    // Each wave is one stream: (m2, l, o) of heads < G -> LDS, then merge.
+    __syncthreads();  // the V staging area is reused for the merge arrays
+    float (*sm_m)[G] = reinterpret_cast<float (*)[G]>(smem);
+    float (*sm_l)[G] = reinterpret_cast<float (*)[G]>(smem + 4 * G * 4);
+    float (*sm_o)[G][D] = reinterpret_cast<float (*)[G][D]>(smem + 4 * G * 4 * 2);
+    if (lq == 0 && li < G) {
+        sm_m[wave][li] = m_h;
+        sm_l[wave][li] = l_h * kMPOffInv;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int h = 4 * lq + e;
+            if (h < G) sm_o[wave][h][16 * nb + li] = oacc[nb][e] * kMPOffInv;
+        }
+    __syncthreads();
+    finish_split<D, G, 4, D>(a, sa, s, g, split, row0, sm_m, sm_l, sm_o, sm_last);
+}
+
+// Groups of up to 5 query heads per KV head run on the VALU kernel; wider
+// groups (with head_dim 128 or 256) on the matrix-core kernel.
+template <int D, int G>
+constexpr bool use_mfma() {
+    return G >= 6 && D >= 128;
+}
+
+template <int D, int G, int KT, int VT>
+int launch_one(const SplitArgs& a, void* stream) {
+    if constexpr (use_mfma<D, G>()) {
+        if (a.plan)
+            hipLaunchKernelGGL((split_mfma_kernel<D, G, KT, VT, true>), dim3(a.n_workgroups), dim3(kThreads), 0,
+                               (hipStream_t)stream, a);
+        else
+            hipLaunchKernelGGL((split_mfma_kernel<D, G, KT, VT, false>), dim3(a.n_workgroups), dim3(kThreads), 0,
+                               (hipStream_t)stream, a);
+    } else
+        hipLaunchKernelGGL((split_kernel<D, G, KT, VT>), dim3(a.n_workgroups), dim3(kThreads), 0,
+                           (hipStream_t)stream, a);
+    return (int)hipGetLastError();
+}
+
+template <int D, int KT, int VT>
+SplitLaunchFn pick_g(int g) {
+    switch (g) {
+        case 1: return &launch_one<D, 1, KT, VT>;
+        case 2: return &launch_one<D, 2, KT, VT>;
+        case 3: return &launch_one<D, 3, KT, VT>;
+        case 4: return &launch_one<D, 4, KT, VT>;
+        case 5: return &launch_one<D, 5, KT, VT>;
+        case 6: return &launch_one<D, 6, KT, VT>;
+        case 7: return &launch_one<D, 7, KT, VT>;
+        case 8: return &launch_one<D, 8, KT, VT>;
+        default: return nullptr;
+    }
+}
+
+// Every (head_dim, group) instance of one pair of storage kinds.
+template <int KT, int VT>
+SplitLaunchFn pick_dg(int head_dim, int g) {
+    switch (head_dim) {
+        case 64: return pick_g<64, KT, VT>(g);
+        case 128: return pick_g<128, KT, VT>(g);
+        case 256: return pick_g<256, KT, VT>(g);
+        default: return nullptr;
+    }
+}
+
+}  // namespace
+}  // namespace kvdec

@@ -25,9 +25,11 @@ class Case:
     """Seeded problem: q, K/V caches (codes, scales) and the cells of each slot."""
 
     def __init__(self, seed, n_q_heads, n_kv_heads, head_dim, kind=O.F16, occupied=None, begins=None,
-                 indirect_lengths=None, shuffle=False, duplicates=0, peaked=False, capacity=None, scale=None):
+                 indirect_lengths=None, shuffle=False, duplicates=0, peaked=False, capacity=None, scale=None,
+                 v_kind=None):
         r = synth.rng(seed)
         self.hq, self.hkv, self.d, self.kind = n_q_heads, n_kv_heads, head_dim, kind
+        self.vkind = kind if v_kind is None else v_kind  # V storage kind (K uses `kind`)
         self.scale = 1.0 / math.sqrt(head_dim) if scale is None else scale
         if indirect_lengths is not None:
             self.raw, cap = synth.interleaved_record_lists(indirect_lengths, r, shuffle=shuffle, duplicates=duplicates)
@@ -47,22 +49,22 @@ class Case:
             self.oracle_cells = [np.arange(b, b + n) for b, n in zip(self.begins, self.occupied)]
         self.q = synth.gen_q(r, self.n_slots, n_q_heads, head_dim)
         self.kc, self.ks = synth.gen_cache(r, kind, self.capacity, n_kv_heads, head_dim)
-        self.vc, self.vs = synth.gen_cache(r, kind, self.capacity, n_kv_heads, head_dim)
+        self.vc, self.vs = synth.gen_cache(r, self.vkind, self.capacity, n_kv_heads, head_dim)
         if peaked:
             assert kind == O.F16
             synth.plant_needles(r, self.q, self.kc, self.oracle_cells, n_kv_heads)
 
     # -- oracle
     def oracle(self):
-        return O.decode_attention(self.q, [((self.kind, self.kc, self.ks), (self.kind, self.vc, self.vs),
+        return O.decode_attention(self.q, [((self.kind, self.kc, self.ks), (self.vkind, self.vc, self.vs),
                                             self.oracle_cells)], self.hkv, self.scale)
 
     # -- GPU
     def plan(self, K, **kw):
         if self.raw is not None:
-            return K.plan(self.hq, self.hkv, self.d, self.n_slots, self.capacity, k_type=self.kind, v_type=self.kind,
-                          scale=self.scale, cells=self.raw, **kw)
-        return K.plan(self.hq, self.hkv, self.d, self.n_slots, self.capacity, k_type=self.kind, v_type=self.kind,
+            return K.plan(self.hq, self.hkv, self.d, self.n_slots, self.capacity, k_type=self.kind,
+                          v_type=self.vkind, scale=self.scale, cells=self.raw, **kw)
+        return K.plan(self.hq, self.hkv, self.d, self.n_slots, self.capacity, k_type=self.kind, v_type=self.vkind,
                       scale=self.scale, n_occupied=self.occupied, cell_begin=self.begins, **kw)
 
     def upload(self):

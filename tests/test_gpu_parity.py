@@ -220,3 +220,24 @@ def test_two_level_merge(K, kind, d, g, occ):
     # split boundaries round differently)
     out1, lse1 = c.run(K, tiles_per_split=max(1, -(-max(occ) // 128) // 8))
     check(out, lse, out1, lse1, tol=1e-3)
+
+
+MIXED = [(O.F16, O.Q8_B32), (O.F16, O.Q4_B32), (O.Q8_B32, O.Q4_B32)]
+
+
+@pytest.mark.parametrize("kv", MIXED)
+@pytest.mark.parametrize("d,g", [(64, 2), (128, 4), (128, 8), (256, 6)])
+def test_mixed_kinds_contiguous(K, kv, d, g):
+    """K stored more finely than V (the pages measure int8 K with 4-bit V):
+    the VALU kernel (G <= 5) and the matrix-core kernel (G >= 6)."""
+    kk, vk = kv
+    c = Case(70 + 3 * kk + vk + d + g, 2 * g, 2, d, kind=kk, v_kind=vk, occupied=[1500, 333])
+    check(*c.run(K), *c.oracle())
+
+
+@pytest.mark.parametrize("kv", MIXED)
+def test_mixed_kinds_indirect(K, kv):
+    kk, vk = kv
+    c = Case(80 + 3 * kk + vk, 24, 4, 256, kind=kk, v_kind=vk, indirect_lengths=[2000, 700, 5], shuffle=True,
+             duplicates=9)
+    check(*c.run(K), *c.oracle())

@@ -35,7 +35,7 @@ def run_tail(K, c, window, tail, chunk, depth, copy_stream=None):
     cells of the host tail, which holds rows [0, tail_capacity) of the cache."""
     import torch
     tail_cap = max(b + n for b, n in tail)
-    p = K.plan(c.hq, c.hkv, c.d, c.n_slots, c.capacity, k_type=c.kind, v_type=c.kind, scale=c.scale,
+    p = K.plan(c.hq, c.hkv, c.d, c.n_slots, c.capacity, k_type=c.kind, v_type=c.vkind, scale=c.scale,
                n_occupied=[n for _, n in window], cell_begin=[b for b, _ in window], n_tail=[n for _, n in tail],
                tail_begin=[b for b, _ in tail], tail_capacity_cells=tail_cap, tail_chunk_cells=chunk,
                tail_ring_depth=depth)
@@ -107,4 +107,11 @@ def test_quantized_tail_two_level_merge(K):
     c = Case(57, 24, 4, 256, kind=O.Q8_B32, occupied=[11000])
     out, lse, p = run_tail(K, c, window=[(9000, 2000)], tail=[(0, 9000)], chunk=8192, depth=2)
     assert p.info()["n_tail_chunks"] == 2
+    check(out, lse, *c.oracle())
+
+
+def test_mixed_kind_tail(K):
+    """int8 K with 4-bit V, GQA-6 head_dim 256: window + streamed tail."""
+    c = Case(58, 24, 4, 256, kind=O.Q8_B32, v_kind=O.Q4_B32, occupied=[4000])
+    out, lse, _ = run_tail(K, c, window=[(1500, 2500)], tail=[(0, 1500)], chunk=512, depth=3)
     check(out, lse, *c.oracle())

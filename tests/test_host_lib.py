@@ -163,6 +163,10 @@ def test_plan_errors():
     assert _status(lambda: K.plan(32, 8, 128, 1, 100, cells=[[3, -2]], n_cu=256)) == K.E_RANGE
     assert _status(lambda: K.plan(32, 2, 128, 1, 100, **base)) == K.E_UNSUPPORTED      # G = 16
     assert _status(lambda: K.plan(32, 8, 128, 1, 100, k_type=K.Q8_B32, v_type=K.F16, **base)) == K.E_UNSUPPORTED
+    # V stored more finely than K has no kernel; K more finely than V does
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, k_type=K.Q4_B32, v_type=K.Q8_B32, **base)) == K.E_UNSUPPORTED
+    for kt, vt in ((K.F16, K.Q8_B32), (K.F16, K.Q4_B32), (K.Q8_B32, K.Q4_B32)):
+        K.plan(32, 8, 128, 1, 100, k_type=kt, v_type=vt, **base).close()
     assert _status(lambda: K.plan(32, 8, 128, 65, 100, n_occupied=[1] * 65, n_cu=256)) == K.E_UNSUPPORTED
     assert _status(lambda: K.plan(32, 8, 128, 1, 100, cells=[[1]], n_tail=[1], tail_capacity_cells=1,
                                   n_cu=256)) == K.E_UNSUPPORTED
