@@ -365,9 +365,15 @@ WORKLOADS = {
 # ---------------------------------------------------------------- traffic from committed counters
 
 def kernel_source_hash():
+    """Hash of every source the split and merge kernels are compiled from."""
+    import glob
+    csrc = os.path.join(ROOT, "long_context_decode_kv_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(csrc, "*.hip"))) + [os.path.join(csrc, f) for f in
+                                                              ("split_kernels.h", "internal.h")]
     h = hashlib.sha256()
-    for f in ("kernels.hip", "internal.h"):
-        h.update(open(os.path.join(ROOT, "long_context_decode_kv_amd", "csrc", f), "rb").read())
+    for f in files:
+        if os.path.basename(f) != "probe.hip":
+            h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
 
