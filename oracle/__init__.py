@@ -1,4 +1,5 @@
-"""Float64 CPU oracle for single-query grouped-query decode attention.
+"""Float64 CPU oracle for grouped-query decode attention (one or several query
+rows per slot).
 
 Test infrastructure only.  Nothing on the product path imports this package:
 only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
@@ -19,5 +20,6 @@ from .kvdec_oracle import (  # noqa: F401
     partial_row,
     merge_partials,
     decode_attention,
+    decode_attention_multi,
     compact_plan,
 )

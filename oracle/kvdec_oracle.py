@@ -1,6 +1,7 @@
-"""Float64 CPU oracle for single-query (n_q = 1) grouped-query decode attention
-over a KV cache, with block-scaled int8 / 4-bit caches, indirect cell plans and
-the log-sum-exp merge of partial results.
+"""Float64 CPU oracle for grouped-query decode attention over a KV cache --
+single-query (n_q = 1) and multi-query with a positional mask -- with
+block-scaled int8 / 4-bit caches, indirect cell plans and the log-sum-exp
+merge of partial results.
 
 Test infrastructure only: only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import it.  It shares no code with the
@@ -15,7 +16,8 @@ Sources (web pages, cited by title and section):
 * "KVARN KV Performance optimizations" (beellama.cpp issue 140), "What was
   implemented" item 3 (duplicate filtering, first occurrence kept, capacity
   checks), item 4 (plans grouped by physical 128-cell record, one monotonic
-  segment per record, -1 holes kept) and item 9 (partial windows keep the
+  segment per record, -1 holes kept), item 7 (split decode for up to 8 query
+  rows, which needs an attention mask) and item 9 (partial windows keep the
   running maximum, numerator and denominator and are merged afterwards).
 
 Readings where the pages are silent (each also listed in the design doc):
@@ -30,7 +32,9 @@ Readings where the pages are silent (each also listed in the design doc):
   (-inf, 0, 0);
 * an indirect entry -1 is a hole (skipped); any other entry is attended with
   multiplicity (the plan builder is what removes duplicates);
-* no positional mask: with one query every attended cell is visible.
+* no positional mask with one query: every attended cell is visible; with
+  several query rows per slot, row t at position q_pos[s][t] sees the cells
+  whose position (cell_pos[c], or the cell index c) is at most q_pos[s][t].
 
 Pins (tests/test_oracle_pins.py): exhaustive f16 decoding against the IEEE
 formula, the dequantisation table, closed forms (one cell, two cells,
@@ -205,6 +209,46 @@ def decode_attention(q, regions, n_kv_heads, scale, return_partials=False):
                         region_parts[r][2][s, h] = o
     if return_partials:
         return out, lse, region_parts
+    return out, lse
+
+
+def decode_attention_multi(q, regions, n_kv_heads, scale, q_pos, cell_pos=None):
+    """Multi-query decode attention with a positional (causal) mask: several
+    query rows per slot, as in speculative verification, where split decoding
+    serves up to 8 query rows and a multi-query call must carry an attention
+    mask ("KVARN KV Performance optimizations", "What was implemented"
+    item 7).
+
+    q: [S][NQ][Hq][D], query row t of slot s at position q_pos[s][t].
+    regions: as in ``decode_attention``.
+    cell_pos: None (a cell's position is its cell index) or an integer array
+        indexed by cell.
+    Query row (s, t) attends to every cell of slot s (holes skipped,
+    multiplicity kept, union over the regions) whose position is at most
+    q_pos[s][t]; a row that sees no cell gets output 0 and lse -inf.
+
+    Returns out [S][NQ][Hq][D] and lse [S][NQ][Hq] in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    n_slots, n_q, n_q_heads, head_dim = q.shape
+    group = n_q_heads // n_kv_heads
+    qp = np.asarray(q_pos, dtype=np.int64).reshape(n_slots, n_q)
+    out = np.zeros((n_slots, n_q, n_q_heads, head_dim))
+    lse = np.full((n_slots, n_q, n_q_heads), -math.inf)
+    for s in range(n_slots):
+        for t in range(n_q):
+            for g in range(n_kv_heads):
+                ks, vs = [], []
+                for k_cache, v_cache, cells in regions:
+                    live = [int(c) for c in cells[s] if int(c) != -1]
+                    pos = live if cell_pos is None else [int(cell_pos[c]) for c in live]
+                    seen = [c for c, p in zip(live, pos) if p <= qp[s, t]]
+                    ks.append(_rows(k_cache, seen, g))
+                    vs.append(_rows(v_cache, seen, g))
+                k_all = np.concatenate(ks, axis=0)
+                v_all = np.concatenate(vs, axis=0)
+                for h in range(g * group, (g + 1) * group):
+                    out[s, t, h], lse[s, t, h] = attend_row(q[s, t, h], k_all, v_all, scale)
     return out, lse
 
 

@@ -434,3 +434,77 @@ def test_compact_plan_invariants():
     lists, cap = synth.interleaved_record_lists([131072, 65536, 20000, 777])
     entries, offsets = O.compact_plan(lists, cap)
     assert cap == 1700 * 128 and len(entries) == cap and int((entries == -1).sum()) == 215
+
+
+# ---------------------------------------------------------------- multi-query (positional mask)
+
+def _multi_problem(seed, kind=O.F16, n_slots=2, n_q=3, hq=4, hkv=2, d=32, n=60):
+    r = synth.rng(seed)
+    q = synth.gen_q(r, n_slots * n_q, hq, d).astype(np.float64).reshape(n_slots, n_q, hq, d)
+    kc, ks = synth.gen_cache(r, kind, n, hkv, d)
+    vc, vs = synth.gen_cache(r, kind, n, hkv, d)
+    return r, q, (kind, kc, ks), (kind, vc, vs)
+
+
+def test_multi_query_all_visible_equals_single_query():
+    """Every cell visible: each query row is the single-query result of that row."""
+    r, q, kcache, vcache = _multi_problem(40)
+    cells = [list(range(0, 60, 3)) + [-1, 5, 5], list(range(10, 50))]
+    got, glse = O.decode_attention_multi(q, [(kcache, vcache, cells)], 2, 0.17, q_pos=np.full((2, 3), 10 ** 6))
+    for t in range(3):
+        want, wlse = O.decode_attention(q[:, t], [(kcache, vcache, cells)], 2, 0.17)
+        assert np.array_equal(got[:, t], want) and np.array_equal(glse[:, t], wlse)
+
+
+def test_multi_query_matches_torch_sdpa_with_boolean_mask():
+    """torch's float64 scaled_dot_product_attention with an explicit mask built
+    from the cell positions (a random permutation as cell_pos)."""
+    r, q, kcache, vcache = _multi_problem(41, n_q=4, hq=6, hkv=2, d=64, n=90)
+    cell_pos = r.permutation(90) + 1000
+    cells = [list(range(90)), list(range(20, 77))]
+    q_pos = np.array([[1010, 1040, 1041, 1089], [1000, 1030, 1060, 1200]])
+    got, glse = O.decode_attention_multi(q, [(kcache, vcache, cells)], 2, 0.125, q_pos=q_pos, cell_pos=cell_pos)
+    kd = kcache[1].view(np.float16).astype(np.float64)
+    vd = vcache[1].view(np.float16).astype(np.float64)
+    for s in range(2):
+        idx = np.array(cells[s])
+        K = torch.from_numpy(kd[idx]).permute(1, 0, 2).repeat_interleave(3, dim=0)   # [Hq, n, D]
+        V = torch.from_numpy(vd[idx]).permute(1, 0, 2).repeat_interleave(3, dim=0)
+        Q = torch.from_numpy(q[s]).permute(1, 0, 2)                                  # [Hq, NQ, D]
+        mask = torch.from_numpy(cell_pos[idx][None, :] <= q_pos[s][:, None])         # [NQ, n]
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=0.125)
+        assert np.allclose(got[s], ref.permute(1, 0, 2).numpy(), atol=1e-13, rtol=0)
+        sc = (K @ Q.transpose(1, 2)).transpose(1, 2) * 0.125                         # [Hq, NQ, n]
+        sc = sc.masked_fill(~mask[None], -math.inf)
+        assert np.allclose(glse[s], torch.logsumexp(sc, dim=-1).T.numpy(), atol=1e-13, rtol=0)
+
+
+@pytest.mark.parametrize("kind", [O.F16, O.Q4_B32])
+def test_multi_query_brute_force_mpmath(kind):
+    """Masked softmax written out term by term in 50-digit arithmetic: row t
+    attends exactly to the cells whose index is at most q_pos[t]."""
+    r, q, kcache, vcache = _multi_problem(42 + kind, n_slots=1, n_q=3, hq=2, hkv=1, d=32, n=7)
+    cells = [[0, 3, 5, -1, 6, 2]]
+    q_pos = np.array([[2, 5, 6]])
+    got, glse = O.decode_attention_multi(q, [(kcache, vcache, cells)], 1, 0.25, q_pos=q_pos)
+    visible = {2: [0, 2], 5: [0, 3, 5, 2], 6: [0, 3, 5, 6, 2]}  # by hand
+    for t in range(3):
+        want, wlse = _mp_attention(q[:, t], kcache, vcache, [visible[int(q_pos[0, t])]], 1, 0.25)
+        assert np.allclose(got[:, t], want, atol=1e-13, rtol=1e-13)
+        assert np.allclose(glse[:, t], wlse, atol=1e-13, rtol=1e-13)
+
+
+def test_multi_query_causality_and_empty_rows():
+    """Changing cells past a row's position leaves the row unchanged; changing
+    a visible cell does not; a row before every cell sees nothing."""
+    r, q, kcache, vcache = _multi_problem(43, n_slots=1, n_q=3, n=40)
+    cells = [list(range(40))]
+    q_pos = np.array([[-1, 20, 39]])
+    base, blse = O.decode_attention_multi(q, [(kcache, vcache, cells)], 2, 0.2, q_pos=q_pos)
+    assert np.all(base[0, 0] == 0) and np.all(blse[0, 0] == -math.inf)
+    k2, v2 = kcache[1].copy(), vcache[1].copy()
+    k2[21:] ^= 0x0155
+    v2[21:] ^= 0x0155
+    got, glse = O.decode_attention_multi(q, [((O.F16, k2, None), (O.F16, v2, None), cells)], 2, 0.2, q_pos=q_pos)
+    assert np.array_equal(got[0, 1], base[0, 1]) and np.array_equal(glse[0, 1], blse[0, 1])
+    assert not np.allclose(got[0, 2], base[0, 2])
