@@ -19,6 +19,9 @@ Workloads (synthetic N(0, 1) data of the named model's attention shape):
   gqa6-q8k-q4v      the same with int8 K and 4-bit V
   rolling-ctx40960  qwen3-8b shape at ctx 40960: newest 14000 cells resident,
                     oldest 26960 streamed from pinned host memory per layer
+  qwen3-8b-ctx16k-verify4
+                    the qwen3-8b-ctx16k caches with 4 query rows per step
+                    (speculative verification, causal positional mask)
   qwen3-8b-ctx16k-1launch
                     secondary figure for the qwen3-8b-ctx16k data: all 36
                     layers as 36 slots of ONE kvdec_attend call (ignores the
@@ -137,17 +140,21 @@ def algorithmic_bytes(n_cells_attended, hkv, d, kind, n_slots, hq, plan_entries=
 
 
 class ContiguousModel(Workload):
-    def __init__(self, name, layers, hq, hkv, d, capacity, occupied):
+    def __init__(self, name, layers, hq, hkv, d, capacity, occupied, n_q=1):
         self.name, self.layers, self.hq, self.hkv, self.d = name, layers, hq, hkv, d
-        self.capacity, self.occupied, self.kind = capacity, occupied, 0
+        self.capacity, self.occupied, self.kind, self.n_q = capacity, occupied, 0, n_q
 
     def config(self):
-        return {"workload": self.name, "layers": self.layers, "q_heads": self.hq, "kv_heads": self.hkv,
-                "head_dim": self.d, "cells_occupied": self.occupied, "cells_capacity": self.capacity,
-                "batch": 1, "kv_dtype": "f16", "cells_per_tile": 128}
+        c = {"workload": self.name, "layers": self.layers, "q_heads": self.hq, "kv_heads": self.hkv,
+             "head_dim": self.d, "cells_occupied": self.occupied, "cells_capacity": self.capacity,
+             "batch": 1, "kv_dtype": "f16", "cells_per_tile": 128}
+        if self.n_q > 1:
+            c.update({"query_rows_per_slot": self.n_q, "mask": "causal: row t at the position of occupied cell "
+                                                                "n - n_q + t (speculative verification)"})
+        return c
 
     def algorithmic_bytes_per_launch(self):
-        return algorithmic_bytes(self.occupied, self.hkv, self.d, 0, 1, self.hq)
+        return algorithmic_bytes(self.occupied, self.hkv, self.d, 0, self.n_q, self.hq)
 
     def setup(self, K, torch, seed0):
         from long_context_decode_kv_amd import synth
@@ -156,17 +163,21 @@ class ContiguousModel(Workload):
             s = seed0 * 100 + layer
             self.k.append(synth.device_f16_cache(3 * s, self.capacity, self.hkv, self.d))
             self.v.append(synth.device_f16_cache(3 * s + 1, self.capacity, self.hkv, self.d))
-            self.q.append(synth.device_q(3 * s + 2, 1, self.hq, self.d))
-            self.out.append(torch.empty(1, self.hq, self.d, device="cuda"))
-            self.lse.append(torch.empty(1, self.hq, device="cuda"))
+            self.q.append(synth.device_q(3 * s + 2, self.n_q, self.hq, self.d))
+            self.out.append(torch.empty(self.n_q, self.hq, self.d, device="cuda"))
+            self.lse.append(torch.empty(self.n_q, self.hq, device="cuda"))
             if layer % 8 == 7:
                 log(f"  generated {layer + 1}/{self.layers} layers")
-        self.plan = K.plan(self.hq, self.hkv, self.d, 1, self.capacity, n_occupied=[self.occupied])
+        self.plan = K.plan(self.hq, self.hkv, self.d, 1, self.capacity, n_occupied=[self.occupied],
+                           n_queries=self.n_q)
         self.ws = K.workspace(self.plan)
+        self.q_pos = None
+        if self.n_q > 1:
+            self.q_pos = torch.arange(self.occupied - self.n_q, self.occupied, dtype=torch.int32, device="cuda")
 
     def launch(self, K, layer):
         K.attend(self.plan, self.q[layer], self.k[layer], self.v[layer], self.ws, out=self.out[layer],
-                 lse=self.lse[layer])
+                 lse=self.lse[layer], q_pos=self.q_pos)
 
     def oracle_sample(self, budget_s):
         """Time the float64 oracle on host copies of the workload's shape:
@@ -175,13 +186,18 @@ class ContiguousModel(Workload):
         import oracle as O
         from long_context_decode_kv_amd import synth
         r = synth.rng(99)
-        q = synth.gen_q(r, 1, self.hq, self.d)
+        q = synth.gen_q(r, self.n_q, self.hq, self.d)
         kc = synth.gen_f16_cache(r, self.occupied, self.hkv, self.d)
         vc = synth.gen_f16_cache(r, self.occupied, self.hkv, self.d)
         cells = [np.arange(self.occupied)]
+        regions = [((O.F16, kc, None), (O.F16, vc, None), cells)]
         done, t0 = 0, time.perf_counter()
         while True:
-            O.decode_attention(q, [((O.F16, kc, None), (O.F16, vc, None), cells)], self.hkv, 1 / math.sqrt(self.d))
+            if self.n_q > 1:
+                qp = np.arange(self.occupied - self.n_q, self.occupied)[None]
+                O.decode_attention_multi(q[None], regions, self.hkv, 1 / math.sqrt(self.d), qp)
+            else:
+                O.decode_attention(q, regions, self.hkv, 1 / math.sqrt(self.d))
             done += 1
             el = time.perf_counter() - t0
             if el >= budget_s or done >= self.layers:
@@ -357,6 +373,8 @@ WORKLOADS = {
     "gqa6-q4": lambda: Gqa6Quant("gqa6-q4", 2),
     "gqa6-q8k-q4v": lambda: Gqa6Quant("gqa6-q8k-q4v", 1, v_kind=2),
     "rolling-ctx40960": lambda: RollingWindow(),
+    "qwen3-8b-ctx16k-verify4": lambda: ContiguousModel("qwen3-8b-ctx16k-verify4", 36, 32, 8, 128, 16384, 13100,
+                                                        n_q=4),
     "qwen3-8b-ctx16k-1launch": lambda: ContiguousModelOneLaunch("qwen3-8b-ctx16k-1launch", 36, 32, 8, 128, 16384,
                                                                 13100),
 }
@@ -540,9 +558,9 @@ def main():
                        tiles_per_split=info["tiles_per_split"]),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "%s<%d,%d,%s,%s>" % ("split_mfma_kernel" if wl.hq // wl.hkv >= 6 and wl.d >= 128
-                                                    else "split_kernel", wl.d, wl.hq // wl.hkv, KIND[wl.kind],
-                                                    KIND[getattr(wl, "v_kind", wl.kind)]),
+                     "kernel": ("split_mfma_kernel<%d,rows %d,%s,%s>" if info.get("matrix_cores") else
+                                "split_kernel<%d,%d,%s,%s>") % (wl.d, wl.hq // wl.hkv * getattr(wl, "n_q", 1),
+                                                                KIND[wl.kind], KIND[getattr(wl, "v_kind", wl.kind)]),
                      "algorithmic_bytes_per_launch": bytes_launch, "launches_per_step": launches_per_step,
                      "avg_launch_us": round(avg_us, 3), "isolated_launch_event_us": round(bracketed_us, 3),
                      "read_ceiling": ceiling},

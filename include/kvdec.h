@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_VERSION 10000 /* 1.0.0 */
+#define KVDEC_VERSION 10100 /* 1.1.0: n_queries, q_pos, cell_pos */
 
 /* Status codes. */
 #define KVDEC_OK 0
@@ -85,7 +85,7 @@ extern "C" {
  *   group size G = n_q_heads / n_kv_heads must lie in 1..16; kernels are
  *   built for G <= 8, larger groups give KVDEC_E_UNSUPPORTED.
  * head_dim: 64, 128 or 256.
- * n_slots: 1..KVDEC_MAX_SLOTS (one query row per slot).
+ * n_slots: 1..KVDEC_MAX_SLOTS.
  * k_type, v_type: KVDEC_F16 / KVDEC_Q8_B32 / KVDEC_Q4_B32.  Kernels exist for
  *   K stored at least as finely as V: equal kinds, or (K, V) = (f16, int8),
  *   (f16, 4-bit), (int8, 4-bit) -- int8 K with 4-bit V is the pair of the
@@ -121,6 +121,16 @@ extern "C" {
  * tiles_per_split: 128-cell tiles per workgroup; 0 lets the planner choose
  *   so that the launch fills the device.  Only the floating-point summation
  *   order depends on it.
+ *
+ * n_queries: query rows per slot, 1..8 (0 means 1).  Several rows per slot
+ *   are the verification step of speculative decoding: split decoding serves
+ *   up to 8 query rows, and such a call carries an attention mask ("KVARN KV
+ *   Performance optimizations", "What was implemented" item 7).  Here the
+ *   mask is positional: query row t of slot s sees the slot's cells whose
+ *   position is at most q_pos[s][t] (kvdec_io).  All G * n_queries rows of a
+ *   KV head share every K / V row read; kernels exist for head_dim 128 / 256
+ *   with G * n_queries <= 16 (and, with one query row, any G <= 8 and
+ *   G <= 16 for head_dim 128 / 256).
  */
 typedef struct kvdec_problem {
     int32_t n_q_heads;
@@ -141,7 +151,7 @@ typedef struct kvdec_problem {
     int64_t tail_capacity_cells;
     int64_t tail_chunk_cells;
     int32_t tail_ring_depth;
-    int32_t reserved;
+    int32_t n_queries; /* query rows per slot, 1..8; 0 means 1 */
 } kvdec_problem;
 
 /* Opaque, immutable plan. */
@@ -150,7 +160,9 @@ typedef struct kvdec_plan kvdec_plan_t;
 /*
  * Device buffers and outputs of one kvdec_attend call.
  *
- * q: device fp32 [n_slots][n_q_heads][head_dim].
+ * q: device fp32 [n_slots][n_queries][n_q_heads][head_dim] (n_queries = 1:
+ *   [n_slots][n_q_heads][head_dim]); out, lse and the partial triple below
+ *   carry the same [n_queries] axis after the slot.
  * k, v: device code arrays.  Row (cell c, KV head g) starts at byte
  *   c * cell_stride + g * head_stride; a row holds head_dim f16 values,
  *   head_dim int8 codes, or head_dim / 2 bytes of 4-bit codes.  A stride of 0
@@ -165,13 +177,18 @@ typedef struct kvdec_plan kvdec_plan_t;
  * k_tail, v_tail (+ k_tail_scales, v_tail_scales): pinned host tail arrays
  *   when the plan has a tail, else NULL.  They must stay valid and unchanged
  *   until the work enqueued by the call has finished.
- * out: device fp32 [n_slots][n_q_heads][head_dim] or NULL.
- * lse: device fp32 [n_slots][n_q_heads] or NULL.
- * part_m, part_l, part_o: device fp32 [n_slots][n_q_heads] (m, l) and
- *   [n_slots][n_q_heads][head_dim] (o): the call's whole result as one
+ * out: device fp32 [n_slots][n_queries][n_q_heads][head_dim] or NULL.
+ * lse: device fp32 [n_slots][n_queries][n_q_heads] or NULL.
+ * part_m, part_l, part_o: device fp32 [n_slots][n_queries][n_q_heads] (m, l)
+ *   and [n_slots][n_queries][n_q_heads][head_dim] (o): the call's whole result as one
  *   partial (m in score units, l and o relative to e^m, o unnormalised), for
  *   merging with other partials through kvdec_merge; all three or none.
  * At least one of out and the partial triple must be given.
+ * q_pos: device int32 [n_slots][n_queries], required when n_queries > 1 and
+ *   ignored otherwise: the position of each query row.
+ * cell_pos: device int32 [capacity_cells] positions of the device cells, or
+ *   NULL: a device cell's position is its cell index.  A host-tail cell's
+ *   position is its index in the tail arrays.  Used with n_queries > 1 only.
  */
 typedef struct kvdec_io {
     const float* q;
@@ -193,6 +210,8 @@ typedef struct kvdec_io {
     float* part_m;
     float* part_l;
     float* part_o;
+    const int32_t* q_pos;
+    const int32_t* cell_pos;
 } kvdec_io;
 
 /* One partial result set for kvdec_merge: rows are (slot, query head) pairs,
@@ -231,6 +250,8 @@ typedef struct kvdec_plan_info {
     int64_t n_entries;        /* indirect entries (0 when contiguous) */
     int64_t n_tail_chunks;    /* tail chunks over all slots */
     int64_t workspace_bytes;
+    int32_t n_queries;        /* query rows per slot */
+    int32_t matrix_cores;     /* 1: served by the matrix-core kernel */
 } kvdec_plan_info;
 
 int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info);

@@ -38,7 +38,13 @@ void common_args(const kvdec_plan_t& p, const kvdec_io& io, kvdec::SplitArgs& a)
     a.pm = io.part_m;
     a.pl = io.part_l;
     a.po = io.part_o;
-    a.acc_rows = p.n_slots * p.n_q_heads;
+    a.acc_rows = p.n_slots * p.n_q * p.n_q_heads;
+    a.n_q = p.n_q;
+    a.group = p.group;
+    // positions are used with several query rows per slot only
+    a.q_pos = p.n_q > 1 ? io.q_pos : nullptr;
+    a.cell_pos = p.n_q > 1 ? io.cell_pos : nullptr;
+    a.pos_offset = 0;
 }
 
 }  // namespace
@@ -113,6 +119,8 @@ int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info) {
     info->n_entries = (int64_t)plan->cells.size();
     info->n_tail_chunks = plan->n_tail_chunks;
     info->workspace_bytes = (int64_t)plan->workspace_bytes;
+    info->n_queries = plan->n_q;
+    info->matrix_cores = kvdec::uses_matrix_cores(plan->group, plan->n_q, plan->head_dim) ? 1 : 0;
     return KVDEC_OK;
 }
 
@@ -179,7 +187,10 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
         if ((kvdec::is_scaled(p.k_type) && !io->k_tail_scales) || (kvdec::is_scaled(p.v_type) && !io->v_tail_scales))
             return fail(KVDEC_E_INVALID, "tail scales needed for block-scaled kinds");
     }
-    if (!kvdec::split_instance_exists(D, p.group, p.k_type, p.v_type))
+    if (p.n_q > 1 && (!io->q_pos || !aligned(io->q_pos, 4)))
+        return fail(KVDEC_E_INVALID, "several query rows per slot need q_pos (device int32 [n_slots][n_queries])");
+    if (!aligned(io->cell_pos, 4)) return fail(KVDEC_E_INVALID, "cell_pos must be 4-byte aligned");
+    if (!kvdec::split_instance_exists(D, p.group, p.n_q, p.k_type, p.v_type))
         return fail(KVDEC_E_UNSUPPORTED, "no kernel for this configuration");
 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -214,7 +225,7 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
     }
 
     if (!p.has_tail) {
-        const int e = kvdec::launch_split(D, p.group, p.k_type, p.v_type, a, stream);
+        const int e = kvdec::launch_split(D, p.group, p.n_q, p.k_type, p.v_type, a, stream);
         if (e != hipSuccess) return device_fail((hipError_t)e, "split kernel launch");
         return KVDEC_OK;
     }
@@ -254,7 +265,7 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
         destroy();
         return device_fail(e, "stream ordering");
     }
-    int le = kvdec::launch_split(D, p.group, p.k_type, p.v_type, a, stream);
+    int le = kvdec::launch_split(D, p.group, p.n_q, p.k_type, p.v_type, a, stream);
     if (le != hipSuccess) {
         destroy();
         return device_fail((hipError_t)le, "window kernel launch");
@@ -319,12 +330,15 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
             t.slot[0].wg_begin = 0;
             t.slot[0].part_begin = 0;
             t.slot[0].to_acc = (c + 1 < n_chunks) ? 1 : 0;
-            t.slot[0].n_clusters = kvdec::merge_clusters(splits, kvdec::merge_chunk(D, p.group));
+            t.slot[0].n_clusters = kvdec::merge_clusters(splits, kvdec::merge_chunk(D, p.rec_rows));
+            // a tail cell's position is its index in the host tail
+            t.cell_pos = nullptr;
+            t.pos_offset = c0;
             t.slot[0].cl_begin = 0;
             t.n_workgroups = splits * p.n_kv_heads;
             t.acc_in = acc[c % 2];
             t.acc_out = acc[(c + 1) % 2];
-            le = kvdec::launch_split(D, p.group, p.k_type, p.v_type, t, stream);
+            le = kvdec::launch_split(D, p.group, p.n_q, p.k_type, p.v_type, t, stream);
             if (le != hipSuccess) {
                 e = (hipError_t)le;
                 break;

@@ -17,7 +17,6 @@ namespace kvdec {
 constexpr int kTile = KVDEC_TILE_CELLS;  // cells per tile / per physical record
 constexpr int kBlock = 32;               // elements sharing one f16 scale
 constexpr int kThreads = 256;            // threads per split workgroup (4 waves)
-constexpr int kMaxGroup = 8;             // largest compiled GQA group
 constexpr int kMergeMaxParts = 64;       // kvdec_merge fan-in
 
 // Bytes of one stored (cell, KV head) row of codes.
@@ -25,6 +24,19 @@ inline constexpr int64_t row_bytes(int type, int head_dim) {
     return type == KVDEC_F16 ? 2 * (int64_t)head_dim : type == KVDEC_Q8_B32 ? (int64_t)head_dim : (int64_t)head_dim / 2;
 }
 inline constexpr bool is_scaled(int type) { return type != KVDEC_F16; }
+
+// Which kernel serves a problem, and the rows of its split records (the
+// query rows one (slot, KV head) workgroup serves).  One query row per slot
+// with G <= 5 (or head_dim 64) runs on the VALU kernel, whose records hold
+// the G rows; wider groups and several query rows per slot (head_dim 128 /
+// 256, G * n_q <= 16) run on the matrix-core kernel, whose records hold the
+// G * n_q rows padded to 8 or 16.
+constexpr bool uses_matrix_cores(int group, int n_q, int head_dim) {
+    return (n_q > 1 || group >= 6) && head_dim >= 128;
+}
+constexpr int record_rows(int group, int n_q, int head_dim) {
+    return uses_matrix_cores(group, n_q, head_dim) ? (group * n_q <= 8 ? 8 : 16) : group;
+}
 
 // Split records one merge round reads: a merging workgroup issues the loads
 // of this many records before it waits (UB records per thread and float4
@@ -84,6 +96,11 @@ struct SplitArgs {
     const float* acc_in;     // running partial merged in by the last workgroup, or null
     float* acc_out;          // running partial written for slots with to_acc
     int32_t acc_rows;        // rows of a running partial: m2 [rows], l [rows], o [rows][D]
+    int32_t n_q;             // query rows per slot (q, out, lse rows: [slot][n_q][Hq])
+    const int32_t* q_pos;    // [slots][n_q] positions of the query rows (n_q > 1)
+    const int32_t* cell_pos; // [capacity] positions of device cells, or null: cell index + pos_offset
+    int64_t pos_offset;      // added to a cell index to give its position (no cell_pos)
+    int32_t group;           // query heads per KV head (G)
     int32_t pad0;
     float scale_log2;        // scale * log2(e)
     int32_t n_slots;         // slots in this launch
@@ -112,15 +129,15 @@ struct MergeArgs {
 // Per pair of storage kinds, the launcher of the split-kernel instance for
 // (head_dim, group), or null.
 using SplitLaunchFn = int (*)(const SplitArgs&, void*);
-SplitLaunchFn pick_split_f16(int head_dim, int group);
-SplitLaunchFn pick_split_q8(int head_dim, int group);
-SplitLaunchFn pick_split_q4(int head_dim, int group);
-SplitLaunchFn pick_split_f16_q8(int head_dim, int group);
-SplitLaunchFn pick_split_f16_q4(int head_dim, int group);
-SplitLaunchFn pick_split_q8_q4(int head_dim, int group);
-int launch_split(int head_dim, int group, int k_type, int v_type, const SplitArgs& a, void* stream);
+SplitLaunchFn pick_split_f16(int head_dim, int group, int n_q);
+SplitLaunchFn pick_split_q8(int head_dim, int group, int n_q);
+SplitLaunchFn pick_split_q4(int head_dim, int group, int n_q);
+SplitLaunchFn pick_split_f16_q8(int head_dim, int group, int n_q);
+SplitLaunchFn pick_split_f16_q4(int head_dim, int group, int n_q);
+SplitLaunchFn pick_split_q8_q4(int head_dim, int group, int n_q);
+int launch_split(int head_dim, int group, int n_q, int k_type, int v_type, const SplitArgs& a, void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
-bool split_instance_exists(int head_dim, int group, int k_type, int v_type);
+bool split_instance_exists(int head_dim, int group, int n_q, int k_type, int v_type);
 
 }  // namespace kvdec
 
@@ -128,6 +145,8 @@ bool split_instance_exists(int head_dim, int group, int k_type, int v_type);
 // The plan object behind the opaque kvdec_plan_t.
 struct kvdec_plan {
     int32_t n_q_heads = 0, n_kv_heads = 0, head_dim = 0, n_slots = 0, group = 0;
+    int32_t n_q = 1;       // query rows per slot
+    int32_t rec_rows = 0;  // rows of a split record (record_rows)
     int32_t k_type = 0, v_type = 0;
     float scale = 0.f;
     int64_t capacity = 0;

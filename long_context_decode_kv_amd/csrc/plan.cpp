@@ -108,20 +108,26 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
         err = "a host tail is supported with contiguous cells only";
         return KVDEC_E_UNSUPPORTED;
     }
-    if (group > kMaxGroup) {
-        err = "no kernel for group sizes above 8";
+    if (p.n_queries < 0 || p.n_queries > 8) {
+        err = "n_queries must be 0 (one) or 1..8";
+        return KVDEC_E_INVALID;
+    }
+    const int n_q = p.n_queries ? p.n_queries : 1;
+    if (!split_instance_exists(p.head_dim, group, n_q, p.k_type, p.v_type)) {
+        err = "no kernel for this (head_dim, group, n_queries, k_type, v_type): groups above 8 and several "
+              "query rows need head_dim 128 or 256 and G * n_queries <= 16, and K is stored at least as "
+              "finely as V";
         return KVDEC_E_UNSUPPORTED;
     }
-    if (!split_instance_exists(p.head_dim, group, p.k_type, p.v_type)) {
-        err = "no kernel for this (head_dim, group, k_type, v_type)";
-        return KVDEC_E_UNSUPPORTED;
-    }
+    const int rec_rows = record_rows(group, n_q, p.head_dim);
 
     plan.n_q_heads = p.n_q_heads;
     plan.n_kv_heads = p.n_kv_heads;
     plan.head_dim = p.head_dim;
     plan.n_slots = p.n_slots;
     plan.group = group;
+    plan.n_q = n_q;
+    plan.rec_rows = rec_rows;
     plan.k_type = p.k_type;
     plan.v_type = p.v_type;
     plan.scale = p.scale;
@@ -198,7 +204,7 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
     }
     plan.n_workgroups = (int32_t)wgs;
     plan.n_part_records = (int32_t)wgs;
-    const int chunk = merge_chunk(p.head_dim, group);
+    const int chunk = merge_chunk(p.head_dim, rec_rows);
     int64_t clusters = 0;
     for (auto& sa : plan.slots) {
         sa.n_clusters = merge_clusters(sa.n_splits, chunk);
@@ -254,18 +260,18 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
     plan.off_tickets = off;
     off = align_up(off + sizeof(uint32_t) * ((size_t)p.n_slots * p.n_kv_heads + (size_t)clusters), 256);
     plan.off_parts = off;
-    plan.parts_o_bytes = sizeof(float) * (size_t)part_capacity * group * D;
+    plan.parts_o_bytes = sizeof(float) * (size_t)part_capacity * rec_rows * D;
     if (plan.parts_o_bytes >= (1ull << 31)) {
         err = "too many split records";
         return KVDEC_E_UNSUPPORTED;
     }
     off = align_up(off + plan.parts_o_bytes, 256);
     plan.off_parts_m = off;
-    off = align_up(off + sizeof(float) * (size_t)part_capacity * group, 256);
+    off = align_up(off + sizeof(float) * (size_t)part_capacity * rec_rows, 256);
     plan.off_parts_l = off;
-    off = align_up(off + sizeof(float) * (size_t)part_capacity * group, 256);
+    off = align_up(off + sizeof(float) * (size_t)part_capacity * rec_rows, 256);
     if (has_tail) {
-        const size_t rows = (size_t)p.n_slots * p.n_q_heads;
+        const size_t rows = (size_t)p.n_slots * n_q * p.n_q_heads;
         plan.off_acc0 = off;
         off = align_up(off + sizeof(float) * rows * (D + 2), 256);
         plan.off_acc1 = off;

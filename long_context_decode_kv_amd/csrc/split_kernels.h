@@ -272,6 +272,21 @@ __device__ __forceinline__ float4 ld_dev4(__amdgpu_buffer_rsrc_t r, int64_t off_
     return make_float4(v.x, v.y, v.z, v.w);
 }
 
+// Output row of a record row.  A (slot, KV head) record holds the G query
+// heads of each of the slot's n_q query rows, query-major; rows of q, out,
+// lse and the partial outputs are [slot][n_q][Hq].  Record rows at or past
+// `rows` are padding and have no output row.
+struct RowMap {
+    int64_t base;     // row of (slot, query 0, first head of the group)
+    int32_t group;    // G
+    int32_t n_q_heads;
+    int32_t rows;     // G * n_q real rows
+    __device__ __forceinline__ bool real(int h) const { return h < rows; }
+    __device__ __forceinline__ int64_t row(int h) const {
+        return base + (int64_t)(h / group) * n_q_heads + h % group;
+    }
+};
+
 // Merge of `count` consecutive partial records of one (slot, KV head),
 // starting at record rec0, by the last workgroup to finish among those that
 // wrote them.  The records were written by workgroups that may sit on other
@@ -283,7 +298,7 @@ __device__ __forceinline__ float4 ld_dev4(__amdgpu_buffer_rsrc_t r, int64_t off_
 // across chunks.  The result goes to the outputs (dest < 0) or, merged but
 // not normalised, to record `dest` (a cluster record).
 template <int D, int G>
-__device__ void merge_records(const SplitArgs& a, const SlotArg& sa, int64_t row0, int64_t rec0, int count,
+__device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMap& rm, int64_t rec0, int count,
                               int64_t dest) {
     constexpr int NV = G * D / 4;                           // float4 columns of o
     constexpr int TS = NV >= kThreads ? 1 : kThreads / NV;  // threads per column
@@ -323,10 +338,12 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, int64_t row
                               : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
-        // (m, l) of the chunk: wave w takes heads w and w + 4, one split per lane.
-        float mv[2], lv[2];
+        // (m, l) of the chunk: wave w takes record rows w, w + 4, w + 8, ...,
+        // one split per lane.
+        constexpr int HW = (G + 3) / 4;  // record rows per wave
+        float mv[HW], lv[HW];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
+        for (int hh = 0; hh < HW; ++hh) {
             const int h = wave + 4 * hh;
             mv[hh] = kNegInf;
             lv[hh] = 0.f;
@@ -337,7 +354,7 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, int64_t row
         }
         __syncthreads();  // the previous chunk is done with f_m / scale_old
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
+        for (int hh = 0; hh < HW; ++hh) {
             const int h = wave + 4 * hh;
             if (h >= G) continue;  // uniform over the wave
             const float mo = run_m[h];
@@ -402,8 +419,9 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, int64_t row
             float M = run_m[h], L = run_l[h];
             float4 O = acc[c];
             if (dest < 0) {
-                merge_acc_in(a, row0 + h, d0, D, M, L, O);
-                emit4(a, sa.to_acc, row0 + h, d0, D, M, L, O);
+                if (!rm.real(h)) continue;
+                merge_acc_in(a, rm.row(h), d0, D, M, L, O);
+                emit4(a, sa.to_acc, rm.row(h), d0, D, M, L, O);
             } else {
                 st_dev4(rs, (dest * (G * D) + 4 * v) * 4, O);
                 if (d0 == 0) {
@@ -434,7 +452,7 @@ __device__ __forceinline__ bool last_arrival(uint32_t* ticket, int expected, int
 // workgroup of the (slot, KV head) merges all records.
 template <int D, int G, int NS, int DP>
 __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& sa, int s, int g, int split,
-                                             int64_t row0, const float (*sm_m)[G], const float (*sm_l)[G],
+                                             const RowMap& rm, const float (*sm_m)[G], const float (*sm_l)[G],
                                              const float (*sm_o)[G][DP], int& sm_last) {
     const int tid = threadIdx.x;
     // Merge the NS streams: thread -> float4 column.  Result of this split in log2 units.
@@ -462,8 +480,10 @@ __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& 
             O.w = fmaf(ok.w, f, O.w);
         }
         if (single) {
-            merge_acc_in(a, row0 + h, d0, D, M, L, O);
-            emit4(a, sa.to_acc, row0 + h, d0, D, M, L, O);
+            if (rm.real(h)) {
+                merge_acc_in(a, rm.row(h), d0, D, M, L, O);
+                emit4(a, sa.to_acc, rm.row(h), d0, D, M, L, O);
+            }
         } else {
             st_dev4(rs, (rec * (G * D) + 4 * v) * 4, O);
             if (d0 == 0) {
@@ -483,7 +503,7 @@ __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& 
     if (ncl <= 1) {
         // the last workgroup of the (slot, KV head) merges every split
         if (!last_arrival(gticket, n_splits, sm_last)) return;
-        merge_records<D, G>(a, sa, row0, srec0, n_splits, -1);
+        merge_records<D, G>(a, sa, rm, srec0, n_splits, -1);
         return;
     }
     // two levels: the last of each cluster of splits merges the cluster into
@@ -494,11 +514,11 @@ __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& 
     const int cn = (n_splits - c0) < CH ? (n_splits - c0) : CH;
     const int64_t cidx = sa.cl_begin + (int64_t)g * ncl + cid;
     if (!last_arrival(a.ctickets + cidx, cn, sm_last)) return;
-    merge_records<D, G>(a, sa, row0, srec0 + c0, cn, a.crec_base + cidx);
+    merge_records<D, G>(a, sa, rm, srec0 + c0, cn, a.crec_base + cidx);
     wait_stores();
     __syncthreads();
     if (!last_arrival(gticket, ncl, sm_last)) return;
-    merge_records<D, G>(a, sa, row0, a.crec_base + sa.cl_begin + (int64_t)g * ncl, ncl, -1);
+    merge_records<D, G>(a, sa, rm, a.crec_base + sa.cl_begin + (int64_t)g * ncl, ncl, -1);
 }
 
 
@@ -777,7 +797,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     __syncthreads();
 
-    finish_split<D, G, NS, D + 16>(a, sa, s, g, split, row0, sm_m, sm_l, sm_o, sm_last);
+    const RowMap rm{row0, G, a.n_q_heads, G};
+    finish_split<D, G, NS, D + 16>(a, sa, s, g, split, rm, sm_m, sm_l, sm_o, sm_last);
 }
 
 // ---------------------------------------------------------------------------
@@ -855,9 +876,12 @@ __device__ __forceinline__ uint16_t scale_of(const Chunk<SB>& r, int j, int lq) 
     }
 }
 
-template <int D, int G, int KT, int VT, bool IND>
+template <int D, int RM, int KT, int VT, bool IND, bool MQ>
 __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a) {
-    static_assert(G >= 1 && G <= 16, "heads padded to one 16-row tile");
+    // RM: rows of a split record (8 or 16); the G * n_q real query rows of
+    // the (slot, KV head) are padded to RM and to the 16-row tile.
+    static_assert(RM == 8 || RM == 16, "record rows");
+    constexpr int G = RM;  // record rows, for the shared publish / merge code
     constexpr int EK = Row16<KT>::EPC, EV = Row16<VT>::EPC;
     constexpr int JK = D / EK / 4, JV = D / EV / 4;  // chunks per lane per row
     static_assert(JK >= 1 && JV >= 1 && JK * 4 * EK == D && JV * 4 * EV == D, "row chunking");
@@ -887,14 +911,23 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
     const int g = local - split * a.n_kv_heads;
     const int t0 = (int)(((int64_t)split * sa.n_tiles) / sa.n_splits);
     const int t1 = (int)(((int64_t)(split + 1) * sa.n_tiles) / sa.n_splits);
-    const int64_t row0 = (int64_t)(a.slot_base + s) * a.n_q_heads + g * G;
+    // Record row r = t * grp + hh is query row t of the slot, head g * grp + hh.
+    const int grp = a.group;
+    const int rows = grp * a.n_q;
+    const RowMap rm{(int64_t)(a.slot_base + s) * a.n_q * a.n_q_heads + (int64_t)g * grp, grp, a.n_q_heads, rows};
+    const bool real_row = li < rows;
+    // Position of this lane's query row (multi-query): it sees cells whose
+    // position is at most qpos; padding rows see nothing.
+    int64_t qpos = INT64_MIN;
+    if constexpr (MQ)
+        if (real_row) qpos = a.q_pos[(int64_t)(a.slot_base + s) * a.n_q + li / grp];
 
-    // B operand of S: q rows (zero rows for heads >= G) in the permuted order
-    // of the K chunks this lane group reads.  Loads are unconditional (row
-    // clamped) so that they all leave before the first wait.
+    // B operand of S: q rows (zero rows past the real ones) in the permuted
+    // order of the K chunks this lane group reads.  Loads are unconditional
+    // (row clamped) so that they all leave before the first wait.
     h8 qb[NKB];
     {
-        const float* qr = a.q + (row0 + (li < G ? li : 0)) * D;
+        const float* qr = a.q + rm.row(real_row ? li : 0) * D;
 #pragma unroll
         for (int j = 0; j < JK; ++j) {
 #pragma unroll
@@ -908,7 +941,7 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
                     x[e + 1] = v.y;
                 }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) qb[j * (EK / 8) + sub][e] = li < G ? (_Float16)x[e] : (_Float16)0.0f;
+                for (int e = 0; e < 8; ++e) qb[j * (EK / 8) + sub][e] = real_row ? (_Float16)x[e] : (_Float16)0.0f;
             }
         }
     }
@@ -982,7 +1015,19 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
         }
     };
 
+    // Multi-query: positions of a step's cells come from cell_pos (loaded a
+    // step ahead, left untouched until used) or are cell index + pos_offset.
+    auto fetch_pos = [&](const int64_t (&c)[2], int32_t (&raw)[2]) {
+        if constexpr (MQ) {
+            if (a.cell_pos) {
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) raw[mb] = a.cell_pos[c[mb]];
+            }
+        }
+    };
+
     int32_t raw_next[2] = {0, 0};
+    int32_t praw[2] = {0, 0};
     int64_t cell[2] = {0, 0};
     bool valid[2] = {false, false};
     if (n_steps > 0) {
@@ -991,9 +1036,18 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
             resolve(base0, mb, fetch(base0, mb), cell[mb], valid[mb]);
             raw_next[mb] = fetch(base0 + kTile, mb);
         }
+        fetch_pos(cell, praw);
         load_k(cell);
         __builtin_amdgcn_sched_barrier(0);  // same issue order as in the loop: K, then V
         load_v(cell);
+        if constexpr (MQ) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                int32_t t;
+                asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"(praw[mb]));
+                praw[mb] = t;
+            }
+        }
         if constexpr (IND) {
             // Land the step-1 entries here, behind an opaque copy: entering the
             // loop with a load still pending on them would make the compiler
@@ -1017,6 +1071,24 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
         for (int mb = 0; mb < 2; ++mb) {
             raw2[mb] = fetch(base + 2 * kTile, mb);
             resolve(base + kTile, mb, raw_next[mb], ncell[mb], nvalid[mb]);
+        }
+        int32_t npraw[2] = {0, 0};
+        fetch_pos(ncell, npraw);
+        // Multi-query mask: bit e of vis[mb] = cell 4 * lq + e of block mb is
+        // visible to this lane's query row.
+        uint32_t vis[2] = {0xFu, 0xFu};
+        if constexpr (MQ) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const int64_t mine = a.cell_pos ? (int64_t)praw[mb] : cell[mb] + a.pos_offset;
+                uint32_t bits = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int64_t p = __shfl(mine, 4 * lq + e);
+                    bits |= (p <= qpos ? 1u : 0u) << e;
+                }
+                vis[mb] = bits;
+            }
         }
 
         // S^T for the two blocks.
@@ -1048,8 +1120,8 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int c = 4 * lq + e;
-            sc[e] = ((vm0 >> c) & 1) ? sacc[0][e] * a.scale_log2 : kNegInf;
-            sc[4 + e] = ((vm1 >> c) & 1) ? sacc[1][e] * a.scale_log2 : kNegInf;
+            sc[e] = (((vm0 >> c) & 1) && ((vis[0] >> e) & 1)) ? sacc[0][e] * a.scale_log2 : kNegInf;
+            sc[4 + e] = (((vm1 >> c) & 1) && ((vis[1] >> e) & 1)) ? sacc[1][e] * a.scale_log2 : kNegInf;
         }
         float mt = sc[0];
 #pragma unroll
@@ -1142,6 +1214,7 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             raw_next[mb] = raw2[mb];
+            praw[mb] = npraw[mb];
             cell[mb] = ncell[mb];
             valid[mb] = nvalid[mb];
         }
@@ -1164,53 +1237,62 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
             if (h < G) sm_o[wave][h][16 * nb + li] = oacc[nb][e] * kMPOffInv;
         }
     __syncthreads();
-    finish_split<D, G, 4, D>(a, sa, s, g, split, row0, sm_m, sm_l, sm_o, sm_last);
-}
-
-// Groups of up to 5 query heads per KV head run on the VALU kernel; wider
-// groups (with head_dim 128 or 256) on the matrix-core kernel.
-template <int D, int G>
-constexpr bool use_mfma() {
-    return G >= 6 && D >= 128;
+    finish_split<D, G, 4, D>(a, sa, s, g, split, rm, sm_m, sm_l, sm_o, sm_last);
 }
 
 template <int D, int G, int KT, int VT>
-int launch_one(const SplitArgs& a, void* stream) {
-    if constexpr (use_mfma<D, G>()) {
-        if (a.plan)
-            hipLaunchKernelGGL((split_mfma_kernel<D, G, KT, VT, true>), dim3(a.n_workgroups), dim3(kThreads), 0,
-                               (hipStream_t)stream, a);
-        else
-            hipLaunchKernelGGL((split_mfma_kernel<D, G, KT, VT, false>), dim3(a.n_workgroups), dim3(kThreads), 0,
-                               (hipStream_t)stream, a);
-    } else
-        hipLaunchKernelGGL((split_kernel<D, G, KT, VT>), dim3(a.n_workgroups), dim3(kThreads), 0,
+int launch_valu(const SplitArgs& a, void* stream) {
+    hipLaunchKernelGGL((split_kernel<D, G, KT, VT>), dim3(a.n_workgroups), dim3(kThreads), 0, (hipStream_t)stream, a);
+    return (int)hipGetLastError();
+}
+
+template <int D, int RM, int KT, int VT, bool MQ>
+int launch_mfma(const SplitArgs& a, void* stream) {
+    if (a.plan)
+        hipLaunchKernelGGL((split_mfma_kernel<D, RM, KT, VT, true, MQ>), dim3(a.n_workgroups), dim3(kThreads), 0,
+                           (hipStream_t)stream, a);
+    else
+        hipLaunchKernelGGL((split_mfma_kernel<D, RM, KT, VT, false, MQ>), dim3(a.n_workgroups), dim3(kThreads), 0,
                            (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
 
+// The instance for (G, n_q) at one head_dim and pair of storage kinds: the
+// VALU kernel for one query row and G <= 5 (any G for head_dim 64), else the
+// matrix-core kernel with 8- or 16-row records (G * n_q <= 16).
 template <int D, int KT, int VT>
-SplitLaunchFn pick_g(int g) {
-    switch (g) {
-        case 1: return &launch_one<D, 1, KT, VT>;
-        case 2: return &launch_one<D, 2, KT, VT>;
-        case 3: return &launch_one<D, 3, KT, VT>;
-        case 4: return &launch_one<D, 4, KT, VT>;
-        case 5: return &launch_one<D, 5, KT, VT>;
-        case 6: return &launch_one<D, 6, KT, VT>;
-        case 7: return &launch_one<D, 7, KT, VT>;
-        case 8: return &launch_one<D, 8, KT, VT>;
-        default: return nullptr;
+SplitLaunchFn pick_g(int g, int n_q) {
+    if (g < 1 || n_q < 1) return nullptr;
+    if (!uses_matrix_cores(g, n_q, D)) {
+        if (n_q != 1) return nullptr;
+        switch (g) {
+            case 1: return &launch_valu<D, 1, KT, VT>;
+            case 2: return &launch_valu<D, 2, KT, VT>;
+            case 3: return &launch_valu<D, 3, KT, VT>;
+            case 4: return &launch_valu<D, 4, KT, VT>;
+            case 5: return &launch_valu<D, 5, KT, VT>;
+            case 6: return &launch_valu<D, 6, KT, VT>;
+            case 7: return &launch_valu<D, 7, KT, VT>;
+            case 8: return &launch_valu<D, 8, KT, VT>;
+            default: return nullptr;
+        }
     }
+    if constexpr (D >= 128) {
+        if (g * n_q > 16) return nullptr;
+        const bool wide = record_rows(g, n_q, D) == 16;
+        if (n_q == 1) return wide ? &launch_mfma<D, 16, KT, VT, false> : &launch_mfma<D, 8, KT, VT, false>;
+        return wide ? &launch_mfma<D, 16, KT, VT, true> : &launch_mfma<D, 8, KT, VT, true>;
+    }
+    return nullptr;
 }
 
-// Every (head_dim, group) instance of one pair of storage kinds.
+// Every (head_dim, group, n_q) instance of one pair of storage kinds.
 template <int KT, int VT>
-SplitLaunchFn pick_dg(int head_dim, int g) {
+SplitLaunchFn pick_dg(int head_dim, int g, int n_q) {
     switch (head_dim) {
-        case 64: return pick_g<64, KT, VT>(g);
-        case 128: return pick_g<128, KT, VT>(g);
-        case 256: return pick_g<256, KT, VT>(g);
+        case 64: return pick_g<64, KT, VT>(g, n_q);
+        case 128: return pick_g<128, KT, VT>(g, n_q);
+        case 256: return pick_g<256, KT, VT>(g, n_q);
         default: return nullptr;
     }
 }

@@ -42,7 +42,7 @@ class Problem(ctypes.Structure):
         ("cell_begin", _p), ("n_occupied", _p), ("cells", _p), ("cells_off", _p),
         ("tail_begin", _p), ("n_tail", _p),
         ("tail_capacity_cells", _i64), ("tail_chunk_cells", _i64),
-        ("tail_ring_depth", _i32), ("reserved", _i32),
+        ("tail_ring_depth", _i32), ("n_queries", _i32),
     ]
 
 
@@ -53,6 +53,7 @@ class IO(ctypes.Structure):
         ("plan_cells", _p),
         ("k_tail", _p), ("v_tail", _p), ("k_tail_scales", _p), ("v_tail_scales", _p),
         ("out", _p), ("lse", _p), ("part_m", _p), ("part_l", _p), ("part_o", _p),
+        ("q_pos", _p), ("cell_pos", _p),
     ]
 
 
@@ -64,6 +65,7 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [
         ("n_slots", _i32), ("group", _i32), ("n_workgroups", _i32), ("tiles_per_split", _i32),
         ("n_tiles", _i64), ("n_entries", _i64), ("n_tail_chunks", _i64), ("workspace_bytes", _i64),
+        ("n_queries", _i32), ("matrix_cores", _i32),
     ]
 
 
@@ -178,10 +180,11 @@ class Plan:
 
 def plan(n_q_heads, n_kv_heads, head_dim, n_slots, capacity_cells, *, k_type=F16, v_type=F16, scale=None,
          n_occupied=None, cell_begin=None, cells=None, n_tail=None, tail_begin=None, tail_capacity_cells=0,
-         tail_chunk_cells=0, tail_ring_depth=0, tiles_per_split=0, n_cu=0):
+         tail_chunk_cells=0, tail_ring_depth=0, tiles_per_split=0, n_cu=0, n_queries=1):
     """Build a plan.  ``cells`` is a list of per-slot raw cell arrays
     (indirect mode); otherwise ``n_occupied`` (and optional ``cell_begin``)
-    give contiguous ranges.  ``n_cu=0`` asks the current HIP device."""
+    give contiguous ranges.  ``n_queries`` query rows per slot.  ``n_cu=0``
+    asks the current HIP device."""
     keep = []
 
     def arr64(x):
@@ -215,6 +218,7 @@ def plan(n_q_heads, n_kv_heads, head_dim, n_slots, capacity_cells, *, k_type=F16
     p.tail_capacity_cells = tail_capacity_cells
     p.tail_chunk_cells = tail_chunk_cells
     p.tail_ring_depth = tail_ring_depth
+    p.n_queries = n_queries
     h = _p()
     ws = ctypes.c_size_t()
     _check(lib.kvdec_plan(ctypes.byref(p), n_cu, ctypes.byref(h), ctypes.byref(ws)), "kvdec_plan")
@@ -229,9 +233,11 @@ def workspace(plan_, device="cuda"):
 
 def attend(plan_, q, k, v, ws, *, out=None, lse=None, part=None, k_scales=None, v_scales=None, plan_cells=None,
            k_cell_stride=0, k_head_stride=0, v_cell_stride=0, v_head_stride=0, k_tail=None, v_tail=None,
-           k_tail_scales=None, v_tail_scales=None, stream=None, copy_stream=None):
+           k_tail_scales=None, v_tail_scales=None, q_pos=None, cell_pos=None, stream=None, copy_stream=None):
     """Enqueue one evaluation (see kvdec_attend in include/kvdec.h).
-    ``part`` is an optional (m, l, o) tuple of output tensors."""
+    ``part`` is an optional (m, l, o) tuple of output tensors; ``q_pos``
+    (int32 [slots][n_queries]) and ``cell_pos`` (int32 [capacity]) are the
+    positions of the multi-query mask."""
     io = IO()
     io.q, io.k, io.v = _ptr(q), _ptr(k), _ptr(v)
     io.k_scales, io.v_scales = _ptr(k_scales), _ptr(v_scales)
@@ -243,6 +249,7 @@ def attend(plan_, q, k, v, ws, *, out=None, lse=None, part=None, k_scales=None, 
     io.out, io.lse = _ptr(out), _ptr(lse)
     if part is not None:
         io.part_m, io.part_l, io.part_o = (_ptr(t) for t in part)
+    io.q_pos, io.cell_pos = _ptr(q_pos), _ptr(cell_pos)
     nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else int(ws[1])
     wptr = _ptr(ws) if hasattr(ws, "numel") else int(ws[0])
     st = _stream_handle(stream)

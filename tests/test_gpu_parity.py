@@ -38,7 +38,8 @@ def test_ragged_lengths_multi_slot(K):
 
 
 @pytest.mark.parametrize("d,g", [(64, 1), (64, 4), (64, 8), (128, 1), (128, 2), (128, 3), (128, 5), (128, 6),
-                                 (128, 7), (128, 8), (256, 2), (256, 4), (256, 5), (256, 6), (256, 8)])
+                                 (128, 7), (128, 8), (256, 2), (256, 4), (256, 5), (256, 6), (256, 8),
+                                 (128, 12), (128, 16), (256, 9), (256, 16)])
 def test_group_sizes_and_head_dims(K, d, g):
     c = Case(20 + d + g, 2 * g, 2, d, occupied=[700, 1500])
     check(*c.run(K), *c.oracle())

@@ -29,7 +29,7 @@ def test_exports_every_declared_function():
     for name in names:
         assert hasattr(K.lib, name), name
     assert set(names) == set(K.EXPORTED)
-    assert K.version() == 10000
+    assert K.version() == 10100
 
 
 def test_probe_library_exports_and_rejects_bad_arguments():
@@ -161,7 +161,8 @@ def test_plan_errors():
     assert _status(lambda: K.plan(32, 8, 128, 1, 100, n_occupied=[10], cell_begin=[95], n_cu=256)) == K.E_RANGE
     assert _status(lambda: K.plan(32, 8, 128, 1, 100, cells=[[3, 100]], n_cu=256)) == K.E_RANGE
     assert _status(lambda: K.plan(32, 8, 128, 1, 100, cells=[[3, -2]], n_cu=256)) == K.E_RANGE
-    assert _status(lambda: K.plan(32, 2, 128, 1, 100, **base)) == K.E_UNSUPPORTED      # G = 16
+    assert _status(lambda: K.plan(32, 2, 64, 1, 100, **base)) == K.E_UNSUPPORTED       # G = 16, head_dim 64
+    K.plan(32, 2, 128, 1, 100, **base).close()                                           # G = 16 on matrix cores
     assert _status(lambda: K.plan(32, 8, 128, 1, 100, k_type=K.Q8_B32, v_type=K.F16, **base)) == K.E_UNSUPPORTED
     # V stored more finely than K has no kernel; K more finely than V does
     assert _status(lambda: K.plan(32, 8, 128, 1, 100, k_type=K.Q4_B32, v_type=K.Q8_B32, **base)) == K.E_UNSUPPORTED
@@ -220,3 +221,31 @@ def test_merge_validation():
     # zero rows: nothing to do, nothing launched
     assert f(1, arr, 0, 128, FAKE, None, None, None, None, None) == K.OK
     del ctypes
+
+
+def test_multi_query_plans():
+    """Several query rows per slot: the matrix-core kernel serves G * n_q <= 16
+    rows for head_dim 128 / 256; everything else is refused at plan time."""
+    base = dict(n_occupied=[1000], n_cu=256)
+    info = K.plan(32, 8, 128, 1, 1000, n_queries=4, **base).info()
+    assert info["n_queries"] == 4 and info["matrix_cores"] == 1
+    one = K.plan(32, 8, 128, 1, 1000, **base).info()
+    assert one["n_queries"] == 1 and one["matrix_cores"] == 0
+    assert K.plan(24, 4, 256, 1, 1000, **base).info()["matrix_cores"] == 1   # G = 6
+    assert _status(lambda: K.plan(32, 8, 128, 1, 1000, n_queries=9, **base)) == K.E_INVALID
+    assert _status(lambda: K.plan(32, 8, 128, 1, 1000, n_queries=-1, **base)) == K.E_INVALID
+    assert _status(lambda: K.plan(40, 8, 128, 1, 1000, n_queries=4, **base)) == K.E_UNSUPPORTED  # 20 rows
+    assert _status(lambda: K.plan(32, 8, 64, 1, 1000, n_queries=2, **base)) == K.E_UNSUPPORTED   # head_dim 64
+    for g, nq in ((1, 8), (2, 8), (4, 4), (8, 2), (16, 1), (3, 5)):
+        p = K.plan(8 * g, 8, 256, 2, 1000, n_queries=nq, n_occupied=[1000, 10], n_cu=256)
+        assert p.info()["n_queries"] == nq
+        p.close()
+
+
+def test_multi_query_attend_needs_q_pos():
+    p = K.plan(32, 8, 128, 1, 1000, n_queries=2, n_occupied=[1000], n_cu=256)
+    ws = (FAKE, p.workspace_bytes)
+    assert _status(lambda: K.attend(p, FAKE, FAKE, FAKE, ws, out=FAKE, stream=0)) == K.E_INVALID
+    assert "q_pos" in K.lib.kvdec_last_error().decode()
+    assert _status(lambda: K.attend(p, FAKE, FAKE, FAKE, ws, out=FAKE, q_pos=FAKE, cell_pos=FAKE + 2,
+                                    stream=0)) == K.E_INVALID
