@@ -19,6 +19,8 @@ Workloads (synthetic N(0, 1) data of the named model's attention shape):
   gqa6-q8k-q4v      the same with int8 K and 4-bit V
   rolling-ctx40960  qwen3-8b shape at ctx 40960: newest 14000 cells resident,
                     oldest 26960 streamed from pinned host memory per layer
+                    (-prefetch: cross-layer prefetch through two workspaces;
+                    -zerocopy: kernels read the pinned tail in place)
   qwen3-8b-ctx16k-verify4
                     the qwen3-8b-ctx16k caches with 4 query rows per step
                     (speculative verification, causal positional mask)
@@ -281,14 +283,22 @@ class RollingWindow(ContiguousModel):
     resident and the oldest 26960 stream from pinned host memory through the
     workspace ring (copy stream + events), merged by log-sum-exp."""
 
-    def __init__(self):
-        super().__init__("rolling-ctx40960", 36, 32, 8, 128, 40960, 40960)
-        self.window, self.tail = 14000, 26960
+    chunk = 0  # tail cells per chunk (bench.py --tail-chunk); 0: 8192 staged, the whole tail otherwise
+
+    def __init__(self, name="rolling-ctx40960", mode="staged"):
+        super().__init__(name, 36, 32, 8, 128, 40960, 40960)
+        self.window, self.tail, self.mode = 14000, 26960, mode
+        if not self.chunk:
+            self.chunk = 8192 if mode == "staged" else -(-self.tail // 128) * 128
 
     def config(self):
         c = super().config()
-        c.update({"cells_resident_window": self.window, "cells_host_tail": self.tail, "tail_chunk_cells": 2048,
-                  "ring_depth": 4})
+        c.update({"cells_resident_window": self.window, "cells_host_tail": self.tail, "tail_chunk_cells": self.chunk,
+                  "ring_depth": 4, "tail_mode": {
+                      "staged": "copies into a workspace ring; each call's copies wait for earlier work",
+                      "prefetch": "copies into a ring; layers alternate two workspaces and each call's copies "
+                                  "wait only for the call two layers back (cross-layer prefetch)",
+                      "zerocopy": "chunk kernels read the pinned host tail in place"}[self.mode]})
         return c
 
     def algorithmic_bytes_per_launch(self):
@@ -317,13 +327,38 @@ class RollingWindow(ContiguousModel):
             self.lse.append(torch.empty(1, self.hq, device="cuda"))
         self.plan = K.plan(self.hq, self.hkv, self.d, 1, self.capacity, n_occupied=[self.window],
                            cell_begin=[self.tail], n_tail=[self.tail], tail_capacity_cells=self.tail,
-                           tail_chunk_cells=2048, tail_ring_depth=4)
-        self.ws = K.workspace(self.plan)
+                           tail_chunk_cells=self.chunk, tail_ring_depth=4, tail_zero_copy=self.mode == "zerocopy")
+        self.ws = [K.workspace(self.plan) for _ in range(2 if self.mode == "prefetch" else 1)]
+        self.ev = [torch.cuda.Event() for _ in range(2)]
         self.copy_stream = torch.cuda.Stream()
+        self.window_plan = K.plan(self.hq, self.hkv, self.d, 1, self.capacity, n_occupied=[self.window],
+                                  cell_begin=[self.tail])
+        self.window_ws = K.workspace(self.window_plan)
 
     def launch(self, K, layer):
-        K.attend(self.plan, self.q[layer], self.k[layer], self.v[layer], self.ws, out=self.out[layer],
-                 lse=self.lse[layer], k_tail=self.hk[layer], v_tail=self.hv[layer], copy_stream=self.copy_stream)
+        pre = self.mode == "prefetch"
+        K.attend(self.plan, self.q[layer], self.k[layer], self.v[layer], self.ws[layer % 2 if pre else 0],
+                 out=self.out[layer], lse=self.lse[layer], k_tail=self.hk[layer], v_tail=self.hv[layer],
+                 copy_stream=self.copy_stream, copy_after=self.ev[layer % 2] if pre else None)
+        if pre:
+            self.ev[layer % 2].record()
+
+    def resident_only_us(self, K, torch, reps=5):
+        """Step time of the resident windows alone (no tail): the first term
+        of t = resident + tail bytes / link rate."""
+        def step():
+            for layer in range(self.layers):
+                K.attend(self.window_plan, self.q[layer], self.k[layer], self.v[layer], self.window_ws,
+                         out=self.out[layer], lse=self.lse[layer])
+        step()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            step()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
 
 
 class ContiguousModelOneLaunch(ContiguousModel):
@@ -373,6 +408,8 @@ WORKLOADS = {
     "gqa6-q4": lambda: Gqa6Quant("gqa6-q4", 2),
     "gqa6-q8k-q4v": lambda: Gqa6Quant("gqa6-q8k-q4v", 1, v_kind=2),
     "rolling-ctx40960": lambda: RollingWindow(),
+    "rolling-ctx40960-prefetch": lambda: RollingWindow("rolling-ctx40960-prefetch", "prefetch"),
+    "rolling-ctx40960-zerocopy": lambda: RollingWindow("rolling-ctx40960-zerocopy", "zerocopy"),
     "qwen3-8b-ctx16k-verify4": lambda: ContiguousModel("qwen3-8b-ctx16k-verify4", 36, 32, 8, 128, 16384, 13100,
                                                         n_q=4),
     "qwen3-8b-ctx16k-1launch": lambda: ContiguousModelOneLaunch("qwen3-8b-ctx16k-1launch", 36, 32, 8, 128, 16384,
@@ -422,6 +459,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-ceiling", action="store_true", help="skip the streaming-read ceiling (profiling runs)")
+    ap.add_argument("--tail-chunk", type=int, default=0,
+                    help="host-tail cells per chunk (rolling workloads; 0: 8192 staged, whole tail otherwise)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -442,6 +481,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    RollingWindow.chunk = args.tail_chunk
     wl = WORKLOADS[args.workload]()
     log(f"[bench] workload {wl.name}: generating inputs on the device")
     wl.setup(K, torch, 1001)
@@ -570,8 +610,15 @@ def main():
     }
     if hasattr(wl, "pcie_bytes_per_launch"):
         pb = wl.pcie_bytes_per_launch() * launches_per_step
+        link = measure_h2d(torch)
+        resident_us = wl.resident_only_us(K, torch)
+        model_us = resident_us + pb / (link * 1e9) * 1e6
         res["pcie"] = {"h2d_bytes_per_step": pb, "h2d_gbs_effective": round(pb / (ms_per_step * 1e-3) / 1e9, 2),
-                       "link_gbs_measured": measure_h2d(torch)}
+                       "link_gbs_measured": link, "frac_of_link": round(pb / (ms_per_step * 1e-3) / 1e9 / link, 4),
+                       "resident_only_us_per_step": round(resident_us, 1),
+                       "model_us_per_step": round(model_us, 1),
+                       "model": "t = resident_only + tail_bytes / link rate",
+                       "residual_vs_model": round(ms_per_step * 1e3 / model_us - 1, 4)}
     print(json.dumps(res), flush=True)
 
 

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_VERSION 10100 /* 1.1.0: n_queries, q_pos, cell_pos */
+#define KVDEC_VERSION 10200 /* 1.2.0: tail_zero_copy, copy_after */
 
 /* Status codes. */
 #define KVDEC_OK 0
@@ -115,8 +115,14 @@ extern "C" {
  *   [tail cell][kv head][row], scales likewise); tail_begin may be NULL (all
  *   zero) and tail_capacity_cells bounds the tail arrays.  The tail is copied
  *   to the device in chunks of tail_chunk_cells (a multiple of 128; 0 picks
- *   2048) through a ring of tail_ring_depth staging slots (>= 2; 0 picks 4)
- *   inside the workspace.
+ *   8192) through a ring of tail_ring_depth staging slots (2..16; 0 picks 4;
+ *   never more than the call's chunks) inside the workspace.  With tail_zero_copy = 1 nothing is staged: the
+ *   chunk kernels read the pinned host arrays in place over the link.  (The
+ *   "KVARN KV Performance optimizations" notes on pinned-host projector
+ *   weights found such in-place reads slower than one staging copy because
+ *   a GEMM re-reads its tiles; attention reads every tail byte once.)  The
+ *   arrays must then be device-mapped pinned memory (hipHostMalloc), and
+ *   the ring takes no workspace.
  *
  * tiles_per_split: 128-cell tiles per workgroup; 0 lets the planner choose
  *   so that the launch fills the device.  Only the floating-point summation
@@ -151,7 +157,9 @@ typedef struct kvdec_problem {
     int64_t tail_capacity_cells;
     int64_t tail_chunk_cells;
     int32_t tail_ring_depth;
-    int32_t n_queries; /* query rows per slot, 1..8; 0 means 1 */
+    int32_t n_queries;      /* query rows per slot, 1..8; 0 means 1 */
+    int32_t tail_zero_copy; /* 1: kernels read the host tail in place */
+    int32_t reserved;       /* 0 */
 } kvdec_problem;
 
 /* Opaque, immutable plan. */
@@ -189,6 +197,13 @@ typedef struct kvdec_plan kvdec_plan_t;
  * cell_pos: device int32 [capacity_cells] positions of the device cells, or
  *   NULL: a device cell's position is its cell index.  A host-tail cell's
  *   position is its index in the tail arrays.  Used with n_queries > 1 only.
+ * copy_after: a hipEvent_t or NULL.  The tail copies of a call may not
+ *   overwrite staging slots that earlier calls on the same workspace still
+ *   read; by default they wait for all work enqueued on `stream` before the
+ *   call.  With copy_after they wait for that event instead, so a caller
+ *   that alternates two workspaces between consecutive layers can record an
+ *   event after call l and pass it to call l + 2: the copies of layer l + 1
+ *   then overlap layer l's kernels (cross-layer tail prefetch).
  */
 typedef struct kvdec_io {
     const float* q;
@@ -212,6 +227,7 @@ typedef struct kvdec_io {
     float* part_o;
     const int32_t* q_pos;
     const int32_t* cell_pos;
+    void* copy_after;
 } kvdec_io;
 
 /* One partial result set for kvdec_merge: rows are (slot, query head) pairs,

@@ -237,9 +237,12 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
     // (acc0 <-> acc1 ping-pong) and, on the slot's last chunk, writing the
     // outputs.  Ring reuse is ordered by events: the copy into a ring slot
     // waits until the kernel that read the slot's previous chunk has finished.
+    // With tail_zero_copy the chunk kernels read the host arrays in place and
+    // nothing is copied.
     hipStream_t cs = static_cast<hipStream_t>(copy_stream ? copy_stream : stream);
     hipStream_t ks = static_cast<hipStream_t>(stream);
-    const int depth = p.ring_depth;
+    const bool zc = p.tail_zero_copy;
+    const int depth = zc ? 0 : p.ring_depth;
     hipEvent_t ev_start = nullptr, ev_landed[16] = {}, ev_free[16] = {};
     auto destroy = [&]() {
         if (ev_start) (void)hipEventDestroy(ev_start);
@@ -248,22 +251,50 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
             if (ev_free[i]) (void)hipEventDestroy(ev_free[i]);
         }
     };
-    hipError_t e = hipEventCreateWithFlags(&ev_start, hipEventDisableTiming);
-    for (int i = 0; i < depth && e == hipSuccess; ++i) {
-        e = hipEventCreateWithFlags(&ev_landed[i], hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_free[i], hipEventDisableTiming);
-    }
-    if (e != hipSuccess) {
-        destroy();
-        return device_fail(e, "hipEventCreate");
-    }
-    // Copies start only after all work already on `stream` (which may still
-    // read the ring through an earlier call).
-    e = hipEventRecord(ev_start, ks);
-    if (e == hipSuccess && cs != ks) e = hipStreamWaitEvent(cs, ev_start, 0);
-    if (e != hipSuccess) {
-        destroy();
-        return device_fail(e, "stream ordering");
+    const uint8_t* hk = static_cast<const uint8_t*>(io->k_tail);
+    const uint8_t* hv = static_cast<const uint8_t*>(io->v_tail);
+    const uint8_t* hks = static_cast<const uint8_t*>(io->k_tail_scales);
+    const uint8_t* hvs = static_cast<const uint8_t*>(io->v_tail_scales);
+    hipError_t e = hipSuccess;
+    if (zc) {
+        if (!aligned(hk, kal) || !aligned(hv, val) || !aligned(hks, sal) || !aligned(hvs, sal))
+            return fail(KVDEC_E_INVALID, "tail arrays read in place must be aligned like device K / V / scales");
+        // device addresses of the pinned host arrays
+        auto mapped = [](const uint8_t*& ptr) -> bool {
+            if (!ptr) return true;
+            hipPointerAttribute_t at;
+            if (hipPointerGetAttributes(&at, ptr) != hipSuccess || !at.devicePointer) {
+                (void)hipGetLastError();
+                return false;
+            }
+            ptr = static_cast<const uint8_t*>(at.devicePointer);
+            return true;
+        };
+        if (!mapped(hk) || !mapped(hv) || !mapped(hks) || !mapped(hvs))
+            return fail(KVDEC_E_INVALID, "tail_zero_copy needs device-mapped pinned host tail arrays");
+    } else {
+        e = hipEventCreateWithFlags(&ev_start, hipEventDisableTiming);
+        for (int i = 0; i < depth && e == hipSuccess; ++i) {
+            e = hipEventCreateWithFlags(&ev_landed[i], hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_free[i], hipEventDisableTiming);
+        }
+        if (e != hipSuccess) {
+            destroy();
+            return device_fail(e, "hipEventCreate");
+        }
+        // Copies start only after the work that may still read the ring:
+        // everything already on `stream` (an earlier call on this workspace),
+        // or the caller's copy_after event.
+        if (io->copy_after) {
+            if (cs != ks) e = hipStreamWaitEvent(cs, static_cast<hipEvent_t>(io->copy_after), 0);
+        } else {
+            e = hipEventRecord(ev_start, ks);
+            if (e == hipSuccess && cs != ks) e = hipStreamWaitEvent(cs, ev_start, 0);
+        }
+        if (e != hipSuccess) {
+            destroy();
+            return device_fail(e, "stream ordering");
+        }
     }
     int le = kvdec::launch_split(D, p.group, p.n_q, p.k_type, p.v_type, a, stream);
     if (le != hipSuccess) {
@@ -274,38 +305,46 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
     const int64_t krow_b = kvdec::row_bytes(p.k_type, D) * p.n_kv_heads;
     const int64_t vrow_b = kvdec::row_bytes(p.v_type, D) * p.n_kv_heads;
     const int64_t srow_b = (int64_t)(D / kvdec::kBlock) * 2 * p.n_kv_heads;
-    const uint8_t* hk = static_cast<const uint8_t*>(io->k_tail);
-    const uint8_t* hv = static_cast<const uint8_t*>(io->v_tail);
-    const uint8_t* hks = static_cast<const uint8_t*>(io->k_tail_scales);
-    const uint8_t* hvs = static_cast<const uint8_t*>(io->v_tail_scales);
     int64_t chunk_no = 0;
     for (int s = 0; s < p.n_slots && e == hipSuccess; ++s) {
         const int64_t n = p.tail_n[s];
         const int64_t n_chunks = (n + p.chunk_cells - 1) / p.chunk_cells;
         for (int64_t c = 0; c < n_chunks; ++c, ++chunk_no) {
-            const int r = (int)(chunk_no % depth);
-            uint8_t* slot = ws + p.off_ring + (size_t)r * p.ring_slot_bytes;
             const int64_t c0 = p.tail_begin[s] + c * p.chunk_cells;
             const int64_t nc = std::min<int64_t>(p.chunk_cells, n - c * p.chunk_cells);
-            if (chunk_no >= depth) e = hipStreamWaitEvent(cs, ev_free[r], 0);
-            if (e == hipSuccess)
-                e = hipMemcpyAsync(slot + p.ring_k, hk + c0 * krow_b, nc * krow_b, hipMemcpyHostToDevice, cs);
-            if (e == hipSuccess)
-                e = hipMemcpyAsync(slot + p.ring_v, hv + c0 * vrow_b, nc * vrow_b, hipMemcpyHostToDevice, cs);
-            if (e == hipSuccess && kvdec::is_scaled(p.k_type))
-                e = hipMemcpyAsync(slot + p.ring_ks, hks + c0 * srow_b, nc * srow_b, hipMemcpyHostToDevice, cs);
-            if (e == hipSuccess && kvdec::is_scaled(p.v_type))
-                e = hipMemcpyAsync(slot + p.ring_vs, hvs + c0 * srow_b, nc * srow_b, hipMemcpyHostToDevice, cs);
-            if (e == hipSuccess) e = hipEventRecord(ev_landed[r], cs);
-            if (e == hipSuccess && cs != ks) e = hipStreamWaitEvent(ks, ev_landed[r], 0);
-            if (e != hipSuccess) break;
+            const int r = zc ? 0 : (int)(chunk_no % depth);
+            const uint8_t *ck, *cv, *cks, *cvs;  // the chunk's rows on the device
+            if (zc) {
+                ck = hk + c0 * krow_b;
+                cv = hv + c0 * vrow_b;
+                cks = hks ? hks + c0 * srow_b : nullptr;
+                cvs = hvs ? hvs + c0 * srow_b : nullptr;
+            } else {
+                uint8_t* slot = ws + p.off_ring + (size_t)r * p.ring_slot_bytes;
+                if (chunk_no >= depth) e = hipStreamWaitEvent(cs, ev_free[r], 0);
+                if (e == hipSuccess)
+                    e = hipMemcpyAsync(slot + p.ring_k, hk + c0 * krow_b, nc * krow_b, hipMemcpyHostToDevice, cs);
+                if (e == hipSuccess)
+                    e = hipMemcpyAsync(slot + p.ring_v, hv + c0 * vrow_b, nc * vrow_b, hipMemcpyHostToDevice, cs);
+                if (e == hipSuccess && kvdec::is_scaled(p.k_type))
+                    e = hipMemcpyAsync(slot + p.ring_ks, hks + c0 * srow_b, nc * srow_b, hipMemcpyHostToDevice, cs);
+                if (e == hipSuccess && kvdec::is_scaled(p.v_type))
+                    e = hipMemcpyAsync(slot + p.ring_vs, hvs + c0 * srow_b, nc * srow_b, hipMemcpyHostToDevice, cs);
+                if (e == hipSuccess) e = hipEventRecord(ev_landed[r], cs);
+                if (e == hipSuccess && cs != ks) e = hipStreamWaitEvent(ks, ev_landed[r], 0);
+                if (e != hipSuccess) break;
+                ck = slot + p.ring_k;
+                cv = slot + p.ring_v;
+                cks = slot + p.ring_ks;
+                cvs = slot + p.ring_vs;
+            }
 
             kvdec::SplitArgs t;
             common_args(p, *io, t);
-            t.k = slot + p.ring_k;
-            t.v = slot + p.ring_v;
-            t.ks = reinterpret_cast<const uint16_t*>(slot + p.ring_ks);
-            t.vs = reinterpret_cast<const uint16_t*>(slot + p.ring_vs);
+            t.k = ck;
+            t.v = cv;
+            t.ks = reinterpret_cast<const uint16_t*>(cks);
+            t.vs = reinterpret_cast<const uint16_t*>(cvs);
             t.k_hs = kvdec::row_bytes(p.k_type, D);
             t.k_cs = krow_b;
             t.v_hs = kvdec::row_bytes(p.v_type, D);
@@ -331,10 +370,10 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
             t.slot[0].part_begin = 0;
             t.slot[0].to_acc = (c + 1 < n_chunks) ? 1 : 0;
             t.slot[0].n_clusters = kvdec::merge_clusters(splits, kvdec::merge_chunk(D, p.rec_rows));
+            t.slot[0].cl_begin = 0;
             // a tail cell's position is its index in the host tail
             t.cell_pos = nullptr;
             t.pos_offset = c0;
-            t.slot[0].cl_begin = 0;
             t.n_workgroups = splits * p.n_kv_heads;
             t.acc_in = acc[c % 2];
             t.acc_out = acc[(c + 1) % 2];
@@ -343,7 +382,7 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
                 e = (hipError_t)le;
                 break;
             }
-            e = hipEventRecord(ev_free[r], ks);
+            if (!zc) e = hipEventRecord(ev_free[r], ks);
         }
     }
     destroy();

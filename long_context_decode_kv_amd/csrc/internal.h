@@ -161,6 +161,7 @@ struct kvdec_plan {
 
     // Tail: per slot, host cell range and chunking.
     bool has_tail = false;
+    bool tail_zero_copy = false;     // chunk kernels read the host tail in place
     std::vector<int64_t> tail_begin, tail_n;
     int64_t tail_capacity = 0;
     int64_t chunk_cells = 0;

@@ -42,7 +42,7 @@ class Problem(ctypes.Structure):
         ("cell_begin", _p), ("n_occupied", _p), ("cells", _p), ("cells_off", _p),
         ("tail_begin", _p), ("n_tail", _p),
         ("tail_capacity_cells", _i64), ("tail_chunk_cells", _i64),
-        ("tail_ring_depth", _i32), ("n_queries", _i32),
+        ("tail_ring_depth", _i32), ("n_queries", _i32), ("tail_zero_copy", _i32), ("reserved", _i32),
     ]
 
 
@@ -53,7 +53,7 @@ class IO(ctypes.Structure):
         ("plan_cells", _p),
         ("k_tail", _p), ("v_tail", _p), ("k_tail_scales", _p), ("v_tail_scales", _p),
         ("out", _p), ("lse", _p), ("part_m", _p), ("part_l", _p), ("part_o", _p),
-        ("q_pos", _p), ("cell_pos", _p),
+        ("q_pos", _p), ("cell_pos", _p), ("copy_after", _p),
     ]
 
 
@@ -180,7 +180,7 @@ class Plan:
 
 def plan(n_q_heads, n_kv_heads, head_dim, n_slots, capacity_cells, *, k_type=F16, v_type=F16, scale=None,
          n_occupied=None, cell_begin=None, cells=None, n_tail=None, tail_begin=None, tail_capacity_cells=0,
-         tail_chunk_cells=0, tail_ring_depth=0, tiles_per_split=0, n_cu=0, n_queries=1):
+         tail_chunk_cells=0, tail_ring_depth=0, tiles_per_split=0, n_cu=0, n_queries=1, tail_zero_copy=False):
     """Build a plan.  ``cells`` is a list of per-slot raw cell arrays
     (indirect mode); otherwise ``n_occupied`` (and optional ``cell_begin``)
     give contiguous ranges.  ``n_queries`` query rows per slot.  ``n_cu=0``
@@ -219,6 +219,7 @@ def plan(n_q_heads, n_kv_heads, head_dim, n_slots, capacity_cells, *, k_type=F16
     p.tail_chunk_cells = tail_chunk_cells
     p.tail_ring_depth = tail_ring_depth
     p.n_queries = n_queries
+    p.tail_zero_copy = 1 if tail_zero_copy else 0
     h = _p()
     ws = ctypes.c_size_t()
     _check(lib.kvdec_plan(ctypes.byref(p), n_cu, ctypes.byref(h), ctypes.byref(ws)), "kvdec_plan")
@@ -233,11 +234,14 @@ def workspace(plan_, device="cuda"):
 
 def attend(plan_, q, k, v, ws, *, out=None, lse=None, part=None, k_scales=None, v_scales=None, plan_cells=None,
            k_cell_stride=0, k_head_stride=0, v_cell_stride=0, v_head_stride=0, k_tail=None, v_tail=None,
-           k_tail_scales=None, v_tail_scales=None, q_pos=None, cell_pos=None, stream=None, copy_stream=None):
+           k_tail_scales=None, v_tail_scales=None, q_pos=None, cell_pos=None, stream=None, copy_stream=None,
+           copy_after=None):
     """Enqueue one evaluation (see kvdec_attend in include/kvdec.h).
     ``part`` is an optional (m, l, o) tuple of output tensors; ``q_pos``
     (int32 [slots][n_queries]) and ``cell_pos`` (int32 [capacity]) are the
-    positions of the multi-query mask."""
+    positions of the multi-query mask.  ``copy_after`` (a torch.cuda.Event
+    or raw hipEvent_t) orders the tail copies after that event instead of
+    after all earlier work on the stream."""
     io = IO()
     io.q, io.k, io.v = _ptr(q), _ptr(k), _ptr(v)
     io.k_scales, io.v_scales = _ptr(k_scales), _ptr(v_scales)
@@ -250,6 +254,8 @@ def attend(plan_, q, k, v, ws, *, out=None, lse=None, part=None, k_scales=None, 
     if part is not None:
         io.part_m, io.part_l, io.part_o = (_ptr(t) for t in part)
     io.q_pos, io.cell_pos = _ptr(q_pos), _ptr(cell_pos)
+    if copy_after is not None:
+        io.copy_after = copy_after.cuda_event if hasattr(copy_after, "cuda_event") else int(copy_after)
     nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else int(ws[1])
     wptr = _ptr(ws) if hasattr(ws, "numel") else int(ws[0])
     st = _stream_handle(stream)

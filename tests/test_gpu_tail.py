@@ -30,7 +30,7 @@ def pinned(a):
     return t
 
 
-def run_tail(K, c, window, tail, chunk, depth, copy_stream=None):
+def run_tail(K, c, window, tail, chunk, depth, copy_stream=None, zero_copy=False):
     """window: per slot (begin, n) resident cells; tail: per slot (begin, n)
     cells of the host tail, which holds rows [0, tail_capacity) of the cache."""
     import torch
@@ -38,7 +38,7 @@ def run_tail(K, c, window, tail, chunk, depth, copy_stream=None):
     p = K.plan(c.hq, c.hkv, c.d, c.n_slots, c.capacity, k_type=c.kind, v_type=c.vkind, scale=c.scale,
                n_occupied=[n for _, n in window], cell_begin=[b for b, _ in window], n_tail=[n for _, n in tail],
                tail_begin=[b for b, _ in tail], tail_capacity_cells=tail_cap, tail_chunk_cells=chunk,
-               tail_ring_depth=depth)
+               tail_ring_depth=depth, tail_zero_copy=zero_copy)
     c.upload()
     hk, hv = pinned(c.kc[:tail_cap]), pinned(c.vc[:tail_cap])
     hks = None if c.ks is None else pinned(c.ks[:tail_cap])
@@ -115,3 +115,52 @@ def test_mixed_kind_tail(K):
     c = Case(58, 24, 4, 256, kind=O.Q8_B32, v_kind=O.Q4_B32, occupied=[4000])
     out, lse, _ = run_tail(K, c, window=[(1500, 2500)], tail=[(0, 1500)], chunk=512, depth=3)
     check(out, lse, *c.oracle())
+
+
+
+@pytest.mark.parametrize("kind,vkind", [(O.F16, O.F16), (O.Q8_B32, O.Q4_B32)])
+def test_zero_copy_tail_equals_staged(K, kind, vkind):
+    """Kernels reading the pinned host tail in place give the staged ring's
+    result bit for bit (same chunks, same splits), and the oracle's."""
+    c = Case(59 + kind, 24, 4, 256, kind=kind, v_kind=vkind, occupied=[6000])
+    staged = run_tail(K, c, window=[(2200, 3800)], tail=[(0, 2200)], chunk=512, depth=2)
+    zc = run_tail(K, c, window=[(2200, 3800)], tail=[(0, 2200)], chunk=512, depth=2, zero_copy=True)
+    assert zc[2].workspace_bytes < staged[2].workspace_bytes  # no ring
+    check(zc[0], zc[1], *c.oracle())
+    assert np.array_equal(zc[0], staged[0]) and np.array_equal(zc[1], staged[1])
+
+
+def test_copy_after_two_workspaces_across_layers(K):
+    """Cross-layer tail prefetch: layers alternate two workspaces and each
+    call's copies wait only for the call two layers back (copy_after); every
+    layer matches the oracle and the default ordering bit for bit."""
+    import torch
+    layers = [Case(90 + i, 32, 8, 128, occupied=[4500]) for i in range(5)]
+    t = 2600
+    p = K.plan(32, 8, 128, 1, 4500, n_occupied=[4500 - t], cell_begin=[t], n_tail=[t], tail_capacity_cells=t,
+               tail_chunk_cells=512, tail_ring_depth=2)
+    for c in layers:
+        c.upload()
+        c.hk, c.hv = pinned(c.kc[:t]), pinned(c.vc[:t])
+    cs = torch.cuda.Stream()
+
+    def run_all(prefetch):
+        ws = [K.workspace(p), K.workspace(p)]
+        ev = [torch.cuda.Event(), torch.cuda.Event()]
+        outs = []
+        for i, c in enumerate(layers):
+            out = torch.full((1, 32, 128), float("nan"), device="cuda")
+            lse = torch.full((1, 32), float("nan"), device="cuda")
+            K.attend(p, c.q_d, c.kc_d, c.vc_d, ws[i % 2] if prefetch else ws[0], out=out, lse=lse, k_tail=c.hk,
+                     v_tail=c.hv, copy_stream=cs, copy_after=ev[i % 2] if prefetch else None)
+            if prefetch:
+                ev[i % 2].record()
+            outs.append((out, lse))
+        torch.cuda.synchronize()
+        return [(o.cpu().numpy(), l.cpu().numpy()) for o, l in outs]
+
+    base = run_all(False)
+    pre = run_all(True)
+    for c, (o, l), (o2, l2) in zip(layers, base, pre):
+        check(o2, l2, *c.oracle())
+        assert np.array_equal(o, o2) and np.array_equal(l, l2)

@@ -29,7 +29,7 @@ def test_exports_every_declared_function():
     for name in names:
         assert hasattr(K.lib, name), name
     assert set(names) == set(K.EXPORTED)
-    assert K.version() == 10100
+    assert K.version() == 10200
 
 
 def test_probe_library_exports_and_rejects_bad_arguments():
@@ -249,3 +249,20 @@ def test_multi_query_attend_needs_q_pos():
     assert "q_pos" in K.lib.kvdec_last_error().decode()
     assert _status(lambda: K.attend(p, FAKE, FAKE, FAKE, ws, out=FAKE, q_pos=FAKE, cell_pos=FAKE + 2,
                                     stream=0)) == K.E_INVALID
+
+
+
+def test_zero_copy_tail_plan():
+    base = dict(n_occupied=[1000], cell_begin=[3000], n_tail=[3000], tail_capacity_cells=3000, n_cu=256,
+                tail_chunk_cells=2048)
+    staged = K.plan(32, 8, 128, 1, 4000, **base)
+    zc = K.plan(32, 8, 128, 1, 4000, tail_zero_copy=True, **base)
+    # two chunks: the default depth 4 is clamped to 2 slots of 2048 cells x 8 heads x (K + V) rows
+    ring = 2 * 2048 * 8 * 128 * 2 * 2
+    assert staged.workspace_bytes - zc.workspace_bytes >= ring
+    assert staged.workspace_bytes - zc.workspace_bytes < 2 * ring
+    assert zc.info()["n_tail_chunks"] == staged.info()["n_tail_chunks"] == 2
+    # default chunk: 8192 cells, one chunk for this tail
+    one = K.plan(32, 8, 128, 1, 4000, n_occupied=[1000], cell_begin=[3000], n_tail=[3000], tail_capacity_cells=3000,
+                 n_cu=256)
+    assert one.info()["n_tail_chunks"] == 1
