@@ -234,12 +234,35 @@ class Gqa6Quant(Workload):
                                  self.v_kind)
 
     def setup(self, K, torch, seed0):
+        import numpy as np
         from long_context_decode_kv_amd import synth
         lists, cap = synth.interleaved_record_lists(self.lengths)
+        t0 = time.perf_counter()
         self.plan = K.plan(24, 4, 256, 4, cap, k_type=self.kind, v_type=self.v_kind, cells=lists)
-        entries, _ = self.plan.cells()
+        entries, offs = self.plan.cells()
         self.n_entries = len(entries)
         self.plan_cells = torch.from_numpy(entries).cuda()
+        torch.cuda.synchronize()
+        host_ms = (time.perf_counter() - t0) * 1e3
+        # the same plan built on the device from the raw lists (kvdec_build_cells)
+        budget = [int(offs[i + 1] - offs[i]) // 128 for i in range(4)]
+        dplan = K.plan(24, 4, 256, 4, cap, k_type=self.kind, v_type=self.v_kind, max_records=budget)
+        dws = K.workspace(dplan)
+        raw = torch.from_numpy(np.concatenate([np.asarray(x, np.int32) for x in lists])).cuda()
+        raw_off = torch.from_numpy(np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int64)).cuda()
+        dcells = torch.empty(dplan.info()["n_entries"], dtype=torch.int32, device="cuda")
+        K.build_cells(dplan, raw, raw_off, dcells, dws)
+        torch.cuda.synchronize()
+        assert torch.equal(dcells, self.plan_cells)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(20):
+            K.build_cells(dplan, raw, raw_off, dcells, dws)
+        b.record()
+        torch.cuda.synchronize()
+        self.plan_build = {"raw_entries": int(raw.numel()), "plan_entries": self.n_entries,
+                           "host_kvdec_plan_and_upload_ms": round(host_ms, 3),
+                           "device_kvdec_build_cells_us": round(a.elapsed_time(b) * 1e3 / 20, 2)}
         self.k, self.v, self.q, self.out, self.lse = [], [], [], [], []
         for c in range(self.layers):
             s = seed0 * 100 + c
@@ -249,6 +272,9 @@ class Gqa6Quant(Workload):
             self.out.append(torch.empty(4, 24, 256, device="cuda"))
             self.lse.append(torch.empty(4, 24, device="cuda"))
         self.ws = K.workspace(self.plan)
+
+    def extra(self):
+        return {"plan_build": self.plan_build}
 
     def launch(self, K, i):
         K.attend(self.plan, self.q[i], self.k[i][0], self.v[i][0], self.ws, out=self.out[i], lse=self.lse[i],
@@ -608,6 +634,8 @@ def main():
         "wall_s_timed": round(wall_s, 4),
         "kernel_source_sha256_16": kernel_source_hash(),
     }
+    if hasattr(wl, "extra"):
+        res.update(wl.extra())
     if hasattr(wl, "pcie_bytes_per_launch"):
         pb = wl.pcie_bytes_per_launch() * launches_per_step
         link = measure_h2d(torch)

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_VERSION 10200 /* 1.2.0: tail_zero_copy, copy_after */
+#define KVDEC_VERSION 10300 /* 1.3.0: device-built plans */
 
 /* Status codes. */
 #define KVDEC_OK 0
@@ -109,6 +109,12 @@ extern "C" {
  *     entry k is record*128 + k when that cell was kept and -1 otherwise
  *     ("KVARN KV Performance optimizations", items 3 and 4).
  *
+ *   device-built (cells == NULL, max_records != NULL): an indirect plan whose
+ *     entries are built on the device by kvdec_build_cells, for cell lists
+ *     that change every step.  Slot s gets max_records[s] 128-entry segments
+ *     (0 .. ceil(capacity_cells / 128)); records the lists do not fill are
+ *     all holes.
+ *
  * Host tail (optional, contiguous mode only): when n_tail != NULL, slot s
  *   also attends cells [tail_begin[s], tail_begin[s] + n_tail[s]) of the
  *   pinned host tail arrays passed to kvdec_attend (dense
@@ -160,6 +166,7 @@ typedef struct kvdec_problem {
     int32_t n_queries;      /* query rows per slot, 1..8; 0 means 1 */
     int32_t tail_zero_copy; /* 1: kernels read the host tail in place */
     int32_t reserved;       /* 0 */
+    const int32_t* max_records; /* [n_slots]: device-built indirect plan, see kvdec_build_cells */
 } kvdec_problem;
 
 /* Opaque, immutable plan. */
@@ -253,8 +260,38 @@ int kvdec_plan(const kvdec_problem* problem, int32_t n_cu, kvdec_plan_t** out, s
 /* Copy out the plan's indirect entries (int32, -1 holes) and per-slot entry
  * offsets (int64 [n_slots + 1]) for upload to the device.  With
  * cells_out == NULL only *n_entries is written.  A contiguous plan has zero
- * entries.  Errors: KVDEC_E_INVALID. */
+ * entries; a device-built plan has no host entries (cells_out must be NULL,
+ * offsets_out may be given).  Errors: KVDEC_E_INVALID. */
 int kvdec_plan_cells(const kvdec_plan_t* plan, int32_t* cells_out, int64_t* offsets_out, int64_t* n_entries);
+
+/*
+ * Build the entries of a device-built indirect plan on the device (the
+ * descriptor setup of "KVARN KV Performance optimizations", "What was
+ * implemented" item 5, with the plan layout of items 3 and 4): per slot,
+ * the raw list is deduplicated through a capacity-sized bitmap, the kept
+ * cells are grouped by physical 128-cell record, a 1024-thread scan takes the
+ * records in ascending order, and one 128-entry segment is emitted per
+ * record (entry k = record*128 + k when kept, else -1), followed by
+ * segments of -1 only up to max_records[s].  The result equals kvdec_plan_cells of a
+ * host plan over the same lists, padded with -1 segments.
+ *
+ * raw_cells: device int32, slot s's list at raw_cells[raw_off[s] ..
+ *   raw_off[s+1]-1]; -1 entries are holes, duplicates are allowed; entries
+ *   below -1 or at / above capacity_cells are dropped and counted.
+ * raw_off: device int64 [n_slots + 1].
+ * plan_cells: device int32 [n_entries of the plan] (kvdec_plan_get_info),
+ *   the plan_cells argument of kvdec_attend.
+ * n_records: device int32 [n_slots + 1] or NULL: records each slot's list
+ *   touches -- more than max_records[s] means records were left out -- and,
+ *   last, the number of dropped entries.
+ * workspace: the plan's workspace (its build area is separate from what an
+ *   in-flight kvdec_attend on the same workspace uses only if enqueued on the
+ *   same stream before it).
+ * Asynchronous on `stream`.  Errors: KVDEC_E_INVALID (not a device-built
+ *   plan, null or misaligned pointers), KVDEC_E_WORKSPACE, KVDEC_E_DEVICE.
+ */
+int kvdec_build_cells(const kvdec_plan_t* plan, const int32_t* raw_cells, const int64_t* raw_off, int32_t* plan_cells,
+                      int32_t* n_records, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Summary of a plan, for logs and tests. */
 typedef struct kvdec_plan_info {

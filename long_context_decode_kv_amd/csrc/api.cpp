@@ -100,8 +100,13 @@ int kvdec_plan(const kvdec_problem* problem, int32_t n_cu, kvdec_plan_t** out, s
 
 int kvdec_plan_cells(const kvdec_plan_t* plan, int32_t* cells_out, int64_t* offsets_out, int64_t* n_entries) {
     if (!plan || !n_entries) return fail(KVDEC_E_INVALID, "plan and n_entries must be non-null");
-    *n_entries = (int64_t)plan->cells.size();
-    if (cells_out && !plan->cells.empty()) std::memcpy(cells_out, plan->cells.data(), plan->cells.size() * 4);
+    if (plan->device_cells) {
+        if (cells_out) return fail(KVDEC_E_INVALID, "a device-built plan's entries come from kvdec_build_cells");
+        *n_entries = plan->n_device_entries;
+    } else {
+        *n_entries = (int64_t)plan->cells.size();
+        if (cells_out && !plan->cells.empty()) std::memcpy(cells_out, plan->cells.data(), plan->cells.size() * 4);
+    }
     if (offsets_out) {
         for (int s = 0; s <= plan->n_slots; ++s)
             offsets_out[s] = plan->indirect ? plan->cells_off[s] : 0;
@@ -116,7 +121,7 @@ int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info) {
     info->n_workgroups = plan->n_workgroups;
     info->tiles_per_split = plan->max_tiles_per_split;
     info->n_tiles = plan->n_tiles;
-    info->n_entries = (int64_t)plan->cells.size();
+    info->n_entries = plan->device_cells ? plan->n_device_entries : (int64_t)plan->cells.size();
     info->n_tail_chunks = plan->n_tail_chunks;
     info->workspace_bytes = (int64_t)plan->workspace_bytes;
     info->n_queries = plan->n_q;
@@ -387,6 +392,44 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
     }
     destroy();
     if (e != hipSuccess) return device_fail(e, "tail streaming");
+    return KVDEC_OK;
+}
+
+int kvdec_build_cells(const kvdec_plan_t* plan, const int32_t* raw_cells, const int64_t* raw_off, int32_t* plan_cells,
+                      int32_t* n_records, void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    if (!plan) return fail(KVDEC_E_INVALID, "plan must be non-null");
+    const kvdec_plan_t& p = *plan;
+    if (!p.device_cells) return fail(KVDEC_E_INVALID, "not a device-built plan (kvdec_problem.max_records)");
+    if (!raw_cells || !raw_off || !aligned(raw_cells, 4) || !aligned(raw_off, 8))
+        return fail(KVDEC_E_INVALID, "raw_cells (4-byte) and raw_off (8-byte) must be aligned device pointers");
+    if (p.n_device_entries > 0 && (!plan_cells || !aligned(plan_cells, 4)))
+        return fail(KVDEC_E_INVALID, "plan_cells must be a 4-byte aligned device pointer");
+    if (!aligned(n_records, 4)) return fail(KVDEC_E_INVALID, "n_records must be 4-byte aligned");
+    if (!workspace || workspace_bytes < p.workspace_bytes)
+        return fail(KVDEC_E_WORKSPACE, "workspace needs " + std::to_string(p.workspace_bytes) + " bytes");
+    if (!aligned(workspace, 256)) return fail(KVDEC_E_INVALID, "workspace must be 256-byte aligned");
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    kvdec::BuildArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.raw = raw_cells;
+    a.raw_off = raw_off;
+    a.bitmap = reinterpret_cast<uint32_t*>(ws + p.off_build_bitmap);
+    a.list = reinterpret_cast<int32_t*>(ws + p.off_build_list);
+    a.count = reinterpret_cast<int32_t*>(ws + p.off_build_count);
+    a.n_records = n_records;
+    a.out = plan_cells;
+    a.capacity = p.capacity;
+    a.words_per_slot = p.bm_words_per_slot;
+    a.n_entries = p.n_device_entries;
+    a.n_slots = p.n_slots;
+    for (int s = 0; s < p.n_slots; ++s) {
+        a.max_records[s] = p.max_records[s];
+        a.list_off[s + 1] = a.list_off[s] + p.max_records[s];
+        a.entry_off[s + 1] = p.cells_off[s + 1];
+    }
+    const int e = kvdec::launch_build_cells(a, stream);
+    if (e != hipSuccess) return device_fail((hipError_t)e, "plan build kernels");
     return KVDEC_OK;
 }
 

@@ -125,6 +125,26 @@ struct MergeArgs {
     float* mo;
 };
 
+// Arguments of the device plan build (plan_device.hip).
+struct BuildArgs {
+    const int32_t* raw;      // raw lists
+    const int64_t* raw_off;  // [n_slots + 1] (device)
+    uint32_t* bitmap;        // [n_slots][words_per_slot]
+    int32_t* list;           // present records, slot s at list_off[s]
+    int32_t* count;          // [n_slots + 1]: records each slot touches, then dropped entries
+    int32_t* n_records;      // caller copy of count, or null
+    int32_t* out;            // plan entries
+    int64_t capacity;
+    int64_t words_per_slot;
+    int64_t n_entries;
+    int32_t n_slots;
+    int32_t pad;
+    int32_t max_records[KVDEC_MAX_SLOTS];
+    int64_t list_off[KVDEC_MAX_SLOTS + 1];
+    int64_t entry_off[KVDEC_MAX_SLOTS + 1];
+};
+int launch_build_cells(const BuildArgs& a, void* stream);
+
 // Kernel launchers (kernels.hip, split_*.hip).  Return a hipError_t value.
 // Per pair of storage kinds, the launcher of the split-kernel instance for
 // (head_dim, group), or null.
@@ -156,8 +176,14 @@ struct kvdec_plan {
     int32_t n_part_records = 0;
     int32_t max_tiles_per_split = 0;
     int64_t n_tiles = 0;
-    std::vector<int32_t> cells;      // indirect entries
+    std::vector<int32_t> cells;      // indirect entries (host-built plans)
     std::vector<int64_t> cells_off;  // [n_slots + 1]
+    // device-built indirect plans (kvdec_build_cells)
+    bool device_cells = false;
+    std::vector<int32_t> max_records;  // segments per slot
+    int64_t n_device_entries = 0;
+    int64_t bm_words_per_slot = 0;
+    size_t off_build_bitmap = 0, off_build_list = 0, off_build_count = 0;
 
     // Tail: per slot, host cell range and chunking.
     bool has_tail = false;

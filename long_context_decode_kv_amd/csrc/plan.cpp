@@ -94,8 +94,9 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
         err = "capacity_cells, tiles_per_split must be >= 0 and n_cu >= 1";
         return KVDEC_E_INVALID;
     }
-    const bool indirect = p.cells != nullptr;
-    if (indirect && !p.cells_off) {
+    const bool device_cells = p.cells == nullptr && p.max_records != nullptr;
+    const bool indirect = p.cells != nullptr || device_cells;
+    if (p.cells != nullptr && !p.cells_off) {
         err = "indirect mode needs cells_off";
         return KVDEC_E_INVALID;
     }
@@ -133,10 +134,28 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
     plan.scale = p.scale;
     plan.capacity = p.capacity_cells;
     plan.indirect = indirect;
+    plan.device_cells = device_cells;
     plan.slots.assign(p.n_slots, SlotArg{});
 
     // ---- cells of each slot
-    if (indirect) {
+    if (device_cells) {
+        // entries come from kvdec_build_cells: max_records[s] segments per slot
+        const int64_t rec_cap = ceil_div(std::max<int64_t>(p.capacity_cells, 1), kTile);
+        plan.cells_off.assign(p.n_slots + 1, 0);
+        plan.max_records.assign(p.n_slots, 0);
+        for (int s = 0; s < p.n_slots; ++s) {
+            const int64_t m = p.max_records[s];
+            if (m < 0 || m > rec_cap) {
+                err = "slot " + std::to_string(s) + ": max_records outside 0 .. ceil(capacity_cells / 128)";
+                return KVDEC_E_INVALID;
+            }
+            plan.max_records[s] = (int32_t)m;
+            plan.slots[s].first = plan.cells_off[s];
+            plan.slots[s].n = m * kTile;
+            plan.cells_off[s + 1] = plan.cells_off[s] + m * kTile;
+        }
+        plan.n_device_entries = plan.cells_off[p.n_slots];
+    } else if (indirect) {
         plan.cells_off.assign(p.n_slots + 1, 0);
         for (int s = 0; s < p.n_slots; ++s) {
             if (p.cells_off[s] < 0 || p.cells_off[s + 1] < p.cells_off[s]) {
@@ -297,6 +316,17 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
         plan.ring_slot_bytes = r;
         plan.off_ring = off;
         if (!plan.tail_zero_copy) off += r * (size_t)plan.ring_depth;  // in-place reads need no ring
+    }
+    if (device_cells) {
+        // build area of kvdec_build_cells: per-slot bitmaps (4 words per
+        // record), the present records of each slot, counters
+        plan.bm_words_per_slot = 4 * ceil_div(std::max<int64_t>(p.capacity_cells, 1), kTile);
+        plan.off_build_bitmap = off;
+        off = align_up(off + sizeof(uint32_t) * (size_t)p.n_slots * plan.bm_words_per_slot, 256);
+        plan.off_build_list = off;
+        off = align_up(off + sizeof(int32_t) * (size_t)std::max<int64_t>(1, plan.n_device_entries / kTile), 256);
+        plan.off_build_count = off;
+        off = align_up(off + sizeof(int32_t) * ((size_t)p.n_slots + 1), 256);
     }
     plan.workspace_bytes = align_up(std::max<size_t>(off, 256), 256);
     return KVDEC_OK;

@@ -43,6 +43,7 @@ class Problem(ctypes.Structure):
         ("tail_begin", _p), ("n_tail", _p),
         ("tail_capacity_cells", _i64), ("tail_chunk_cells", _i64),
         ("tail_ring_depth", _i32), ("n_queries", _i32), ("tail_zero_copy", _i32), ("reserved", _i32),
+        ("max_records", _p),
     ]
 
 
@@ -83,6 +84,8 @@ lib.kvdec_attend.argtypes = [_p, ctypes.POINTER(IO), _p, ctypes.c_size_t, _p, _p
 lib.kvdec_attend.restype = ctypes.c_int
 lib.kvdec_merge.argtypes = [_i32, ctypes.POINTER(PartialC), _i64, _i32, _p, _p, _p, _p, _p, _p]
 lib.kvdec_merge.restype = ctypes.c_int
+lib.kvdec_build_cells.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
+lib.kvdec_build_cells.restype = ctypes.c_int
 lib.kvdec_strerror.argtypes = [ctypes.c_int]
 lib.kvdec_strerror.restype = ctypes.c_char_p
 lib.kvdec_last_error.argtypes = []
@@ -92,7 +95,7 @@ lib.kvdec_version.restype = ctypes.c_int
 
 EXPORTED = [
     "kvdec_plan", "kvdec_plan_cells", "kvdec_plan_get_info", "kvdec_plan_splits", "kvdec_plan_free",
-    "kvdec_attend", "kvdec_merge", "kvdec_strerror", "kvdec_last_error", "kvdec_version",
+    "kvdec_attend", "kvdec_merge", "kvdec_build_cells", "kvdec_strerror", "kvdec_last_error", "kvdec_version",
 ]
 
 
@@ -180,7 +183,8 @@ class Plan:
 
 def plan(n_q_heads, n_kv_heads, head_dim, n_slots, capacity_cells, *, k_type=F16, v_type=F16, scale=None,
          n_occupied=None, cell_begin=None, cells=None, n_tail=None, tail_begin=None, tail_capacity_cells=0,
-         tail_chunk_cells=0, tail_ring_depth=0, tiles_per_split=0, n_cu=0, n_queries=1, tail_zero_copy=False):
+         tail_chunk_cells=0, tail_ring_depth=0, tiles_per_split=0, n_cu=0, n_queries=1, tail_zero_copy=False,
+         max_records=None):
     """Build a plan.  ``cells`` is a list of per-slot raw cell arrays
     (indirect mode); otherwise ``n_occupied`` (and optional ``cell_begin``)
     give contiguous ranges.  ``n_queries`` query rows per slot.  ``n_cu=0``
@@ -220,6 +224,10 @@ def plan(n_q_heads, n_kv_heads, head_dim, n_slots, capacity_cells, *, k_type=F16
     p.tail_ring_depth = tail_ring_depth
     p.n_queries = n_queries
     p.tail_zero_copy = 1 if tail_zero_copy else 0
+    if max_records is not None:
+        mr = np.ascontiguousarray(np.asarray(max_records, dtype=np.int32))
+        keep.append(mr)
+        p.max_records = mr.ctypes.data
     h = _p()
     ws = ctypes.c_size_t()
     _check(lib.kvdec_plan(ctypes.byref(p), n_cu, ctypes.byref(h), ctypes.byref(ws)), "kvdec_plan")
@@ -261,6 +269,17 @@ def attend(plan_, q, k, v, ws, *, out=None, lse=None, part=None, k_scales=None, 
     st = _stream_handle(stream)
     cst = None if copy_stream is None else _stream_handle(copy_stream)
     _check(lib.kvdec_attend(plan_.handle, ctypes.byref(io), wptr, nbytes, st, cst), "kvdec_attend")
+
+
+def build_cells(plan_, raw_cells, raw_off, plan_cells, ws, *, n_records=None, stream=None):
+    """Build a device-built plan's entries on the device (kvdec_build_cells):
+    raw_cells int32 and raw_off int64 [n_slots + 1] device tensors; writes
+    plan_cells (int32 [n_entries]) and optionally n_records (int32
+    [n_slots + 1])."""
+    nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else int(ws[1])
+    wptr = _ptr(ws) if hasattr(ws, "numel") else int(ws[0])
+    _check(lib.kvdec_build_cells(plan_.handle, _ptr(raw_cells), _ptr(raw_off), _ptr(plan_cells), _ptr(n_records),
+                                 wptr, nbytes, _stream_handle(stream)), "kvdec_build_cells")
 
 
 def merge(parts, n_rows, head_dim, *, out=None, lse=None, merged=None, stream=None):

@@ -1,0 +1,105 @@
+"""GPU checks of the device-built indirect plan (kvdec_build_cells): the
+entries are bit-exact against the oracle's compact plan of the same raw lists
+(padded with -1 segments up to each slot's record budget), the record counts
+and dropped entries are reported, and attention through the device-built
+plan matches the float64 oracle."""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from gpu_cases import Case, check, dev
+from long_context_decode_kv_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    import torch
+    assert torch.cuda.is_available()
+    from long_context_decode_kv_amd import kvdec
+    return kvdec
+
+
+def flat(lists):
+    off = np.concatenate([[0], np.cumsum([len(x) for x in lists])]).astype(np.int64)
+    cells = np.concatenate([np.asarray(x, np.int32) for x in lists]) if off[-1] else np.zeros(1, np.int32)
+    return cells, off
+
+
+def build(K, lists, capacity, max_records, hq=24, hkv=4, d=256, kind=O.Q8_B32):
+    import torch
+    p = K.plan(hq, hkv, d, len(lists), capacity, k_type=kind, v_type=kind, max_records=max_records)
+    ws = K.workspace(p)
+    cells, off = flat(lists)
+    out = torch.full((max(1, p.info()["n_entries"]),), 12345, dtype=torch.int32, device="cuda")
+    nrec = torch.full((len(lists) + 1,), -7, dtype=torch.int32, device="cuda")
+    K.build_cells(p, dev(cells), dev(off), out, ws, n_records=nrec)
+    torch.cuda.synchronize()
+    return p, ws, out.cpu().numpy()[:p.info()["n_entries"]], nrec.cpu().numpy()
+
+
+def expected(lists, capacity, max_records):
+    """Oracle compact plan of the in-range entries, each slot padded (or cut)
+    to its record budget."""
+    want, counts = [], []
+    for raw, m in zip(lists, max_records):
+        keep = [c for c in raw if -1 <= c < capacity]
+        entries, _ = O.compact_plan([keep], capacity)
+        n_rec = len(entries) // 128
+        counts.append(n_rec)
+        seg = entries[:m * 128]
+        want.append(np.concatenate([seg, np.full(m * 128 - len(seg), -1, np.int32)]))
+    return np.concatenate(want) if want else np.zeros(0, np.int32), counts
+
+
+def test_entries_bit_exact_against_oracle(K):
+    r = synth.rng(300)
+    lists, cap = synth.interleaved_record_lists([3000, 1500, 200, 0, 129], r, shuffle=True, duplicates=40)
+    lists = [list(x) for x in lists]
+    lists[1] += [cap + 5, -3, cap]        # dropped: out of range
+    lists[2] += [-1, -1]
+    budget = [-(-3000 // 128) + 2, -(-1500 // 128), -(-200 // 128) + 5, 1, 2]
+    _, _, got, nrec = build(K, lists, cap, budget)
+    want, counts = expected(lists, cap, budget)
+    assert np.array_equal(got, want)
+    assert list(nrec[:5]) == counts and nrec[5] == 3
+
+
+def test_budget_overflow_keeps_lowest_records_and_reports_count(K):
+    r = synth.rng(301)
+    raw = r.permutation(5000)[:3000].tolist()
+    budget = [7]
+    _, _, got, nrec = build(K, [raw], 5000, budget)
+    want, counts = expected([raw], 5000, budget)
+    assert np.array_equal(got, want)
+    assert nrec[0] == counts[0] > 7
+
+
+def test_attend_through_device_built_plan_and_rebuild(K):
+    """Attention through the device-built plan equals the oracle; rebuilding
+    with changed lists on the same workspace (a plan that changes every step)
+    stays exact."""
+    import torch
+    c = Case(302, 24, 4, 256, kind=O.Q8_B32, indirect_lengths=[2500, 800, 7], shuffle=True, duplicates=11)
+    budget = [-(-2500 // 128) + 3, -(-800 // 128) + 1, 2]
+    p = K.plan(24, 4, 256, 3, c.capacity, k_type=O.Q8_B32, v_type=O.Q8_B32, scale=c.scale, max_records=budget)
+    ws = K.workspace(p)
+    c.upload()
+    entries = torch.empty(p.info()["n_entries"], dtype=torch.int32, device="cuda")
+    for step in range(2):
+        lists = [list(x) for x in c.raw]
+        if step == 1:  # the next step: one more cell per slot, one cell dropped
+            lists = [x[1:] + [int(x[0])] for x in lists]
+            lists[0].append(int((max(c for c in lists[0] if c >= 0) + 1) % c.capacity))
+        cells, off = flat(lists)
+        K.build_cells(p, dev(cells), dev(off), entries, ws)
+        out = torch.empty(3, 24, 256, device="cuda")
+        lse = torch.empty(3, 24, device="cuda")
+        K.attend(p, c.q_d, c.kc_d, c.vc_d, ws, out=out, lse=lse, k_scales=c.ks_d, v_scales=c.vs_d,
+                 plan_cells=entries)
+        torch.cuda.synchronize()
+        oc = [O.compact_plan([x], c.capacity)[0] for x in lists]
+        wo, wl = O.decode_attention(c.q, [((c.kind, c.kc, c.ks), (c.vkind, c.vc, c.vs), oc)], c.hkv, c.scale)
+        check(out.cpu().numpy(), lse.cpu().numpy(), wo, wl)

@@ -3,6 +3,7 @@ function include/kvdec.h declares, the planner's compact plan is bit-exact
 against the oracle, the split table covers every tile exactly once, and every
 error path returns its status before any device work (no GPU needed)."""
 
+import ctypes
 import math
 import os
 import re
@@ -29,7 +30,7 @@ def test_exports_every_declared_function():
     for name in names:
         assert hasattr(K.lib, name), name
     assert set(names) == set(K.EXPORTED)
-    assert K.version() == 10200
+    assert K.version() == 10300
 
 
 def test_probe_library_exports_and_rejects_bad_arguments():
@@ -266,3 +267,26 @@ def test_zero_copy_tail_plan():
     one = K.plan(32, 8, 128, 1, 4000, n_occupied=[1000], cell_begin=[3000], n_tail=[3000], tail_capacity_cells=3000,
                  n_cu=256)
     assert one.info()["n_tail_chunks"] == 1
+
+
+def test_device_built_plan_shape_and_errors():
+    """A device-built indirect plan: max_records segments per slot, no host
+    entries, validation of the record budget and of kvdec_build_cells."""
+    p = K.plan(24, 4, 256, 3, 5000, k_type=K.Q8_B32, v_type=K.Q8_B32, max_records=[10, 0, 40], n_cu=256)
+    info = p.info()
+    assert info["n_entries"] == 50 * 128
+    n = K._i64()
+    offs = np.zeros(4, np.int64)
+    assert K.lib.kvdec_plan_cells(p.handle, None, offs.ctypes.data, ctypes.byref(n)) == 0
+    assert n.value == 50 * 128 and list(offs) == [0, 1280, 1280, 6400]
+    buf = np.zeros(10, np.int32)
+    assert K.lib.kvdec_plan_cells(p.handle, buf.ctypes.data, None, ctypes.byref(n)) == K.E_INVALID
+    assert _status(lambda: K.plan(24, 4, 256, 1, 5000, k_type=K.Q8_B32, v_type=K.Q8_B32, max_records=[41],
+                                  n_cu=256)) == K.E_INVALID                    # > ceil(5000 / 128)
+    assert _status(lambda: K.plan(24, 4, 256, 1, 5000, max_records=[-1], n_cu=256)) == K.E_INVALID
+    ws = (FAKE, p.workspace_bytes)
+    assert _status(lambda: K.build_cells(p, FAKE, FAKE, FAKE, (FAKE, 16), stream=0)) == K.E_WORKSPACE
+    assert _status(lambda: K.build_cells(p, FAKE, FAKE + 4, FAKE, ws, stream=0)) == K.E_INVALID  # raw_off align
+    assert _status(lambda: K.build_cells(p, 0, FAKE, FAKE, ws, stream=0)) == K.E_INVALID
+    host = K.plan(24, 4, 256, 1, 5000, cells=[[1, 2]], n_cu=256)
+    assert _status(lambda: K.build_cells(host, FAKE, FAKE, FAKE, ws, stream=0)) == K.E_INVALID  # not device-built
