@@ -421,6 +421,7 @@ class ContiguousModelOneLaunch(ContiguousModel):
         self.plan = K.plan(self.hq, self.hkv, self.d, L, L * cap, n_occupied=[self.occupied] * L,
                            cell_begin=[layer * cap for layer in range(L)])
         self.ws = K.workspace(self.plan)
+        self.q_pos = None
 
     def oracle_sample(self, budget_s):
         done, el, sample = super().oracle_sample(budget_s)

@@ -193,6 +193,7 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
 
     // ---- split decomposition: tiles of every (slot, KV head) spread over
     // about two workgroups per compute unit.
+    const bool staged = p.k_type == KVDEC_F16 && p.v_type == KVDEC_F16 && !uses_matrix_cores(group, n_q, p.head_dim);
     int64_t total_tiles = 0;
     for (auto& sa : plan.slots) {
         const int64_t t = ceil_div(sa.n, kTile);
@@ -205,7 +206,23 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
     }
     plan.n_tiles = total_tiles;
     int64_t tps = p.tiles_per_split;
-    if (tps == 0) tps = std::max<int64_t>(1, ceil_div(total_tiles, 2 * (int64_t)n_cu));
+    if (tps == 0) {
+        tps = std::max<int64_t>(1, ceil_div(total_tiles, 2 * (int64_t)n_cu));
+        // f16 caches on the vector-ALU kernel stage the next step of a long
+        // split through LDS, so one workgroup keeps enough bytes in flight
+        // for its compute unit. Once splits are eight tiles or longer: one
+        // split per compute unit when that covers every (slot, KV head),
+        // else about eight splits per compute unit, which the dispatcher
+        // balances (a second partial round of long splits would leave most
+        // of the chip idle at the end).
+        if (staged && tps >= 8) {
+            const int64_t one = ceil_div(total_tiles, (int64_t)n_cu);
+            int64_t wgs_one = 0;
+            for (auto& sa : plan.slots)
+                wgs_one += std::max<int64_t>(1, ceil_div((int64_t)sa.n_tiles, one)) * p.n_kv_heads;
+            tps = wgs_one <= n_cu ? one : std::max<int64_t>(8, ceil_div(total_tiles, 8 * (int64_t)n_cu));
+        }
+    }
     int64_t wgs = 0;
     plan.max_tiles_per_split = 0;
     for (auto& sa : plan.slots) {

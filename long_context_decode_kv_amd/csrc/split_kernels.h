@@ -539,8 +539,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     __shared__ float sm_m[NS][G];
     __shared__ float sm_l[NS][G];
+    // f16 caches: the next step's K / V rows are loaded straight into LDS
+    // (global_load_lds, 16 bytes per lane, lane l's data at slot l) while the
+    // current step computes from registers -- a second step in flight that
+    // costs no VGPRs.  The staging area (16 KiB per wave) is reused for the
+    // stream merge after the loop.
+    constexpr bool kDma = KT == KVDEC_F16 && VT == KVDEC_F16;
+    constexpr int kMergeBytes = NS * G * (D + 16) * 4;
+    constexpr int kDmaBytes = kDma ? 4 * 64 * NCW * (NCK + NCV) * 16 : 0;
+    __shared__ __align__(16) unsigned char lds_raw[kMergeBytes > kDmaBytes ? kMergeBytes : kDmaBytes];
     // stream stride padded by 16 floats: streams written by one instruction land in different banks
-    __shared__ __align__(16) float sm_o[NS][G][D + 16];
+    float (*sm_o)[G][D + 16] = reinterpret_cast<float (*)[G][D + 16]>(lds_raw);
     __shared__ int sm_last;
 
     const int tid = threadIdx.x;
@@ -752,10 +761,94 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
     };
 
-    for (int64_t base = (int64_t)t0 * kTile; base < pos_end; base += STEP) {
-        Step st;
-        load_step(base, st);
-        compute_step(st);
+    // Short splits (one or two steps) gain nothing from staging -- their
+    // loads all leave at once anyway -- and take the plain path.
+    bool staged = false;
+    if constexpr (kDma) staged = (pos_end - (int64_t)t0 * kTile) > 2 * STEP;
+    if constexpr (kDma) if (staged) {
+        static_assert(FK::CB == 16 && FV::CB == 16 && !FK::scaled && !FV::scaled, "16-byte f16 chunks");
+        typedef __attribute__((address_space(3))) void lds_void;
+        unsigned char* stage = lds_raw + wave * (64 * NCW * (NCK + NCV) * 16);
+        // Slot of (cell j, chunk c) of this wave's staged step: K chunks, then V.
+        auto slot_k = [&](int j, int c) { return stage + ((j * (NCK + NCV) + c) * 64) * 16; };
+        auto slot_v = [&](int j, int c) { return stage + ((j * (NCK + NCV) + NCK + c) * 64) * 16; };
+        bool staged_valid[NCW];
+        auto stage_step = [&](int64_t base) {
+            int64_t cell[NCW];
+#pragma unroll
+            for (int j = 0; j < NCW; ++j) {
+                const int64_t pos = base + (wave * NCW + j) * CPW + cl;
+                if (a.plan) {
+                    const int64_t c = pos < pos_end ? (int64_t)a.plan[sa.first + pos] : -1;
+                    staged_valid[j] = c >= 0 && c < a.capacity;
+                    cell[j] = staged_valid[j] ? c : 0;
+                } else {
+                    staged_valid[j] = pos < pos_end;
+                    cell[j] = sa.first + (staged_valid[j] ? pos : 0);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NCW; ++j) {
+                const uint8_t* kr = kbase + cell[j] * a.k_cs;
+                const uint8_t* vr = vbase + cell[j] * a.v_cs;
+#pragma unroll
+                for (int c = 0; c < NCK; ++c)
+                    if (staged_valid[j])
+                        __builtin_amdgcn_global_load_lds((const void*)(kr + (c * R + sub) * 16), (lds_void*)slot_k(j, c),
+                                                         16, 0, 0);
+#pragma unroll
+                for (int c = 0; c < NCV; ++c)
+                    if (staged_valid[j])
+                        __builtin_amdgcn_global_load_lds((const void*)(vr + (c * R + sub) * 16), (lds_void*)slot_v(j, c),
+                                                         16, 0, 0);
+            }
+        };
+        auto read_staged = [&](Step& st) {
+#pragma unroll
+            for (int j = 0; j < NCW; ++j) {
+                st.valid[j] = staged_valid[j];
+#pragma unroll
+                for (int c = 0; c < NCK; ++c) {
+                    const uint4 x = *reinterpret_cast<const uint4*>(slot_k(j, c) + lane * 16);
+                    st.kc[j][c] = staged_valid[j] ? Chunk<16>{{x.x, x.y, x.z, x.w}} : zero_chunk<16>();
+                }
+#pragma unroll
+                for (int c = 0; c < NCV; ++c) {
+                    const uint4 x = *reinterpret_cast<const uint4*>(slot_v(j, c) + lane * 16);
+                    st.vc[j][c] = staged_valid[j] ? Chunk<16>{{x.x, x.y, x.z, x.w}} : zero_chunk<16>();
+                }
+            }
+        };
+        int64_t base = (int64_t)t0 * kTile;
+        if (base < pos_end) {
+            {
+                Step st;
+                load_step(base, st);                                 // step 0 -> registers
+                if (base + STEP < pos_end) stage_step(base + STEP);  // step 1 -> LDS
+                compute_step(st);
+            }
+            for (base += STEP; base < pos_end; base += STEP) {
+                // this step was staged: wait for its LDS loads, move it to
+                // registers, then stage the following step into the freed
+                // slots before computing
+                Step st;
+                __builtin_amdgcn_s_waitcnt(0);
+                __builtin_amdgcn_wave_barrier();
+                read_staged(st);
+                __builtin_amdgcn_s_waitcnt(0);
+                __builtin_amdgcn_wave_barrier();
+                if (base + STEP < pos_end) stage_step(base + STEP);
+                compute_step(st);
+            }
+        }
+        __syncthreads();  // every wave is done with its staging area before the merge reuses it
+    }
+    if (!staged) {
+        for (int64_t base = (int64_t)t0 * kTile; base < pos_end; base += STEP) {
+            Step st;
+            load_step(base, st);
+            compute_step(st);
+        }
     }
 
     // Merge the cell streams.  Lanes with the same sub own the same d-slice

@@ -60,6 +60,18 @@ def test_split_count_only_changes_rounding(K, tps):
     check(out, lse, *c.oracle())
 
 
+@pytest.mark.parametrize("d,g", [(64, 2), (128, 1), (128, 4), (128, 5), (256, 2), (256, 4)])
+@pytest.mark.parametrize("indirect", [False, True])
+def test_long_f16_splits(K, d, g, indirect):
+    """Splits of several steps, whose later steps are staged through LDS while
+    the current one is computed; ragged last step, holes in indirect plans."""
+    if indirect:
+        c = Case(40 + d + g, 2 * g, 2, d, indirect_lengths=[2900, 1000, 3], shuffle=True, duplicates=7)
+    else:
+        c = Case(40 + d + g, 2 * g, 2, d, occupied=[2900, 1000, 3])
+    check(*c.run(K, tiles_per_split=9), *c.oracle())
+
+
 @pytest.mark.parametrize("kind", [O.Q8_B32, O.Q4_B32])
 def test_quantized_indirect_interleaved(K, kind):
     """GQA-6, head_dim 256, four slots whose 128-cell records are interleaved,

@@ -127,10 +127,24 @@ def test_split_table_covers_every_tile_once(tps):
 def test_auto_split_fills_device():
     p = K.plan(32, 8, 128, 1, 16384, n_occupied=[13100], n_cu=256)
     info = p.info()
-    assert 256 <= info["n_workgroups"] <= 1024
+    assert 256 <= info["n_workgroups"] <= 512
+    # long f16 splits on the vector-ALU kernel: one workgroup per compute unit
+    p = K.plan(32, 8, 128, 1, 65536, n_occupied=[65536], n_cu=256)
+    info = p.info()
+    assert info["n_workgroups"] == 256 and info["tiles_per_split"] == 16
+    # long f16 splits over more (slot, KV head) pairs than compute units:
+    # about eight splits per compute unit
+    p = K.plan(32, 8, 128, 36, 36 * 16384, n_occupied=[13100] * 36, cell_begin=[i * 16384 for i in range(36)],
+               n_cu=256)
+    info = p.info()
+    assert info["tiles_per_split"] == 15 and info["n_workgroups"] == 36 * 8 * 7
     p = K.plan(40, 8, 128, 1, 524288, n_occupied=[524288], n_cu=256)
     info = p.info()
-    assert info["n_workgroups"] == 512 and info["tiles_per_split"] == 64
+    assert info["n_workgroups"] == 256 and info["tiles_per_split"] == 128
+    # quantized (matrix-core kernel): about two per compute unit
+    p = K.plan(24, 4, 256, 1, 65536, k_type=K.Q8_B32, v_type=K.Q8_B32, n_occupied=[65536], n_cu=256)
+    info = p.info()
+    assert info["n_workgroups"] == 512 and info["tiles_per_split"] == 4
 
 
 def test_tail_plan_chunks_and_workspace():
