@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_VERSION 10300 /* 1.3.0: device-built plans */
+#define KVDEC_VERSION 10400 /* 1.4.0: 32-cell split boundaries */
 
 /* Status codes. */
 #define KVDEC_OK 0
@@ -134,6 +134,13 @@ extern "C" {
  *   so that the launch fills the device.  Only the floating-point summation
  *   order depends on it.
  *
+ * split_cells: cells (plan positions) per workgroup, a multiple of 32; it
+ *   overrides tiles_per_split when nonzero.  Splits of the vector-ALU kernel
+ *   may end inside a 128-cell tile; the matrix-core kernel works on whole
+ *   tiles and rounds split_cells up to a multiple of 128.  The planner picks
+ *   32-cell split boundaries itself for the vector-ALU kernel, so that a
+ *   short context can still give every compute unit one equal split.
+ *
  * n_queries: query rows per slot, 1..8 (0 means 1).  Several rows per slot
  *   are the verification step of speculative decoding: split decoding serves
  *   up to 8 query rows, and such a call carries an attention mask ("KVARN KV
@@ -165,7 +172,7 @@ typedef struct kvdec_problem {
     int32_t tail_ring_depth;
     int32_t n_queries;      /* query rows per slot, 1..8; 0 means 1 */
     int32_t tail_zero_copy; /* 1: kernels read the host tail in place */
-    int32_t reserved;       /* 0 */
+    int32_t split_cells;    /* cells per split, multiple of 32; 0: tiles_per_split */
     const int32_t* max_records; /* [n_slots]: device-built indirect plan, see kvdec_build_cells */
 } kvdec_problem;
 
@@ -305,13 +312,16 @@ typedef struct kvdec_plan_info {
     int64_t workspace_bytes;
     int32_t n_queries;        /* query rows per slot */
     int32_t matrix_cores;     /* 1: served by the matrix-core kernel */
+    int32_t split_cells;      /* largest position count of any split */
+    int32_t split_unit;       /* split boundaries fall on multiples of this many positions */
 } kvdec_plan_info;
 
 int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info);
 
 /* Split table: for each workgroup of the resident launch, in launch order, 4 int64 values
- * (slot, kv head, first tile, tile count).  With splits_out == NULL only
- * *n_splits is written. */
+ * (slot, kv head, first position, position count), positions clipped to the
+ * slot's cells (contiguous) or plan entries (indirect).  With splits_out ==
+ * NULL only *n_splits is written. */
 int kvdec_plan_splits(const kvdec_plan_t* plan, int64_t* splits_out, int64_t* n_splits);
 
 void kvdec_plan_free(kvdec_plan_t* plan);

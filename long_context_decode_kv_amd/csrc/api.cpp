@@ -41,6 +41,7 @@ void common_args(const kvdec_plan_t& p, const kvdec_io& io, kvdec::SplitArgs& a)
     a.acc_rows = p.n_slots * p.n_q * p.n_q_heads;
     a.n_q = p.n_q;
     a.group = p.group;
+    a.split_unit = p.split_unit;
     // positions are used with several query rows per slot only
     a.q_pos = p.n_q > 1 ? io.q_pos : nullptr;
     a.cell_pos = p.n_q > 1 ? io.cell_pos : nullptr;
@@ -126,6 +127,8 @@ int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info) {
     info->workspace_bytes = (int64_t)plan->workspace_bytes;
     info->n_queries = plan->n_q;
     info->matrix_cores = kvdec::uses_matrix_cores(plan->group, plan->n_q, plan->head_dim) ? 1 : 0;
+    info->split_cells = plan->max_split_cells;
+    info->split_unit = plan->split_unit;
     return KVDEC_OK;
 }
 
@@ -138,12 +141,14 @@ int kvdec_plan_splits(const kvdec_plan_t* plan, int64_t* splits_out, int64_t* n_
         const kvdec::SlotArg& sa = plan->slots[s];
         for (int sp = 0; sp < sa.n_splits; ++sp)  // workgroup order: split-major
             for (int g = 0; g < plan->n_kv_heads; ++g) {
-                const int64_t t0 = (int64_t)sp * sa.n_tiles / sa.n_splits;
-                const int64_t t1 = (int64_t)(sp + 1) * sa.n_tiles / sa.n_splits;
+                const int64_t u0 = (int64_t)sp * sa.n_units / sa.n_splits;
+                const int64_t u1 = (int64_t)(sp + 1) * sa.n_units / sa.n_splits;
+                const int64_t p0 = std::min<int64_t>(u0 * plan->split_unit, sa.n);
+                const int64_t p1 = std::min<int64_t>(u1 * plan->split_unit, sa.n);
                 splits_out[4 * i + 0] = s;
                 splits_out[4 * i + 1] = g;
-                splits_out[4 * i + 2] = t0;
-                splits_out[4 * i + 3] = t1 - t0;
+                splits_out[4 * i + 2] = p0;
+                splits_out[4 * i + 3] = p1 - p0;
                 ++i;
             }
     }
@@ -369,7 +374,8 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
             const int32_t splits = std::max<int32_t>(1, (tiles + p.chunk_tiles_per_split - 1) / p.chunk_tiles_per_split);
             t.slot[0].first = 0;
             t.slot[0].n = nc;
-            t.slot[0].n_tiles = tiles;
+            t.slot[0].n_units = tiles;  // whole-tile splits
+            t.split_unit = kvdec::kTile;
             t.slot[0].n_splits = splits;
             t.slot[0].wg_begin = 0;
             t.slot[0].part_begin = 0;

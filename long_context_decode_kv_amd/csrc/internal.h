@@ -17,6 +17,7 @@ namespace kvdec {
 constexpr int kTile = KVDEC_TILE_CELLS;  // cells per tile / per physical record
 constexpr int kBlock = 32;               // elements sharing one f16 scale
 constexpr int kThreads = 256;            // threads per split workgroup (4 waves)
+constexpr int kSplitUnit = 32;           // split boundary granularity of the vector-ALU kernel
 constexpr int kMergeMaxParts = 64;       // kvdec_merge fan-in
 
 // Bytes of one stored (cell, KV head) row of codes.
@@ -59,7 +60,7 @@ constexpr int merge_clusters(int n_splits, int chunk) {
 struct SlotArg {
     int64_t first;       // contiguous: first cell; indirect: first plan entry
     int64_t n;           // contiguous: occupied cells; indirect: plan entries
-    int32_t n_tiles;     // ceil(n / 128)
+    int32_t n_units;     // ceil(n / split_unit): split boundaries fall on multiples of split_unit
     int32_t n_splits;    // splits per KV head (>= 1)
     int32_t wg_begin;    // first workgroup of this slot (n_kv_heads * n_splits of them)
     int32_t part_begin;  // first partial record of this slot
@@ -101,7 +102,7 @@ struct SplitArgs {
     const int32_t* cell_pos; // [capacity] positions of device cells, or null: cell index + pos_offset
     int64_t pos_offset;      // added to a cell index to give its position (no cell_pos)
     int32_t group;           // query heads per KV head (G)
-    int32_t pad0;
+    int32_t split_unit;      // positions per split unit (SlotArg::n_units)
     float scale_log2;        // scale * log2(e)
     int32_t n_slots;         // slots in this launch
     int32_t slot_base;       // index of slot 0 of this launch in q / out / lse / p*
@@ -175,6 +176,8 @@ struct kvdec_plan {
     int32_t n_workgroups = 0;
     int32_t n_part_records = 0;
     int32_t max_tiles_per_split = 0;
+    int32_t split_unit = 0;        // positions per split unit: 32 (vector-ALU kernel) or 128
+    int32_t max_split_cells = 0;   // largest split, in positions
     int64_t n_tiles = 0;
     std::vector<int32_t> cells;      // indirect entries (host-built plans)
     std::vector<int64_t> cells_off;  // [n_slots + 1]

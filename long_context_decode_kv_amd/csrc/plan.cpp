@@ -192,22 +192,36 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
     }
 
     // ---- split decomposition: tiles of every (slot, KV head) spread over
-    // about two workgroups per compute unit.
-    const bool staged = p.k_type == KVDEC_F16 && p.v_type == KVDEC_F16 && !uses_matrix_cores(group, n_q, p.head_dim);
+    // about two workgroups per compute unit.  Split boundaries fall on
+    // multiples of 32 positions for the vector-ALU kernel (a split may end
+    // inside a tile), on whole tiles for the matrix-core kernel.
+    const bool mfma = uses_matrix_cores(group, n_q, p.head_dim);
+    const bool staged = p.k_type == KVDEC_F16 && p.v_type == KVDEC_F16 && !mfma;
+    const int64_t unit = mfma ? kTile : kSplitUnit;
+    const int64_t upt = kTile / unit;  // units per tile
+    plan.split_unit = (int32_t)unit;
+    if (p.split_cells < 0 || p.split_cells % kSplitUnit != 0) {
+        err = "split_cells must be a non-negative multiple of 32";
+        return KVDEC_E_INVALID;
+    }
     int64_t total_tiles = 0;
     for (auto& sa : plan.slots) {
         const int64_t t = ceil_div(sa.n, kTile);
-        if (t > (1 << 30)) {
+        if (t > (1 << 24)) {
             err = "slot too long";
             return KVDEC_E_UNSUPPORTED;
         }
-        sa.n_tiles = (int32_t)t;
+        sa.n_units = (int32_t)ceil_div(sa.n, unit);
         total_tiles += t * p.n_kv_heads;
     }
     plan.n_tiles = total_tiles;
-    int64_t tps = p.tiles_per_split;
-    if (tps == 0) {
-        tps = std::max<int64_t>(1, ceil_div(total_tiles, 2 * (int64_t)n_cu));
+    int64_t ups = 0;  // units per split
+    if (p.split_cells > 0) {
+        ups = ceil_div((int64_t)p.split_cells, unit);
+    } else if (p.tiles_per_split > 0) {
+        ups = (int64_t)p.tiles_per_split * upt;
+    } else {
+        int64_t tps = std::max<int64_t>(1, ceil_div(total_tiles, 2 * (int64_t)n_cu));
         // f16 caches on the vector-ALU kernel stage the next step of a long
         // split through LDS, so one workgroup keeps enough bytes in flight
         // for its compute unit. Once splits are eight tiles or longer: one
@@ -219,14 +233,16 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
             const int64_t one = ceil_div(total_tiles, (int64_t)n_cu);
             int64_t wgs_one = 0;
             for (auto& sa : plan.slots)
-                wgs_one += std::max<int64_t>(1, ceil_div((int64_t)sa.n_tiles, one)) * p.n_kv_heads;
+                wgs_one += std::max<int64_t>(1, ceil_div(ceil_div(sa.n, kTile), one)) * p.n_kv_heads;
             tps = wgs_one <= n_cu ? one : std::max<int64_t>(8, ceil_div(total_tiles, 8 * (int64_t)n_cu));
         }
+        ups = tps * upt;
     }
     int64_t wgs = 0;
     plan.max_tiles_per_split = 0;
+    plan.max_split_cells = 0;
     for (auto& sa : plan.slots) {
-        const int64_t ns = std::max<int64_t>(1, ceil_div(sa.n_tiles, tps));
+        const int64_t ns = std::max<int64_t>(1, ceil_div(sa.n_units, ups));
         sa.n_splits = (int32_t)ns;
         sa.wg_begin = (int32_t)wgs;
         sa.part_begin = (int32_t)wgs;
@@ -236,8 +252,10 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
             err = "too many workgroups";
             return KVDEC_E_UNSUPPORTED;
         }
-        plan.max_tiles_per_split = std::max<int32_t>(plan.max_tiles_per_split, (int32_t)ceil_div(sa.n_tiles, ns));
+        const int64_t longest = std::min<int64_t>(sa.n, ceil_div(sa.n_units, ns) * unit);
+        plan.max_split_cells = std::max<int32_t>(plan.max_split_cells, (int32_t)longest);
     }
+    plan.max_tiles_per_split = (int32_t)ceil_div((int64_t)plan.max_split_cells, kTile);
     plan.n_workgroups = (int32_t)wgs;
     plan.n_part_records = (int32_t)wgs;
     const int chunk = merge_chunk(p.head_dim, rec_rows);

@@ -569,8 +569,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // cell row.
     const int split = local / a.n_kv_heads;
     const int g = local - split * a.n_kv_heads;
-    const int t0 = (int)(((int64_t)split * sa.n_tiles) / sa.n_splits);
-    const int t1 = (int)(((int64_t)(split + 1) * sa.n_tiles) / sa.n_splits);
+    // Positions [pos_begin, pos_end) of the slot: split boundaries fall on
+    // multiples of a.split_unit.
+    const int64_t pos_begin = (((int64_t)split * sa.n_units) / sa.n_splits) * a.split_unit;
+    const int64_t span_end = (((int64_t)(split + 1) * sa.n_units) / sa.n_splits) * a.split_unit;
     const int hq0 = g * G;  // first query head of the group
     const int64_t row0 = (int64_t)(a.slot_base + s) * a.n_q_heads + hq0;
 
@@ -604,8 +606,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const uint8_t* kbase = a.k + (int64_t)g * a.k_hs;
     const uint8_t* vbase = a.v + (int64_t)g * a.v_hs;
     const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-    const int64_t tile_end = (int64_t)t1 * kTile;
-    const int64_t pos_end = tile_end < sa.n ? tile_end : sa.n;
+    const int64_t pos_end = span_end < sa.n ? span_end : sa.n;
 
     // One step: NCW cells per lane.  Buffers of a step in flight.
     struct Step {
@@ -764,7 +765,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // Short splits (one or two steps) gain nothing from staging -- their
     // loads all leave at once anyway -- and take the plain path.
     bool staged = false;
-    if constexpr (kDma) staged = (pos_end - (int64_t)t0 * kTile) > 2 * STEP;
+    if constexpr (kDma) staged = (pos_end - pos_begin) > 2 * STEP;
     if constexpr (kDma) if (staged) {
         static_assert(FK::CB == 16 && FV::CB == 16 && !FK::scaled && !FV::scaled, "16-byte f16 chunks");
         typedef __attribute__((address_space(3))) void lds_void;
@@ -819,7 +820,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 }
             }
         };
-        int64_t base = (int64_t)t0 * kTile;
+        int64_t base = pos_begin;
         if (base < pos_end) {
             {
                 Step st;
@@ -844,7 +845,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         __syncthreads();  // every wave is done with its staging area before the merge reuses it
     }
     if (!staged) {
-        for (int64_t base = (int64_t)t0 * kTile; base < pos_end; base += STEP) {
+        for (int64_t base = pos_begin; base < pos_end; base += STEP) {
             Step st;
             load_step(base, st);
             compute_step(st);
@@ -1002,8 +1003,8 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
     const int local = wg - sa.wg_begin;
     const int split = local / a.n_kv_heads;
     const int g = local - split * a.n_kv_heads;
-    const int t0 = (int)(((int64_t)split * sa.n_tiles) / sa.n_splits);
-    const int t1 = (int)(((int64_t)(split + 1) * sa.n_tiles) / sa.n_splits);
+    const int64_t base0 = (((int64_t)split * sa.n_units) / sa.n_splits) * a.split_unit;
+    const int64_t span_end = (((int64_t)(split + 1) * sa.n_units) / sa.n_splits) * a.split_unit;
     // Record row r = t * grp + hh is query row t of the slot, head g * grp + hh.
     const int grp = a.group;
     const int rows = grp * a.n_q;
@@ -1055,10 +1056,9 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
     const uint8_t* vbase = a.v + (int64_t)g * a.v_hs;
     unsigned char* vst = smem + wave * 32 * VSTR;
     const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-    const int64_t tile_end = (int64_t)t1 * kTile;
-    const int64_t pos_end = tile_end < sa.n ? tile_end : sa.n;
-    const int64_t base0 = (int64_t)t0 * kTile;
-    const int n_steps = t1 - t0;  // one 32-cell step of every tile per wave
+    const int64_t pos_end = span_end < sa.n ? span_end : sa.n;
+    // one step per 128 positions: 32 cells per wave
+    const int n_steps = pos_end > base0 ? (int)((pos_end - base0 + kTile - 1) / kTile) : 0;
 
     // Cells of a step: lane li owns cell li of the wave's two 16-cell blocks.
     // Loads never branch: an invalid cell reads row 0 of the cache instead,
@@ -1350,6 +1350,15 @@ int launch_mfma(const SplitArgs& a, void* stream) {
     return (int)hipGetLastError();
 }
 
+// Vector-ALU instances exist only where the picker can select them.
+template <int D, int G, int KT, int VT>
+SplitLaunchFn valu_fn() {
+    if constexpr (uses_matrix_cores(G, 1, D))
+        return nullptr;
+    else
+        return &launch_valu<D, G, KT, VT>;
+}
+
 // The instance for (G, n_q) at one head_dim and pair of storage kinds: the
 // VALU kernel for one query row and G <= 5 (any G for head_dim 64), else the
 // matrix-core kernel with 8- or 16-row records (G * n_q <= 16).
@@ -1359,14 +1368,14 @@ SplitLaunchFn pick_g(int g, int n_q) {
     if (!uses_matrix_cores(g, n_q, D)) {
         if (n_q != 1) return nullptr;
         switch (g) {
-            case 1: return &launch_valu<D, 1, KT, VT>;
-            case 2: return &launch_valu<D, 2, KT, VT>;
-            case 3: return &launch_valu<D, 3, KT, VT>;
-            case 4: return &launch_valu<D, 4, KT, VT>;
-            case 5: return &launch_valu<D, 5, KT, VT>;
-            case 6: return &launch_valu<D, 6, KT, VT>;
-            case 7: return &launch_valu<D, 7, KT, VT>;
-            case 8: return &launch_valu<D, 8, KT, VT>;
+            case 1: return valu_fn<D, 1, KT, VT>();
+            case 2: return valu_fn<D, 2, KT, VT>();
+            case 3: return valu_fn<D, 3, KT, VT>();
+            case 4: return valu_fn<D, 4, KT, VT>();
+            case 5: return valu_fn<D, 5, KT, VT>();
+            case 6: return valu_fn<D, 6, KT, VT>();
+            case 7: return valu_fn<D, 7, KT, VT>();
+            case 8: return valu_fn<D, 8, KT, VT>();
             default: return nullptr;
         }
     }

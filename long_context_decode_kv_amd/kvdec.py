@@ -42,7 +42,7 @@ class Problem(ctypes.Structure):
         ("cell_begin", _p), ("n_occupied", _p), ("cells", _p), ("cells_off", _p),
         ("tail_begin", _p), ("n_tail", _p),
         ("tail_capacity_cells", _i64), ("tail_chunk_cells", _i64),
-        ("tail_ring_depth", _i32), ("n_queries", _i32), ("tail_zero_copy", _i32), ("reserved", _i32),
+        ("tail_ring_depth", _i32), ("n_queries", _i32), ("tail_zero_copy", _i32), ("split_cells", _i32),
         ("max_records", _p),
     ]
 
@@ -66,7 +66,7 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [
         ("n_slots", _i32), ("group", _i32), ("n_workgroups", _i32), ("tiles_per_split", _i32),
         ("n_tiles", _i64), ("n_entries", _i64), ("n_tail_chunks", _i64), ("workspace_bytes", _i64),
-        ("n_queries", _i32), ("matrix_cores", _i32),
+        ("n_queries", _i32), ("matrix_cores", _i32), ("split_cells", _i32), ("split_unit", _i32),
     ]
 
 
@@ -162,7 +162,7 @@ class Plan:
         return entries[:n.value], offsets
 
     def splits(self):
-        """int64 [n_workgroups, 4]: (slot, kv head, first tile, tile count)."""
+        """int64 [n_workgroups, 4]: (slot, kv head, first position, position count)."""
         n = _i64()
         _check(lib.kvdec_plan_splits(self._h, None, ctypes.byref(n)), "kvdec_plan_splits")
         out = np.empty((max(n.value, 1), 4), dtype=np.int64)
@@ -184,7 +184,7 @@ class Plan:
 def plan(n_q_heads, n_kv_heads, head_dim, n_slots, capacity_cells, *, k_type=F16, v_type=F16, scale=None,
          n_occupied=None, cell_begin=None, cells=None, n_tail=None, tail_begin=None, tail_capacity_cells=0,
          tail_chunk_cells=0, tail_ring_depth=0, tiles_per_split=0, n_cu=0, n_queries=1, tail_zero_copy=False,
-         max_records=None):
+         max_records=None, split_cells=0):
     """Build a plan.  ``cells`` is a list of per-slot raw cell arrays
     (indirect mode); otherwise ``n_occupied`` (and optional ``cell_begin``)
     give contiguous ranges.  ``n_queries`` query rows per slot.  ``n_cu=0``
@@ -203,6 +203,7 @@ def plan(n_q_heads, n_kv_heads, head_dim, n_slots, capacity_cells, *, k_type=F16
     p.k_type, p.v_type = k_type, v_type
     p.scale = (1.0 / np.sqrt(head_dim)) if scale is None else scale
     p.tiles_per_split = tiles_per_split
+    p.split_cells = split_cells
     p.capacity_cells = capacity_cells
     p.cell_begin = arr64(cell_begin)
     p.n_occupied = arr64(n_occupied)

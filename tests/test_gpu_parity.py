@@ -72,6 +72,22 @@ def test_long_f16_splits(K, d, g, indirect):
     check(*c.run(K, tiles_per_split=9), *c.oracle())
 
 
+@pytest.mark.parametrize("split_cells", [32, 96, 224, 608])
+@pytest.mark.parametrize("kind,d,g", [(O.F16, 128, 4), (O.Q8_B32, 128, 2), (O.Q4_B32, 64, 4), (O.F16, 256, 8),
+                                      (O.Q8_B32, 256, 6)])
+def test_split_boundaries_inside_tiles(K, split_cells, kind, d, g):
+    """Splits of 32-cell multiples end inside 128-cell tiles on the
+    vector-ALU kernel (whole tiles on the matrix-core kernel); contiguous
+    and indirect slots with holes."""
+    c = Case(70 + split_cells % 97 + d + g + kind, 2 * g, 2, d, kind=kind, occupied=[3000, 77, 1000])
+    p = c.plan(K, split_cells=split_cells)
+    assert p.info()["split_unit"] == (128 if p.info()["matrix_cores"] else 32)
+    check(*c.run(K, plan=p), *c.oracle())
+    ci = Case(71 + split_cells % 97 + d + g + kind, 2 * g, 2, d, kind=kind, indirect_lengths=[2500, 129, 1],
+              shuffle=True, duplicates=5)
+    check(*ci.run(K, split_cells=split_cells), *ci.oracle())
+
+
 @pytest.mark.parametrize("kind", [O.Q8_B32, O.Q4_B32])
 def test_quantized_indirect_interleaved(K, kind):
     """GQA-6, head_dim 256, four slots whose 128-cell records are interleaved,

@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
     for name in names:
         assert hasattr(K.lib, name), name
     assert set(names) == set(K.EXPORTED)
-    assert K.version() == 10300
+    assert K.version() == 10400
 
 
 def test_probe_library_exports_and_rejects_bad_arguments():
@@ -93,35 +93,60 @@ def test_compact_plan_gqa6_workload_shape():
     assert list(np.diff(off) // 128) == [1024, 512, 157, 7]
 
 
-def _coverage(p, tiles_per_slot, n_kv):
+def _coverage(p, n_per_slot, n_kv):
+    """The split table covers every position [0, n) of every (slot, KV head)
+    exactly once, in contiguous ascending pieces."""
     sp = p.splits()
     seen = {}
-    for s, g, t0, nt in sp:
-        for t in range(t0, t0 + nt):
+    for s, g, p0, n in sp:
+        for t in range(p0, p0 + n):
             key = (int(s), int(g), int(t))
             assert key not in seen
             seen[key] = 1
-    want = {(s, g, t) for s, T in enumerate(tiles_per_slot) for g in range(n_kv) for t in range(T)}
+    want = {(s, g, t) for s, n in enumerate(n_per_slot) for g in range(n_kv) for t in range(n)}
     assert set(seen) == want
     return sp
 
 
-@pytest.mark.parametrize("tps", [0, 1, 3, 1000])
-def test_split_table_covers_every_tile_once(tps):
+@pytest.mark.parametrize("tps,split_cells", [(0, 0), (1, 0), (3, 0), (1000, 0), (0, 96), (7, 32), (0, 4096)])
+def test_split_table_covers_every_position_once(tps, split_cells):
     occ = [13100, 0, 1, 128, 129, 40000]
-    p = K.plan(32, 8, 128, len(occ), 50000, n_occupied=occ, tiles_per_split=tps, n_cu=256)
-    tiles = [-(-n // 128) for n in occ]
-    sp = _coverage(p, tiles, 8)
-    # splits of one (slot, head) differ by at most one tile
+    p = K.plan(32, 8, 128, len(occ), 50000, n_occupied=occ, tiles_per_split=tps, split_cells=split_cells,
+               n_cu=256)
+    sp = _coverage(p, occ, 8)
+    info = p.info()
+    unit = info["split_unit"]
+    assert unit == 32  # vector-ALU kernel
+    want = split_cells or 128 * tps
     for s in range(len(occ)):
         for g in range(8):
-            counts = [int(r[3]) for r in sp if r[0] == s and r[1] == g]
-            assert max(counts) - min(counts) <= 1
-            if tps:
-                assert max(counts) <= max(tps, 1) or tiles[s] == 0
-    info = p.info()
+            rows = [r for r in sp if r[0] == s and r[1] == g]
+            # boundaries on multiples of the unit; pieces differ by at most one unit
+            assert all(int(r[2]) % unit == 0 for r in rows)
+            counts = [int(r[3]) for r in rows[:-1]]
+            if counts:
+                assert max(counts) - min(counts) <= unit
+            if want:
+                assert max(int(r[3]) for r in rows) <= max(want, unit)
     assert info["n_workgroups"] == len(sp)
-    assert info["n_tiles"] == sum(tiles) * 8
+    assert info["n_tiles"] == sum(-(-n // 128) for n in occ) * 8
+    assert info["split_cells"] == max(int(r[3]) for r in sp)
+
+
+def test_matrix_core_splits_are_whole_tiles():
+    occ = [9000, 300]
+    p = K.plan(24, 4, 256, 2, 20000, k_type=K.Q8_B32, v_type=K.Q8_B32, n_occupied=occ, cell_begin=[0, 10000],
+               split_cells=160, n_cu=256)
+    info = p.info()
+    assert info["matrix_cores"] == 1 and info["split_unit"] == 128 and info["split_cells"] == 256
+    sp = _coverage(p, occ, 4)
+    assert all(int(r[2]) % 128 == 0 for r in sp)
+
+
+@pytest.mark.parametrize("bad", [-32, 48, 1])
+def test_split_cells_must_be_multiple_of_32(bad):
+    with pytest.raises(K.KvdecError):
+        K.plan(32, 8, 128, 1, 4096, n_occupied=[4096], split_cells=bad)
 
 
 def test_auto_split_fills_device():
