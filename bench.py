@@ -142,6 +142,8 @@ def algorithmic_bytes(n_cells_attended, hkv, d, kind, n_slots, hq, plan_entries=
 
 
 class ContiguousModel(Workload):
+    split_cells = 0  # planner's choice unless --split-cells
+
     def __init__(self, name, layers, hq, hkv, d, capacity, occupied, n_q=1):
         self.name, self.layers, self.hq, self.hkv, self.d = name, layers, hq, hkv, d
         self.capacity, self.occupied, self.kind, self.n_q = capacity, occupied, 0, n_q
@@ -150,6 +152,8 @@ class ContiguousModel(Workload):
         c = {"workload": self.name, "layers": self.layers, "q_heads": self.hq, "kv_heads": self.hkv,
              "head_dim": self.d, "cells_occupied": self.occupied, "cells_capacity": self.capacity,
              "batch": 1, "kv_dtype": "f16", "cells_per_tile": 128}
+        if self.split_cells:
+            c["split_cells"] = self.split_cells
         if self.n_q > 1:
             c.update({"query_rows_per_slot": self.n_q, "mask": "causal: row t at the position of occupied cell "
                                                                 "n - n_q + t (speculative verification)"})
@@ -171,7 +175,7 @@ class ContiguousModel(Workload):
             if layer % 8 == 7:
                 log(f"  generated {layer + 1}/{self.layers} layers")
         self.plan = K.plan(self.hq, self.hkv, self.d, 1, self.capacity, n_occupied=[self.occupied],
-                           n_queries=self.n_q)
+                           n_queries=self.n_q, split_cells=self.split_cells)
         self.ws = K.workspace(self.plan)
         self.q_pos = None
         if self.n_q > 1:
@@ -419,6 +423,7 @@ class ContiguousModelOneLaunch(ContiguousModel):
         self.out = [torch.empty(L, self.hq, self.d, device="cuda")]
         self.lse = [torch.empty(L, self.hq, device="cuda")]
         self.plan = K.plan(self.hq, self.hkv, self.d, L, L * cap, n_occupied=[self.occupied] * L,
+                           split_cells=self.split_cells,
                            cell_begin=[layer * cap for layer in range(L)])
         self.ws = K.workspace(self.plan)
         self.q_pos = None
@@ -486,6 +491,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-ceiling", action="store_true", help="skip the streaming-read ceiling (profiling runs)")
+    ap.add_argument("--split-cells", type=int, default=0,
+                    help="cells per split for the contiguous-model workloads (multiple of 32; 0: planner)")
     ap.add_argument("--tail-chunk", type=int, default=0,
                     help="host-tail cells per chunk (rolling workloads; 0: 8192 staged, whole tail otherwise)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -509,6 +516,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     RollingWindow.chunk = args.tail_chunk
+    ContiguousModel.split_cells = args.split_cells
     wl = WORKLOADS[args.workload]()
     log(f"[bench] workload {wl.name}: generating inputs on the device")
     wl.setup(K, torch, 1001)
