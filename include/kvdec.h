@@ -314,6 +314,7 @@ typedef struct kvdec_plan_info {
     int32_t matrix_cores;     /* 1: served by the matrix-core kernel */
     int32_t split_cells;      /* largest position count of any split */
     int32_t split_unit;       /* split boundaries fall on multiples of this many positions */
+    int32_t waves;            /* waves per workgroup of the resident launch (4 or 8) */
 } kvdec_plan_info;
 
 int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info);

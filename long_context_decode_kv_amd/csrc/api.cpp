@@ -42,6 +42,7 @@ void common_args(const kvdec_plan_t& p, const kvdec_io& io, kvdec::SplitArgs& a)
     a.n_q = p.n_q;
     a.group = p.group;
     a.split_unit = p.split_unit;
+    a.waves = p.waves;
     // positions are used with several query rows per slot only
     a.q_pos = p.n_q > 1 ? io.q_pos : nullptr;
     a.cell_pos = p.n_q > 1 ? io.cell_pos : nullptr;
@@ -129,6 +130,7 @@ int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info) {
     info->matrix_cores = kvdec::uses_matrix_cores(plan->group, plan->n_q, plan->head_dim) ? 1 : 0;
     info->split_cells = plan->max_split_cells;
     info->split_unit = plan->split_unit;
+    info->waves = plan->waves;
     return KVDEC_OK;
 }
 
@@ -376,6 +378,7 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
             t.slot[0].n = nc;
             t.slot[0].n_units = tiles;  // whole-tile splits
             t.split_unit = kvdec::kTile;
+            t.waves = 4;
             t.slot[0].n_splits = splits;
             t.slot[0].wg_begin = 0;
             t.slot[0].part_begin = 0;

@@ -237,6 +237,21 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
             tps = wgs_one <= n_cu ? one : std::max<int64_t>(8, ceil_div(total_tiles, 8 * (int64_t)n_cu));
         }
         ups = tps * upt;
+        // Short contexts (splits of at most two steps at two workgroups per
+        // compute unit): one eight-wave workgroup per compute unit instead,
+        // each split exactly two of its steps.  The same waves are in flight,
+        // and a (slot, KV head) leaves half as many records to merge.
+        const int64_t step4 = 4 * (64 / (p.head_dim / 16)) * 4;  // cells per 4-wave step (G <= 5)
+        if (staged && p.head_dim <= 128 && group <= 5 && tps * kTile <= 2 * step4) {
+            const int64_t cells8 = 2 * 2 * step4;  // two 8-wave steps
+            const int64_t ups8 = cells8 / unit;
+            int64_t wgs8 = 0;
+            for (auto& sa : plan.slots) wgs8 += std::max<int64_t>(1, ceil_div((int64_t)sa.n_units, ups8)) * p.n_kv_heads;
+            if (4 * wgs8 >= 3 * (int64_t)n_cu && wgs8 <= n_cu) {
+                plan.waves = 8;
+                ups = ups8;
+            }
+        }
     }
     int64_t wgs = 0;
     plan.max_tiles_per_split = 0;

@@ -297,23 +297,24 @@ struct RowMap {
 // residue class); the running maximum and sums per head are kept in LDS
 // across chunks.  The result goes to the outputs (dest < 0) or, merged but
 // not normalised, to record `dest` (a cluster record).
-template <int D, int G>
+template <int D, int G, int NT = kThreads>
 __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMap& rm, int64_t rec0, int count,
                               int64_t dest) {
     constexpr int NV = G * D / 4;                           // float4 columns of o
-    constexpr int TS = NV >= kThreads ? 1 : kThreads / NV;  // threads per column
-    constexpr int COLS = (NV + kThreads - 1) / kThreads;    // columns per thread
-    constexpr int UB = COLS == 1 ? 32 : 32 / COLS;          // records per thread per chunk
+    constexpr int TS = NV >= NT ? 1 : NT / NV;              // threads per column
+    constexpr int COLS = (NV + NT - 1) / NT;                // columns per thread
     constexpr int SPC = merge_chunk(D, G);                  // records per chunk (one per lane)
-    static_assert(SPC == (64 < UB * TS ? 64 : UB * TS), "merge chunk");
+    constexpr int UB = (SPC + TS - 1) / TS;                 // records per thread per chunk
+    static_assert(SPC <= 64 && UB * COLS <= 32, "merge chunk");
+    constexpr int NW = NT / 64;                             // waves
     __shared__ float f_m[64 * G];
     __shared__ float run_m[G], run_l[G], scale_old[G];
-    __shared__ float4 red[TS > 1 ? kThreads : 1];
+    __shared__ float4 red[TS > 1 ? NT : 1];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int col = tid % (NV < kThreads ? NV : kThreads);
-    const int cls = tid / (NV < kThreads ? NV : kThreads);  // threads with cls >= TS idle
+    const int col = tid % (NV < NT ? NV : NT);
+    const int cls = tid / (NV < NT ? NV : NT);  // threads with cls >= TS idle
     const __amdgpu_buffer_rsrc_t rs = part_rsrc(a);
     const int n_splits = count;
 
@@ -329,7 +330,7 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMa
         float4 x[COLS][UB];
 #pragma unroll
         for (int c = 0; c < COLS; ++c) {
-            const int v = col + c * kThreads;
+            const int v = col + c * NT;
 #pragma unroll
             for (int u = 0; u < UB; ++u) {
                 const int sp = cls + u * TS;
@@ -338,13 +339,13 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMa
                               : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
-        // (m, l) of the chunk: wave w takes record rows w, w + 4, w + 8, ...,
-        // one split per lane.
-        constexpr int HW = (G + 3) / 4;  // record rows per wave
+        // (m, l) of the chunk: wave w takes record rows w, w + NW, w + 2 NW,
+        // ..., one split per lane.
+        constexpr int HW = (G + NW - 1) / NW;  // record rows per wave
         float mv[HW], lv[HW];
 #pragma unroll
         for (int hh = 0; hh < HW; ++hh) {
-            const int h = wave + 4 * hh;
+            const int h = wave + NW * hh;
             mv[hh] = kNegInf;
             lv[hh] = 0.f;
             if (h < G && lane < nsp) {
@@ -355,7 +356,7 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMa
         __syncthreads();  // the previous chunk is done with f_m / scale_old
 #pragma unroll
         for (int hh = 0; hh < HW; ++hh) {
-            const int h = wave + 4 * hh;
+            const int h = wave + NW * hh;
             if (h >= G) continue;  // uniform over the wave
             const float mo = run_m[h];
             const float mn = fmaxf(mo, wave_max(mv[hh]));
@@ -372,7 +373,7 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMa
         __syncthreads();
 #pragma unroll
         for (int c = 0; c < COLS; ++c) {
-            const int v = col + c * kThreads;
+            const int v = col + c * NT;
             if (cls >= TS || v >= NV) continue;
             const int h = (4 * v) / D;
             const float so = scale_old[h];
@@ -412,7 +413,7 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMa
     if (cls == 0) {
 #pragma unroll
         for (int c = 0; c < COLS; ++c) {
-            const int v = col + c * kThreads;
+            const int v = col + c * NT;
             if (v >= NV) continue;
             const int h = (4 * v) / D;
             const int d0 = 4 * v - h * D;
@@ -450,7 +451,7 @@ __device__ __forceinline__ bool last_arrival(uint32_t* ticket, int expected, int
 // stream and head) into the split's result; a single-split group writes its
 // output directly, otherwise the split's record is published and the last
 // workgroup of the (slot, KV head) merges all records.
-template <int D, int G, int NS, int DP>
+template <int D, int G, int NS, int DP, int NT = kThreads>
 __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& sa, int s, int g, int split,
                                              const RowMap& rm, const float (*sm_m)[G], const float (*sm_l)[G],
                                              const float (*sm_o)[G][DP], int& sm_last) {
@@ -461,7 +462,7 @@ __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& 
     const bool single = (n_splits == 1);
     const int64_t rec = sa.part_begin + (int64_t)g * n_splits + split;
     const __amdgpu_buffer_rsrc_t rs = part_rsrc(a);
-    for (int v = tid; v < NV; v += kThreads) {
+    for (int v = tid; v < NV; v += NT) {
         const int h = (4 * v) / D, d0 = 4 * v - h * D;
         float M = kNegInf;
 #pragma unroll
@@ -503,7 +504,7 @@ __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& 
     if (ncl <= 1) {
         // the last workgroup of the (slot, KV head) merges every split
         if (!last_arrival(gticket, n_splits, sm_last)) return;
-        merge_records<D, G>(a, sa, rm, srec0, n_splits, -1);
+        merge_records<D, G, NT>(a, sa, rm, srec0, n_splits, -1);
         return;
     }
     // two levels: the last of each cluster of splits merges the cluster into
@@ -514,18 +515,19 @@ __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& 
     const int cn = (n_splits - c0) < CH ? (n_splits - c0) : CH;
     const int64_t cidx = sa.cl_begin + (int64_t)g * ncl + cid;
     if (!last_arrival(a.ctickets + cidx, cn, sm_last)) return;
-    merge_records<D, G>(a, sa, rm, srec0 + c0, cn, a.crec_base + cidx);
+    merge_records<D, G, NT>(a, sa, rm, srec0 + c0, cn, a.crec_base + cidx);
     wait_stores();
     __syncthreads();
     if (!last_arrival(gticket, ncl, sm_last)) return;
-    merge_records<D, G>(a, sa, rm, a.crec_base + sa.cl_begin + (int64_t)g * ncl, ncl, -1);
+    merge_records<D, G, NT>(a, sa, rm, a.crec_base + sa.cl_begin + (int64_t)g * ncl, ncl, -1);
 }
 
 
-template <int D, int G, int KT, int VT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void split_kernel(const SplitArgs a) {
+template <int D, int G, int KT, int VT, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void split_kernel(const SplitArgs a) {
     using Gm = Geo<D, G>;
-    constexpr int DL = Gm::DL, R = Gm::R, CPW = Gm::CPW, NCW = Gm::NB, STEP = Gm::STEP;
+    constexpr int DL = Gm::DL, R = Gm::R, CPW = Gm::CPW, NCW = Gm::NB;
+    constexpr int STEP = W * CPW * NCW;  // cells per workgroup step (W waves)
     using FK = Fmt<KT, DL>;
     using FV = Fmt<VT, DL>;
     constexpr int NCK = DL / FK::EPC;  // K chunks per lane per cell
@@ -535,7 +537,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // Cell streams per wave left after the in-register (DPP) merge step.
     constexpr bool kDppStep = R <= 8;
     constexpr int NSW = kDppStep ? CPW / 2 : CPW;
-    constexpr int NS = 4 * NSW;        // streams per workgroup merged through LDS
+    constexpr int NS = W * NSW;        // streams per workgroup merged through LDS
 
     __shared__ float sm_m[NS][G];
     __shared__ float sm_l[NS][G];
@@ -546,7 +548,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // stream merge after the loop.
     constexpr bool kDma = KT == KVDEC_F16 && VT == KVDEC_F16;
     constexpr int kMergeBytes = NS * G * (D + 16) * 4;
-    constexpr int kDmaBytes = kDma ? 4 * 64 * NCW * (NCK + NCV) * 16 : 0;
+    constexpr int kDmaBytes = kDma ? W * 64 * NCW * (NCK + NCV) * 16 : 0;
     __shared__ __align__(16) unsigned char lds_raw[kMergeBytes > kDmaBytes ? kMergeBytes : kDmaBytes];
     // stream stride padded by 16 floats: streams written by one instruction land in different banks
     float (*sm_o)[G][D + 16] = reinterpret_cast<float (*)[G][D + 16]>(lds_raw);
@@ -892,7 +894,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     __syncthreads();
 
     const RowMap rm{row0, G, a.n_q_heads, G};
-    finish_split<D, G, NS, D + 16>(a, sa, s, g, split, rm, sm_m, sm_l, sm_o, sm_last);
+    finish_split<D, G, NS, D + 16, 64 * W>(a, sa, s, g, split, rm, sm_m, sm_l, sm_o, sm_last);
 }
 
 // ---------------------------------------------------------------------------
@@ -1335,7 +1337,16 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
 
 template <int D, int G, int KT, int VT>
 int launch_valu(const SplitArgs& a, void* stream) {
-    hipLaunchKernelGGL((split_kernel<D, G, KT, VT>), dim3(a.n_workgroups), dim3(kThreads), 0, (hipStream_t)stream, a);
+    // eight-wave workgroups: head_dim up to 128 (their stream-merge area fits LDS)
+    if constexpr (D <= 128 && KT == KVDEC_F16 && VT == KVDEC_F16) {
+        if (a.waves == 8) {
+            hipLaunchKernelGGL((split_kernel<D, G, KT, VT, 8>), dim3(a.n_workgroups), dim3(512), 0,
+                               (hipStream_t)stream, a);
+            return (int)hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((split_kernel<D, G, KT, VT, 4>), dim3(a.n_workgroups), dim3(kThreads), 0, (hipStream_t)stream,
+                       a);
     return (int)hipGetLastError();
 }
 

@@ -88,6 +88,18 @@ def test_split_boundaries_inside_tiles(K, split_cells, kind, d, g):
     check(*ci.run(K, split_cells=split_cells), *ci.oracle())
 
 
+@pytest.mark.parametrize("d,g,hkv,occ", [(128, 4, 8, [13100]), (128, 5, 8, [13100]), (128, 1, 8, [12000]),
+                                         (64, 2, 8, [26000]), (128, 3, 4, [900, 25000, 1])])
+def test_eight_wave_workgroups(K, d, g, hkv, occ):
+    """Short f16 contexts take one eight-wave workgroup per compute unit with
+    two-step splits (512 cells at head_dim 128); ragged last split, a slot
+    of one cell."""
+    c = Case(500 + d + g + len(occ), g * hkv, hkv, d, occupied=occ)
+    p = c.plan(K, n_cu=256)
+    assert p.info()["waves"] == 8
+    check(*c.run(K, plan=p), *c.oracle())
+
+
 @pytest.mark.parametrize("kind", [O.Q8_B32, O.Q4_B32])
 def test_quantized_indirect_interleaved(K, kind):
     """GQA-6, head_dim 256, four slots whose 128-cell records are interleaved,

@@ -150,9 +150,19 @@ def test_split_cells_must_be_multiple_of_32(bad):
 
 
 def test_auto_split_fills_device():
+    p = K.plan(32, 8, 128, 1, 16384, n_occupied=[8192], n_cu=256)
+    info = p.info()
+    assert 256 <= info["n_workgroups"] <= 512 and info["waves"] == 4
+    # short f16 context: one eight-wave workgroup per compute unit at most,
+    # each split two of its 256-cell steps
     p = K.plan(32, 8, 128, 1, 16384, n_occupied=[13100], n_cu=256)
     info = p.info()
-    assert 256 <= info["n_workgroups"] <= 512
+    assert info["waves"] == 8 and info["n_workgroups"] == 208 and info["split_cells"] == 512
+    # not for quantized caches, explicit split sizes or head_dim 256
+    assert K.plan(32, 8, 128, 1, 16384, n_occupied=[13100], n_cu=256, split_cells=512).info()["waves"] == 4
+    assert K.plan(32, 8, 128, 1, 16384, k_type=K.Q8_B32, v_type=K.Q8_B32, n_occupied=[13100],
+                  n_cu=256).info()["waves"] == 4
+    assert K.plan(16, 8, 256, 1, 16384, n_occupied=[13100], n_cu=256).info()["waves"] == 4
     # long f16 splits on the vector-ALU kernel: one workgroup per compute unit
     p = K.plan(32, 8, 128, 1, 65536, n_occupied=[65536], n_cu=256)
     info = p.info()
