@@ -456,21 +456,28 @@ __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& 
                                              const RowMap& rm, const float (*sm_m)[G], const float (*sm_l)[G],
                                              const float (*sm_o)[G][DP], int& sm_last) {
     const int tid = threadIdx.x;
-    // Merge the NS streams: thread -> float4 column.  Result of this split in log2 units.
+    // Merge the NS streams: P adjacent threads per float4 column, each over
+    // every P-th stream, combined by lane shuffles.  Result of this split in
+    // log2 units.
     constexpr int NV = G * D / 4;
+    constexpr int PQ = NT / NV;
+    constexpr int P = (NS % 4 == 0 && PQ >= 4) ? 4 : ((NS % 2 == 0 && PQ >= 2) ? 2 : 1);
+    const int part = tid % P;
     const int n_splits = sa.n_splits;
     const bool single = (n_splits == 1);
     const int64_t rec = sa.part_begin + (int64_t)g * n_splits + split;
     const __amdgpu_buffer_rsrc_t rs = part_rsrc(a);
-    for (int v = tid; v < NV; v += NT) {
+    for (int v = tid / P; v < NV; v += NT / P) {
         const int h = (4 * v) / D, d0 = 4 * v - h * D;
         float M = kNegInf;
 #pragma unroll
-        for (int k = 0; k < NS; ++k) M = fmaxf(M, sm_m[k][h]);
+        for (int k = part; k < NS; k += P) M = fmaxf(M, sm_m[k][h]);
+#pragma unroll
+        for (int o = 1; o < P; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
         float L = 0.f;
         float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int k = 0; k < NS; ++k) {
+        for (int k = part; k < NS; k += P) {
             const float mk = sm_m[k][h];
             const float f = (mk == kNegInf) ? 0.f : exp2_fast(mk - M);
             const float4 ok = *reinterpret_cast<const float4*>(&sm_o[k][h][d0]);
@@ -480,6 +487,15 @@ __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& 
             O.z = fmaf(ok.z, f, O.z);
             O.w = fmaf(ok.w, f, O.w);
         }
+#pragma unroll
+        for (int o = 1; o < P; o <<= 1) {
+            L += __shfl_xor(L, o);
+            O.x += __shfl_xor(O.x, o);
+            O.y += __shfl_xor(O.y, o);
+            O.z += __shfl_xor(O.z, o);
+            O.w += __shfl_xor(O.w, o);
+        }
+        if (part != 0) continue;
         if (single) {
             if (rm.real(h)) {
                 merge_acc_in(a, rm.row(h), d0, D, M, L, O);
