@@ -630,12 +630,15 @@ def main():
                   f"{KIND[wl.kind]} K / {KIND[wl.v_kind]} V (f16 scale per 32)") + ", fp32 accumulate",
         "data": "synthetic: q ~ N(0,1); K, V ~ N(0,1) rounded to f16 or block-encoded; seeded on-device generator",
         "config": dict(wl.config(), mode=mode, workgroups_per_launch=info["n_workgroups"],
-                       tiles_per_split=info["tiles_per_split"]),
+                       tiles_per_split=info["tiles_per_split"], cells_per_split=info["split_cells"]),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": ("split_mfma_kernel<%d,rows %d,%s,%s>" if info.get("matrix_cores") else
-                                "split_kernel<%d,%d,%s,%s>") % (wl.d, wl.hq // wl.hkv * getattr(wl, "n_q", 1),
-                                                                KIND[wl.kind], KIND[getattr(wl, "v_kind", wl.kind)]),
+                     "kernel": (("split_mfma_kernel<%d,rows %d,%s,%s>" % (
+                         wl.d, wl.hq // wl.hkv * getattr(wl, "n_q", 1), KIND[wl.kind],
+                         KIND[getattr(wl, "v_kind", wl.kind)])) if info.get("matrix_cores") else
+                         ("split_kernel<%d,%d,%s,%s,%d waves>" % (wl.d, wl.hq // wl.hkv, KIND[wl.kind],
+                                                                  KIND[getattr(wl, "v_kind", wl.kind)],
+                                                                  info.get("waves", 4)))),
                      "algorithmic_bytes_per_launch": bytes_launch, "launches_per_step": launches_per_step,
                      "avg_launch_us": round(avg_us, 3), "isolated_launch_event_us": round(bracketed_us, 3),
                      "read_ceiling": ceiling},
