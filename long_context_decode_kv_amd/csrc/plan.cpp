@@ -222,14 +222,18 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
         ups = (int64_t)p.tiles_per_split * upt;
     } else {
         int64_t tps = std::max<int64_t>(1, ceil_div(total_tiles, 2 * (int64_t)n_cu));
-        // f16 caches on the vector-ALU kernel stage the next step of a long
-        // split through LDS, so one workgroup keeps enough bytes in flight
-        // for its compute unit. Once splits are eight tiles or longer: one
-        // split per compute unit when that covers every (slot, KV head),
+        // Once splits are eight tiles or longer: one split per compute unit
+        // when that covers every (slot, KV head) -- f16 caches on the
+        // vector-ALU kernel stage the next step of a long split through LDS,
+        // and the matrix-core kernel prefetches a step ahead, so one
+        // workgroup keeps enough bytes in flight for its compute unit (on
+        // the matrix-core kernel only for rows of 384 bytes or more per cell:
+        // 4-bit K and V measured 5% faster at two workgroups per unit) --
         // else about eight splits per compute unit, which the dispatcher
         // balances (a second partial round of long splits would leave most
         // of the chip idle at the end).
-        if (staged && tps >= 8) {
+        const bool heavy_rows = row_bytes(p.k_type, p.head_dim) + row_bytes(p.v_type, p.head_dim) >= 384;
+        if ((staged || (mfma && heavy_rows)) && tps >= 8) {
             const int64_t one = ceil_div(total_tiles, (int64_t)n_cu);
             int64_t wgs_one = 0;
             for (auto& sa : plan.slots)
