@@ -185,9 +185,10 @@ class ContiguousModel(Workload):
         K.attend(self.plan, self.q[layer], self.k[layer], self.v[layer], self.ws, out=self.out[layer],
                  lse=self.lse[layer], q_pos=self.q_pos)
 
-    def oracle_sample(self, budget_s):
+    def oracle_sample(self, budget_s, max_layers=None):
         """Time the float64 oracle on host copies of the workload's shape:
         whole layers until the budget is spent (at least one)."""
+        max_layers = max_layers or self.layers
         import numpy as np
         import oracle as O
         from long_context_decode_kv_amd import synth
@@ -206,8 +207,8 @@ class ContiguousModel(Workload):
                 O.decode_attention(q, regions, self.hkv, 1 / math.sqrt(self.d))
             done += 1
             el = time.perf_counter() - t0
-            if el >= budget_s or done >= self.layers:
-                return done, el, f"{done} of {self.layers} layers (full layer each: {self.occupied} cells x " \
+            if el >= budget_s or done >= max_layers:
+                return done, el, f"{done} of {max_layers} layers (full layer each: {self.occupied} cells x " \
                                  f"{self.hkv} KV heads x {self.hq} q heads)"
 
 
@@ -429,7 +430,7 @@ class ContiguousModelOneLaunch(ContiguousModel):
         self.q_pos = None
 
     def oracle_sample(self, budget_s):
-        done, el, sample = super().oracle_sample(budget_s)
+        done, el, sample = super().oracle_sample(budget_s, self.model_layers)
         return done / self.model_layers, el, sample
 
 
