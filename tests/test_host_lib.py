@@ -163,6 +163,12 @@ def test_auto_split_fills_device():
     assert K.plan(32, 8, 128, 1, 16384, k_type=K.Q8_B32, v_type=K.Q8_B32, n_occupied=[13100],
                   n_cu=256).info()["waves"] == 4
     assert K.plan(16, 8, 256, 1, 16384, n_occupied=[13100], n_cu=256).info()["waves"] == 4
+    # matrix-core kernel, short splits: two tiles double to four when that
+    # still gives at most one workgroup per compute unit
+    for hq, nq in ((48, 1), (32, 4)):
+        info = K.plan(hq, 8, 128, 1, 16384, n_occupied=[13100], n_queries=nq, n_cu=256).info()
+        assert info["matrix_cores"] == 1 and info["n_workgroups"] == 208 and info["tiles_per_split"] == 4
+    assert K.plan(48, 8, 128, 1, 16384, n_occupied=[8192], n_cu=256).info()["n_workgroups"] == 512
     # long f16 splits on the vector-ALU kernel: one workgroup per compute unit
     p = K.plan(32, 8, 128, 1, 65536, n_occupied=[65536], n_cu=256)
     info = p.info()
