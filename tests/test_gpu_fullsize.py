@@ -140,3 +140,46 @@ def test_rolling_window_ctx40960_layer(K):
                               8, 1 / math.sqrt(128))
     check(out.cpu().numpy(), lse.cpu().numpy(), *want)
     check(out.cpu().numpy(), lse.cpu().numpy(), ro.cpu().numpy(), rl.cpu().numpy(), tol=1e-4)
+
+
+def test_qwen3_8b_verify4_layer(K):
+    """Speculative verification on the Qwen3-8B layer: 4 query rows at
+    positions 13096..13099 (causal), 13100 cells, the benchmark's launch
+    (matrix-core kernel, four-tile splits); whole layer checked."""
+    import torch
+    cap, n, nq = 16384, 13100, 4
+    k = synth.device_f16_cache(2100, cap, 8, 128)
+    v = synth.device_f16_cache(2101, cap, 8, 128)
+    q = synth.device_q(2102, nq, 32, 128)
+    q_pos = torch.arange(n - nq, n, dtype=torch.int32, device="cuda")
+    p = K.plan(32, 8, 128, 1, cap, n_occupied=[n], n_queries=nq)
+    assert p.info()["matrix_cores"] == 1
+    out = torch.empty(nq, 32, 128, device="cuda")
+    lse = torch.empty(nq, 32, device="cuda")
+    K.attend(p, q, k, v, K.workspace(p), out=out, lse=lse, q_pos=q_pos)
+    torch.cuda.synchronize()
+    want_o, want_l = O.decode_attention_multi(q.cpu().numpy()[None], [((O.F16, bits(k), None), (O.F16, bits(v), None),
+                                                                       [np.arange(n)])], 8, 1 / math.sqrt(128),
+                                              np.arange(n - nq, n)[None])
+    check(out.cpu().numpy(), lse.cpu().numpy(), want_o[0], want_l[0])
+
+
+def test_qwen3_8b_36_slots_one_launch(K):
+    """The one-launch figure: all 36 layers as slots of one call (13100 of
+    16384 cells each, 2016 workgroups); slots 0, 17 and 35 checked whole."""
+    import torch
+    L, cap, n = 36, 16384, 13100
+    k = synth.device_f16_cache(2200, L * cap, 8, 128)
+    v = synth.device_f16_cache(2201, L * cap, 8, 128)
+    q = synth.device_q(2202, L, 32, 128)
+    p = K.plan(32, 8, 128, L, L * cap, n_occupied=[n] * L, cell_begin=[s * cap for s in range(L)])
+    out = torch.empty(L, 32, 128, device="cuda")
+    lse = torch.empty(L, 32, device="cuda")
+    K.attend(p, q, k, v, K.workspace(p), out=out, lse=lse)
+    torch.cuda.synchronize()
+    go, gl = out.cpu().numpy(), lse.cpu().numpy()
+    for s in (0, 17, 35):
+        kh, vh = bits(k[s * cap:(s + 1) * cap]), bits(v[s * cap:(s + 1) * cap])
+        wo, wl = O.decode_attention(q[s:s + 1].cpu().numpy(), [((O.F16, kh, None), (O.F16, vh, None), [np.arange(n)])],
+                                    8, 1 / math.sqrt(128))
+        check(go[s:s + 1], gl[s:s + 1], wo, wl)

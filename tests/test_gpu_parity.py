@@ -100,6 +100,16 @@ def test_eight_wave_workgroups(K, d, g, hkv, occ):
     check(*c.run(K, plan=p), *c.oracle())
 
 
+@pytest.mark.parametrize("hq,kind", [(48, O.F16), (64, O.F16), (48, O.Q8_B32)])
+def test_matrix_core_four_tile_splits(K, hq, kind):
+    """Wide groups on a 13100-cell layer: two-tile splits doubled to four
+    (208 workgroups at 256 CUs); ragged last split."""
+    c = Case(600 + hq + kind, hq, 8, 128, kind=kind, occupied=[13100])
+    p = c.plan(K, n_cu=256)
+    assert p.info()["matrix_cores"] == 1 and p.info()["tiles_per_split"] == 4
+    check(*c.run(K, plan=p), *c.oracle())
+
+
 @pytest.mark.parametrize("kind", [O.Q8_B32, O.Q4_B32])
 def test_quantized_indirect_interleaved(K, kind):
     """GQA-6, head_dim 256, four slots whose 128-cell records are interleaved,
