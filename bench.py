@@ -611,6 +611,13 @@ def main():
         cpu = {"value": round(bytes_launch * layers_done / el / 1e9, 4), "unit": "GB/s", "cores": threads,
                "kind": "oracle", "sample": sample + f"; {el:.1f} s float64 numpy on the host",
                "us_per_step_extrapolated": round(el / layers_done * wl.layers * 1e6, 1)}
+        # the same oracle on one thread, where one unit of the sample stays short
+        if el / layers_done * threads < 20.0:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                d1, e1, s1 = wl.oracle_sample(min(4.0, args.cpu_budget / 3))
+            cpu["value_1thread"] = round(bytes_launch * d1 / e1 / 1e9, 4)
+            cpu["sample_1thread"] = s1 + f"; {e1:.1f} s on 1 thread"
 
     res = {
         "metric": "decode-attention µs/step and effective KV GB/s (fraction of HBM peak)",
