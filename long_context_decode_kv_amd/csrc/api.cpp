@@ -127,7 +127,7 @@ int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info) {
     info->n_tail_chunks = plan->n_tail_chunks;
     info->workspace_bytes = (int64_t)plan->workspace_bytes;
     info->n_queries = plan->n_q;
-    info->matrix_cores = kvdec::uses_matrix_cores(plan->group, plan->n_q, plan->head_dim) ? 1 : 0;
+    info->matrix_cores = plan->mfma ? 1 : 0;
     info->split_cells = plan->max_split_cells;
     info->split_unit = plan->split_unit;
     info->waves = plan->waves;
@@ -202,7 +202,7 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
     if (p.n_q > 1 && (!io->q_pos || !aligned(io->q_pos, 4)))
         return fail(KVDEC_E_INVALID, "several query rows per slot need q_pos (device int32 [n_slots][n_queries])");
     if (!aligned(io->cell_pos, 4)) return fail(KVDEC_E_INVALID, "cell_pos must be 4-byte aligned");
-    if (!kvdec::split_instance_exists(D, p.group, p.n_q, p.k_type, p.v_type))
+    if (!kvdec::split_instance_exists(D, p.group, p.n_q, p.k_type, p.v_type, p.mfma))
         return fail(KVDEC_E_UNSUPPORTED, "no kernel for this configuration");
 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -237,7 +237,7 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
     }
 
     if (!p.has_tail) {
-        const int e = kvdec::launch_split(D, p.group, p.n_q, p.k_type, p.v_type, a, stream);
+        const int e = kvdec::launch_split(D, p.group, p.n_q, p.k_type, p.v_type, p.mfma, a, stream);
         if (e != hipSuccess) return device_fail((hipError_t)e, "split kernel launch");
         return KVDEC_OK;
     }
@@ -308,7 +308,7 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
             return device_fail(e, "stream ordering");
         }
     }
-    int le = kvdec::launch_split(D, p.group, p.n_q, p.k_type, p.v_type, a, stream);
+    int le = kvdec::launch_split(D, p.group, p.n_q, p.k_type, p.v_type, p.mfma, a, stream);
     if (le != hipSuccess) {
         destroy();
         return device_fail((hipError_t)le, "window kernel launch");
@@ -391,7 +391,7 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
             t.n_workgroups = splits * p.n_kv_heads;
             t.acc_in = acc[c % 2];
             t.acc_out = acc[(c + 1) % 2];
-            le = kvdec::launch_split(D, p.group, p.n_q, p.k_type, p.v_type, t, stream);
+            le = kvdec::launch_split(D, p.group, p.n_q, p.k_type, p.v_type, p.mfma, t, stream);
             if (le != hipSuccess) {
                 e = (hipError_t)le;
                 break;

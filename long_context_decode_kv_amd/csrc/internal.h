@@ -35,8 +35,12 @@ inline constexpr bool is_scaled(int type) { return type != KVDEC_F16; }
 constexpr bool uses_matrix_cores(int group, int n_q, int head_dim) {
     return (n_q > 1 || group >= 6) && head_dim >= 128;
 }
+// Rows of a split record on the matrix-core kernel (mfma) or the VALU kernel.
+constexpr int record_rows_of(bool mfma, int group, int n_q) {
+    return mfma ? (group * n_q <= 8 ? 8 : 16) : group;
+}
 constexpr int record_rows(int group, int n_q, int head_dim) {
-    return uses_matrix_cores(group, n_q, head_dim) ? (group * n_q <= 8 ? 8 : 16) : group;
+    return record_rows_of(uses_matrix_cores(group, n_q, head_dim), group, n_q);
 }
 
 // Split records one merge round reads: a merging workgroup issues the loads
@@ -150,15 +154,16 @@ int launch_build_cells(const BuildArgs& a, void* stream);
 // Per pair of storage kinds, the launcher of the split-kernel instance for
 // (head_dim, group), or null.
 using SplitLaunchFn = int (*)(const SplitArgs&, void*);
-SplitLaunchFn pick_split_f16(int head_dim, int group, int n_q);
-SplitLaunchFn pick_split_q8(int head_dim, int group, int n_q);
-SplitLaunchFn pick_split_q4(int head_dim, int group, int n_q);
-SplitLaunchFn pick_split_f16_q8(int head_dim, int group, int n_q);
-SplitLaunchFn pick_split_f16_q4(int head_dim, int group, int n_q);
-SplitLaunchFn pick_split_q8_q4(int head_dim, int group, int n_q);
-int launch_split(int head_dim, int group, int n_q, int k_type, int v_type, const SplitArgs& a, void* stream);
+SplitLaunchFn pick_split_f16(int head_dim, int group, int n_q, bool mfma);
+SplitLaunchFn pick_split_q8(int head_dim, int group, int n_q, bool mfma);
+SplitLaunchFn pick_split_q4(int head_dim, int group, int n_q, bool mfma);
+SplitLaunchFn pick_split_f16_q8(int head_dim, int group, int n_q, bool mfma);
+SplitLaunchFn pick_split_f16_q4(int head_dim, int group, int n_q, bool mfma);
+SplitLaunchFn pick_split_q8_q4(int head_dim, int group, int n_q, bool mfma);
+int launch_split(int head_dim, int group, int n_q, int k_type, int v_type, bool mfma, const SplitArgs& a,
+                 void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
-bool split_instance_exists(int head_dim, int group, int n_q, int k_type, int v_type);
+bool split_instance_exists(int head_dim, int group, int n_q, int k_type, int v_type, bool mfma);
 
 }  // namespace kvdec
 
@@ -179,6 +184,7 @@ struct kvdec_plan {
     int32_t split_unit = 0;        // positions per split unit: 32 (vector-ALU kernel) or 128
     int32_t max_split_cells = 0;   // largest split, in positions
     int32_t waves = 4;             // waves per vector-ALU workgroup (4 or 8)
+    bool mfma = false;             // served by the matrix-core kernel
     int64_t n_tiles = 0;
     std::vector<int32_t> cells;      // indirect entries (host-built plans)
     std::vector<int64_t> cells_off;  // [n_slots + 1]

@@ -38,24 +38,25 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
 
 }  // namespace
 
-SplitLaunchFn pick_split(int head_dim, int g, int n_q, int kt, int vt) {
+SplitLaunchFn pick_split(int head_dim, int g, int n_q, int kt, int vt, bool mfma) {
     // K stored at least as finely as V: f16/f16, int8/int8, 4-bit/4-bit,
     // f16/int8, f16/4-bit, int8/4-bit.
-    if (kt == KVDEC_F16 && vt == KVDEC_F16) return pick_split_f16(head_dim, g, n_q);
-    if (kt == KVDEC_Q8_B32 && vt == KVDEC_Q8_B32) return pick_split_q8(head_dim, g, n_q);
-    if (kt == KVDEC_Q4_B32 && vt == KVDEC_Q4_B32) return pick_split_q4(head_dim, g, n_q);
-    if (kt == KVDEC_F16 && vt == KVDEC_Q8_B32) return pick_split_f16_q8(head_dim, g, n_q);
-    if (kt == KVDEC_F16 && vt == KVDEC_Q4_B32) return pick_split_f16_q4(head_dim, g, n_q);
-    if (kt == KVDEC_Q8_B32 && vt == KVDEC_Q4_B32) return pick_split_q8_q4(head_dim, g, n_q);
+    if (kt == KVDEC_F16 && vt == KVDEC_F16) return pick_split_f16(head_dim, g, n_q, mfma);
+    if (kt == KVDEC_Q8_B32 && vt == KVDEC_Q8_B32) return pick_split_q8(head_dim, g, n_q, mfma);
+    if (kt == KVDEC_Q4_B32 && vt == KVDEC_Q4_B32) return pick_split_q4(head_dim, g, n_q, mfma);
+    if (kt == KVDEC_F16 && vt == KVDEC_Q8_B32) return pick_split_f16_q8(head_dim, g, n_q, mfma);
+    if (kt == KVDEC_F16 && vt == KVDEC_Q4_B32) return pick_split_f16_q4(head_dim, g, n_q, mfma);
+    if (kt == KVDEC_Q8_B32 && vt == KVDEC_Q4_B32) return pick_split_q8_q4(head_dim, g, n_q, mfma);
     return nullptr;
 }
 
-bool split_instance_exists(int head_dim, int group, int n_q, int k_type, int v_type) {
-    return pick_split(head_dim, group, n_q, k_type, v_type) != nullptr;
+bool split_instance_exists(int head_dim, int group, int n_q, int k_type, int v_type, bool mfma) {
+    return pick_split(head_dim, group, n_q, k_type, v_type, mfma) != nullptr;
 }
 
-int launch_split(int head_dim, int group, int n_q, int k_type, int v_type, const SplitArgs& a, void* stream) {
-    SplitLaunchFn f = pick_split(head_dim, group, n_q, k_type, v_type);
+int launch_split(int head_dim, int group, int n_q, int k_type, int v_type, bool mfma, const SplitArgs& a,
+                 void* stream) {
+    SplitLaunchFn f = pick_split(head_dim, group, n_q, k_type, v_type, mfma);
     if (!f) return (int)hipErrorInvalidValue;
     return f(a, stream);
 }

@@ -114,13 +114,13 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
         return KVDEC_E_INVALID;
     }
     const int n_q = p.n_queries ? p.n_queries : 1;
-    if (!split_instance_exists(p.head_dim, group, n_q, p.k_type, p.v_type)) {
+    if (!split_instance_exists(p.head_dim, group, n_q, p.k_type, p.v_type,
+                               uses_matrix_cores(group, n_q, p.head_dim))) {
         err = "no kernel for this (head_dim, group, n_queries, k_type, v_type): groups above 8 and several "
               "query rows need head_dim 128 or 256 and G * n_queries <= 16, and K is stored at least as "
               "finely as V";
         return KVDEC_E_UNSUPPORTED;
     }
-    const int rec_rows = record_rows(group, n_q, p.head_dim);
 
     plan.n_q_heads = p.n_q_heads;
     plan.n_kv_heads = p.n_kv_heads;
@@ -128,7 +128,6 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
     plan.n_slots = p.n_slots;
     plan.group = group;
     plan.n_q = n_q;
-    plan.rec_rows = rec_rows;
     plan.k_type = p.k_type;
     plan.v_type = p.v_type;
     plan.scale = p.scale;
@@ -195,7 +194,30 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
     // about two workgroups per compute unit.  Split boundaries fall on
     // multiples of 32 positions for the vector-ALU kernel (a split may end
     // inside a tile), on whole tiles for the matrix-core kernel.
-    const bool mfma = uses_matrix_cores(group, n_q, p.head_dim);
+    bool mfma = uses_matrix_cores(group, n_q, p.head_dim);
+    int64_t total_tiles = 0;
+    for (auto& sa : plan.slots) {
+        const int64_t t = ceil_div(sa.n, kTile);
+        if (t > (1 << 24)) {
+            err = "slot too long";
+            return KVDEC_E_UNSUPPORTED;
+        }
+        total_tiles += t * p.n_kv_heads;
+    }
+    // Five f16 query rows at head_dim 128 over short contexts (splits of at
+    // most two tiles at two workgroups per CU) run faster on the matrix-core
+    // kernel with four-tile splits (16384-cell layer 22.6 -> 20.8 us); long
+    // splits stay on the vector-ALU kernel, whose LDS staging wins there.
+    if (!mfma && group == 5 && n_q == 1 && p.head_dim == 128 && p.k_type == KVDEC_F16 &&
+        p.v_type == KVDEC_F16 && p.split_cells == 0 && p.tiles_per_split == 0 &&
+        ceil_div(total_tiles, 2 * (int64_t)n_cu) <= 2) {
+        int64_t wgs4 = 0;
+        for (auto& sa : plan.slots) wgs4 += std::max<int64_t>(1, ceil_div(sa.n, 4 * (int64_t)kTile)) * p.n_kv_heads;
+        if (4 * wgs4 >= 3 * (int64_t)n_cu && wgs4 <= n_cu) mfma = true;
+    }
+    plan.mfma = mfma;
+    const int rec_rows = record_rows_of(mfma, group, n_q);
+    plan.rec_rows = rec_rows;
     const bool staged = p.k_type == KVDEC_F16 && p.v_type == KVDEC_F16 && !mfma;
     const int64_t unit = mfma ? kTile : kSplitUnit;
     const int64_t upt = kTile / unit;  // units per tile
@@ -204,16 +226,7 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
         err = "split_cells must be a non-negative multiple of 32";
         return KVDEC_E_INVALID;
     }
-    int64_t total_tiles = 0;
-    for (auto& sa : plan.slots) {
-        const int64_t t = ceil_div(sa.n, kTile);
-        if (t > (1 << 24)) {
-            err = "slot too long";
-            return KVDEC_E_UNSUPPORTED;
-        }
-        sa.n_units = (int32_t)ceil_div(sa.n, unit);
-        total_tiles += t * p.n_kv_heads;
-    }
+    for (auto& sa : plan.slots) sa.n_units = (int32_t)ceil_div(sa.n, unit);
     plan.n_tiles = total_tiles;
     int64_t ups = 0;  // units per split
     if (p.split_cells > 0) {

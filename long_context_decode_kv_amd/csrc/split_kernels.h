@@ -1387,12 +1387,13 @@ SplitLaunchFn valu_fn() {
 }
 
 // The instance for (G, n_q) at one head_dim and pair of storage kinds: the
-// VALU kernel for one query row and G <= 5 (any G for head_dim 64), else the
-// matrix-core kernel with 8- or 16-row records (G * n_q <= 16).
+// VALU kernel (mfma false; one query row and G <= 5, any G <= 8 for
+// head_dim 64), or the matrix-core kernel with 8- or 16-row records
+// (head_dim 128 / 256, G * n_q <= 16).
 template <int D, int KT, int VT>
-SplitLaunchFn pick_g(int g, int n_q) {
+SplitLaunchFn pick_g(int g, int n_q, bool mfma) {
     if (g < 1 || n_q < 1) return nullptr;
-    if (!uses_matrix_cores(g, n_q, D)) {
+    if (!mfma) {
         if (n_q != 1) return nullptr;
         switch (g) {
             case 1: return valu_fn<D, 1, KT, VT>();
@@ -1408,7 +1409,7 @@ SplitLaunchFn pick_g(int g, int n_q) {
     }
     if constexpr (D >= 128) {
         if (g * n_q > 16) return nullptr;
-        const bool wide = record_rows(g, n_q, D) == 16;
+        const bool wide = record_rows_of(true, g, n_q) == 16;
         if (n_q == 1) return wide ? &launch_mfma<D, 16, KT, VT, false> : &launch_mfma<D, 8, KT, VT, false>;
         return wide ? &launch_mfma<D, 16, KT, VT, true> : &launch_mfma<D, 8, KT, VT, true>;
     }
@@ -1417,11 +1418,11 @@ SplitLaunchFn pick_g(int g, int n_q) {
 
 // Every (head_dim, group, n_q) instance of one pair of storage kinds.
 template <int KT, int VT>
-SplitLaunchFn pick_dg(int head_dim, int g, int n_q) {
+SplitLaunchFn pick_dg(int head_dim, int g, int n_q, bool mfma) {
     switch (head_dim) {
-        case 64: return pick_g<64, KT, VT>(g, n_q);
-        case 128: return pick_g<128, KT, VT>(g, n_q);
-        case 256: return pick_g<256, KT, VT>(g, n_q);
+        case 64: return pick_g<64, KT, VT>(g, n_q, mfma);
+        case 128: return pick_g<128, KT, VT>(g, n_q, mfma);
+        case 256: return pick_g<256, KT, VT>(g, n_q, mfma);
         default: return nullptr;
     }
 }

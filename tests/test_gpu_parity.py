@@ -88,7 +88,7 @@ def test_split_boundaries_inside_tiles(K, split_cells, kind, d, g):
     check(*ci.run(K, split_cells=split_cells), *ci.oracle())
 
 
-@pytest.mark.parametrize("d,g,hkv,occ", [(128, 4, 8, [13100]), (128, 5, 8, [13100]), (128, 1, 8, [12000]),
+@pytest.mark.parametrize("d,g,hkv,occ", [(128, 4, 8, [13100]), (128, 1, 8, [12000]), (64, 5, 8, [26000]),
                                          (64, 2, 8, [26000]), (128, 3, 4, [900, 25000, 1])])
 def test_eight_wave_workgroups(K, d, g, hkv, occ):
     """Short f16 contexts take one eight-wave workgroup per compute unit with
@@ -100,10 +100,11 @@ def test_eight_wave_workgroups(K, d, g, hkv, occ):
     check(*c.run(K, plan=p), *c.oracle())
 
 
-@pytest.mark.parametrize("hq,kind", [(48, O.F16), (64, O.F16), (48, O.Q8_B32)])
+@pytest.mark.parametrize("hq,kind", [(48, O.F16), (64, O.F16), (48, O.Q8_B32), (40, O.F16)])
 def test_matrix_core_four_tile_splits(K, hq, kind):
     """Wide groups on a 13100-cell layer: two-tile splits doubled to four
-    (208 workgroups at 256 CUs); ragged last split."""
+    (208 workgroups at 256 CUs); ragged last split.  Five f16 rows per KV
+    head take the matrix-core kernel at this length."""
     c = Case(600 + hq + kind, hq, 8, 128, kind=kind, occupied=[13100])
     p = c.plan(K, n_cu=256)
     assert p.info()["matrix_cores"] == 1 and p.info()["tiles_per_split"] == 4

@@ -169,6 +169,12 @@ def test_auto_split_fills_device():
         info = K.plan(hq, 8, 128, 1, 16384, n_occupied=[13100], n_queries=nq, n_cu=256).info()
         assert info["matrix_cores"] == 1 and info["n_workgroups"] == 208 and info["tiles_per_split"] == 4
     assert K.plan(48, 8, 128, 1, 16384, n_occupied=[8192], n_cu=256).info()["n_workgroups"] == 512
+    # five f16 rows: matrix-core kernel for short contexts, vector-ALU for long ones
+    short = K.plan(40, 8, 128, 1, 16384, n_occupied=[13100], n_cu=256).info()
+    assert short["matrix_cores"] == 1 and short["tiles_per_split"] == 4
+    long_ = K.plan(40, 8, 128, 1, 524288, n_occupied=[524288], n_cu=256).info()
+    assert long_["matrix_cores"] == 0 and long_["n_workgroups"] == 256
+    assert K.plan(40, 8, 128, 1, 16384, n_occupied=[13100], n_cu=256, split_cells=512).info()["matrix_cores"] == 0
     # long f16 splits on the vector-ALU kernel: one workgroup per compute unit
     p = K.plan(32, 8, 128, 1, 65536, n_occupied=[65536], n_cu=256)
     info = p.info()
