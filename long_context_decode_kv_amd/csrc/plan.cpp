@@ -204,17 +204,23 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
         }
         total_tiles += t * p.n_kv_heads;
     }
+    // Workgroups when every (slot, KV head) is cut into splits of at most
+    // `cells` positions, and whether that is 3/4 to one workgroup per CU.
+    auto wgs_for = [&](int64_t cells) {
+        int64_t w = 0;
+        for (auto& sa : plan.slots) w += std::max<int64_t>(1, ceil_div(sa.n, cells)) * p.n_kv_heads;
+        return w;
+    };
+    auto one_round = [&](int64_t w) { return 4 * w >= 3 * (int64_t)n_cu && w <= n_cu; };
+    const bool auto_split = p.split_cells == 0 && p.tiles_per_split == 0;
     // Five f16 query rows at head_dim 128 over short contexts (splits of at
     // most two tiles at two workgroups per CU) run faster on the matrix-core
     // kernel with four-tile splits (16384-cell layer 22.6 -> 20.8 us); long
     // splits stay on the vector-ALU kernel, whose LDS staging wins there.
     if (!mfma && group == 5 && n_q == 1 && p.head_dim == 128 && p.k_type == KVDEC_F16 &&
-        p.v_type == KVDEC_F16 && p.split_cells == 0 && p.tiles_per_split == 0 &&
-        ceil_div(total_tiles, 2 * (int64_t)n_cu) <= 2) {
-        int64_t wgs4 = 0;
-        for (auto& sa : plan.slots) wgs4 += std::max<int64_t>(1, ceil_div(sa.n, 4 * (int64_t)kTile)) * p.n_kv_heads;
-        if (4 * wgs4 >= 3 * (int64_t)n_cu && wgs4 <= n_cu) mfma = true;
-    }
+        p.v_type == KVDEC_F16 && auto_split && ceil_div(total_tiles, 2 * (int64_t)n_cu) <= 2 &&
+        one_round(wgs_for(4 * kTile)))
+        mfma = true;
     plan.mfma = mfma;
     const int rec_rows = record_rows_of(mfma, group, n_q);
     plan.rec_rows = rec_rows;
@@ -248,10 +254,7 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
         const bool heavy_rows = row_bytes(p.k_type, p.head_dim) + row_bytes(p.v_type, p.head_dim) >= 384;
         if ((staged || (mfma && heavy_rows)) && tps >= 8) {
             const int64_t one = ceil_div(total_tiles, (int64_t)n_cu);
-            int64_t wgs_one = 0;
-            for (auto& sa : plan.slots)
-                wgs_one += std::max<int64_t>(1, ceil_div(ceil_div(sa.n, kTile), one)) * p.n_kv_heads;
-            tps = wgs_one <= n_cu ? one : std::max<int64_t>(8, ceil_div(total_tiles, 8 * (int64_t)n_cu));
+            tps = wgs_for(one * kTile) <= n_cu ? one : std::max<int64_t>(8, ceil_div(total_tiles, 8 * (int64_t)n_cu));
         }
         ups = tps * upt;
         // Short contexts (splits of at most two steps at two workgroups per
@@ -259,25 +262,16 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
         // each split exactly two of its steps.  The same waves are in flight,
         // and a (slot, KV head) leaves half as many records to merge.
         const int64_t step4 = 4 * (64 / (p.head_dim / 16)) * 4;  // cells per 4-wave step (G <= 5)
-        if (staged && p.head_dim <= 128 && group <= 5 && tps * kTile <= 2 * step4) {
-            const int64_t cells8 = 2 * 2 * step4;  // two 8-wave steps
-            const int64_t ups8 = cells8 / unit;
-            int64_t wgs8 = 0;
-            for (auto& sa : plan.slots) wgs8 += std::max<int64_t>(1, ceil_div((int64_t)sa.n_units, ups8)) * p.n_kv_heads;
-            if (4 * wgs8 >= 3 * (int64_t)n_cu && wgs8 <= n_cu) {
-                plan.waves = 8;
-                ups = ups8;
-            }
+        const int64_t cells8 = 2 * 2 * step4;  // two 8-wave steps
+        if (staged && p.head_dim <= 128 && group <= 5 && tps * kTile <= 2 * step4 && one_round(wgs_for(cells8))) {
+            plan.waves = 8;
+            ups = cells8 / unit;
         }
         // The matrix-core kernel likewise: short splits of at most two tiles
         // double to four when that still gives 3/4 to one workgroup per
         // compute unit (fewer, wider records to merge; 4-query Qwen3-8B-shaped
         // layer 28.5 -> 26.6 us).
-        if (mfma && tps <= 2) {
-            int64_t wgs4 = 0;
-            for (auto& sa : plan.slots) wgs4 += std::max<int64_t>(1, ceil_div((int64_t)sa.n_units, 4 * upt)) * p.n_kv_heads;
-            if (4 * wgs4 >= 3 * (int64_t)n_cu && wgs4 <= n_cu) ups = 4 * upt;
-        }
+        if (mfma && tps <= 2 && one_round(wgs_for(4 * kTile))) ups = 4 * upt;
     }
     int64_t wgs = 0;
     plan.max_tiles_per_split = 0;
