@@ -314,13 +314,13 @@ class RollingWindow(ContiguousModel):
     resident and the oldest 26960 stream from pinned host memory through the
     workspace ring (copy stream + events), merged by log-sum-exp."""
 
-    chunk = 0  # tail cells per chunk (bench.py --tail-chunk); 0: 8192 staged, the whole tail otherwise
+    chunk = 0  # tail cells per chunk (bench.py --tail-chunk); 0: the whole tail (the library's default chunking)
 
     def __init__(self, name="rolling-ctx40960", mode="staged"):
         super().__init__(name, 36, 32, 8, 128, 40960, 40960)
         self.window, self.tail, self.mode = 14000, 26960, mode
         if not self.chunk:
-            self.chunk = 8192 if mode == "staged" else -(-self.tail // 128) * 128
+            self.chunk = -(-self.tail // 128) * 128
 
     def config(self):
         c = super().config()
@@ -495,7 +495,7 @@ def main():
     ap.add_argument("--split-cells", type=int, default=0,
                     help="cells per split for the contiguous-model workloads (multiple of 32; 0: planner)")
     ap.add_argument("--tail-chunk", type=int, default=0,
-                    help="host-tail cells per chunk (rolling workloads; 0: 8192 staged, whole tail otherwise)")
+                    help="host-tail cells per chunk (rolling workloads; 0: the whole tail in one chunk)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device-to-device copy of this many MiB first (counter calibration)")
     args = ap.parse_args()

@@ -121,8 +121,9 @@ extern "C" {
  *   [tail cell][kv head][row], scales likewise); tail_begin may be NULL (all
  *   zero) and tail_capacity_cells bounds the tail arrays.  The tail is copied
  *   to the device in chunks of tail_chunk_cells (a multiple of 128; 0 picks
- *   8192) through a ring of tail_ring_depth staging slots (2..16; 0 picks 4;
- *   never more than the call's chunks) inside the workspace.  With tail_zero_copy = 1 nothing is staged: the
+ *   32768: larger copies run closer to the link rate) through a ring of
+ *   tail_ring_depth staging slots (2..16; 0 picks 4; never more than the
+ *   call's chunks) inside the workspace.  With tail_zero_copy = 1 nothing is staged: the
  *   chunk kernels read the pinned host arrays in place over the link.  (The
  *   "KVARN KV Performance optimizations" notes on pinned-host projector
  *   weights found such in-place reads slower than one staging copy because

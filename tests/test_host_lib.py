@@ -324,7 +324,7 @@ def test_zero_copy_tail_plan():
     assert staged.workspace_bytes - zc.workspace_bytes >= ring
     assert staged.workspace_bytes - zc.workspace_bytes < 2 * ring
     assert zc.info()["n_tail_chunks"] == staged.info()["n_tail_chunks"] == 2
-    # default chunk: 8192 cells, one chunk for this tail
+    # default chunk: 32768 cells, one chunk for this tail
     one = K.plan(32, 8, 128, 1, 4000, n_occupied=[1000], cell_begin=[3000], n_tail=[3000], tail_capacity_cells=3000,
                  n_cu=256)
     assert one.info()["n_tail_chunks"] == 1
