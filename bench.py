@@ -607,9 +607,13 @@ def main():
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_info
         layers_done, el, sample = wl.oracle_sample(args.cpu_budget)
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        pools = threadpool_info()
+        threads = max([p.get("num_threads", 1) for p in pools] + [1])
+        blas = ", ".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in pools
+                                 if p.get("user_api") == "blas"}))
         cpu = {"value": round(bytes_launch * layers_done / el / 1e9, 4), "unit": "GB/s", "cores": threads,
                "kind": "oracle", "sample": sample + f"; {el:.1f} s float64 numpy on the host",
+               "blas": blas or None, "host_cpus": os.cpu_count(),
                "us_per_step_extrapolated": round(el / layers_done * wl.layers * 1e6, 1)}
         # the same oracle on one thread, where one unit of the sample stays short
         if el / layers_done * threads < 20.0:
