@@ -383,7 +383,8 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
             t.slot[0].wg_begin = 0;
             t.slot[0].part_begin = 0;
             t.slot[0].to_acc = (c + 1 < n_chunks) ? 1 : 0;
-            t.slot[0].n_clusters = kvdec::merge_clusters(splits, kvdec::merge_chunk(D, p.rec_rows));
+            t.slot[0].chunk = kvdec::merge_chunk_for(D, p.rec_rows, splits);
+            t.slot[0].n_clusters = kvdec::merge_clusters(splits, t.slot[0].chunk);
             t.slot[0].cl_begin = 0;
             // a tail cell's position is its index in the host tail
             t.cell_pos = nullptr;

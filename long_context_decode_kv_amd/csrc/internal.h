@@ -53,6 +53,18 @@ constexpr int merge_chunk(int head_dim, int group) {
     const int ub = cols == 1 ? 32 : 32 / cols;
     return ub * ts < 64 ? ub * ts : 64;
 }
+// Records of 16 rows at head_dim 128 (512 float4 columns) take two columns
+// per thread and, by merge_chunk, 16 records per round; the kernel holds up
+// to 28 without spilling, so a group of at most 28 splits merges in one round
+// instead of two (4-query Qwen3-8B-shaped layer 26.7 -> 25.4 us).  At
+// head_dim 256 the larger round measured slower on the GQA-6 caches.
+constexpr int merge_chunk_max(int head_dim, int group) {
+    return head_dim == 128 && group == 16 ? 28 : merge_chunk(head_dim, group);
+}
+// Round size for the records of a (slot, KV head) with n_splits splits.
+constexpr int merge_chunk_for(int head_dim, int group, int n_splits) {
+    return n_splits <= merge_chunk_max(head_dim, group) ? merge_chunk_max(head_dim, group) : merge_chunk(head_dim, group);
+}
 // Clusters per (slot, KV head): one level of merging while it takes at most
 // two rounds, else clusters of merge_chunk splits merged first, each into a
 // cluster record, and the cluster records merged last.
@@ -69,9 +81,9 @@ struct SlotArg {
     int32_t wg_begin;    // first workgroup of this slot (n_kv_heads * n_splits of them)
     int32_t part_begin;  // first partial record of this slot
     int32_t to_acc;      // 1: the slot's result goes to acc_out (more partials follow)
-    int32_t n_clusters;  // merge_clusters(n_splits, merge_chunk(D, G))
+    int32_t n_clusters;  // merge_clusters(n_splits, chunk)
     int32_t cl_begin;    // first cluster (ticket and record) of this slot
-    int32_t pad;
+    int32_t chunk;       // records per merge round: merge_chunk_for(D, G, n_splits)
 };
 
 // Kernel arguments of one split launch (fits the 4 KiB kernarg segment).

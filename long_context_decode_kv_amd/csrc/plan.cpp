@@ -293,10 +293,10 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
     plan.max_tiles_per_split = (int32_t)ceil_div((int64_t)plan.max_split_cells, kTile);
     plan.n_workgroups = (int32_t)wgs;
     plan.n_part_records = (int32_t)wgs;
-    const int chunk = merge_chunk(p.head_dim, rec_rows);
     int64_t clusters = 0;
     for (auto& sa : plan.slots) {
-        sa.n_clusters = merge_clusters(sa.n_splits, chunk);
+        sa.chunk = merge_chunk_for(p.head_dim, rec_rows, sa.n_splits);
+        sa.n_clusters = merge_clusters(sa.n_splits, sa.chunk);
         sa.cl_begin = (int32_t)clusters;
         if (sa.n_clusters > 1) clusters += (int64_t)sa.n_clusters * p.n_kv_heads;
     }
@@ -344,7 +344,7 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
         plan.chunk_tiles_per_split = (int32_t)ctps;
         plan.chunk_splits = (int32_t)std::max<int64_t>(1, ceil_div(chunk_tiles, ctps));
         part_capacity = std::max<int64_t>(part_capacity, (int64_t)plan.chunk_splits * p.n_kv_heads);
-        const int cc = merge_clusters(plan.chunk_splits, chunk);
+        const int cc = merge_clusters(plan.chunk_splits, merge_chunk_for(p.head_dim, rec_rows, plan.chunk_splits));
         if (cc > 1) clusters = std::max<int64_t>(clusters, (int64_t)cc * p.n_kv_heads);
     }
     // cluster records follow the split records

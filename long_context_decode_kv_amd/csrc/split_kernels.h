@@ -303,9 +303,11 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMa
     constexpr int NV = G * D / 4;                           // float4 columns of o
     constexpr int TS = NV >= NT ? 1 : NT / NV;              // threads per column
     constexpr int COLS = (NV + NT - 1) / NT;                // columns per thread
-    constexpr int SPC = merge_chunk(D, G);                  // records per chunk (one per lane)
-    constexpr int UB = (SPC + TS - 1) / TS;                 // records per thread per chunk
-    static_assert(SPC <= 64 && UB * COLS <= 32, "merge chunk");
+    constexpr int SPC_MAX = merge_chunk_max(D, G);          // largest round (one record per lane)
+    constexpr int UB = (SPC_MAX + TS - 1) / TS;             // records per thread per round
+    static_assert(SPC_MAX <= 64 && UB * COLS <= 56, "merge chunk");
+    // this slot's round (a constant where the kernel has no choice)
+    const int SPC = SPC_MAX == merge_chunk(D, G) ? SPC_MAX : sa.chunk;
     constexpr int NW = NT / 64;                             // waves
     __shared__ float f_m[64 * G];
     __shared__ float run_m[G], run_l[G], scale_old[G];
@@ -525,7 +527,7 @@ __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& 
     }
     // two levels: the last of each cluster of splits merges the cluster into
     // a cluster record; the last cluster merger merges the cluster records
-    constexpr int CH = merge_chunk(D, G);
+    const int CH = merge_chunk_max(D, G) == merge_chunk(D, G) ? merge_chunk(D, G) : sa.chunk;
     const int cid = split / CH;
     const int c0 = cid * CH;
     const int cn = (n_splits - c0) < CH ? (n_splits - c0) : CH;
