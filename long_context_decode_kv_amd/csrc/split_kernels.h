@@ -782,8 +782,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
         }
     };
 
-    // Short splits (one or two steps) gain nothing from staging -- their
-    // loads all leave at once anyway -- and take the plain path.
+    // Short splits (one or two steps) take the plain path: staging the
+    // second step of a two-step split measured slower (on short layers the
+    // requests already in flight saturate the memory system).
     bool staged = false;
     if constexpr (kDma) staged = (pos_end - pos_begin) > 2 * STEP;
     if constexpr (kDma) if (staged) {
