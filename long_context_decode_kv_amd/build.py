@@ -10,6 +10,7 @@ streaming-read probe used by the benchmark to ``libkvprobe.so`` beside it.
 """
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -46,14 +47,38 @@ def hipcc():
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
+# Kernel resource remarks: a kernel that needs per-lane scratch (a spilled
+# or dynamically indexed register array) fails the build -- on these kernels
+# it has meant a many-fold slowdown, never a valid trade.
+RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
+
+
+def _scratch_kernels(log):
+    """(kernel, bytes per lane) for every kernel the remarks show using scratch."""
+    found, name = [], None
+    for line in log.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            found.append((name, int(m.group(1))))
+    return found
+
+
 def _compile(src, extra):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc()] + lang + FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
+    remarks = RESOURCE_REMARKS if src.endswith(".hip") else []
+    cmd = [hipcc()] + lang + FLAGS + remarks + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    return obj, r.stderr
+    spills = _scratch_kernels(r.stderr)
+    if spills:
+        raise RuntimeError(f"{src}: kernels using scratch memory: {spills}")
+    log = "\n".join(line for line in r.stderr.splitlines() if "remark:" not in line)
+    return obj, log
 
 
 def build(verbose=False, extra=()):

@@ -351,3 +351,16 @@ def test_device_built_plan_shape_and_errors():
     assert _status(lambda: K.build_cells(p, 0, FAKE, FAKE, ws, stream=0)) == K.E_INVALID
     host = K.plan(24, 4, 256, 1, 5000, cells=[[1, 2]], n_cu=256)
     assert _status(lambda: K.build_cells(host, FAKE, FAKE, FAKE, ws, stream=0)) == K.E_INVALID  # not device-built
+
+
+def test_build_rejects_kernels_with_scratch():
+    """The build parses the compiler's kernel-resource remarks and refuses
+    any kernel that needs per-lane scratch memory."""
+    from long_context_decode_kv_amd import build
+    log = "\n".join([
+        "x.h:1:1: remark: Function Name: _Z2k1v [-Rpass-analysis=kernel-resource-usage]",
+        "x.h:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "x.h:9:1: remark: Function Name: _Z2k2v [-Rpass-analysis=kernel-resource-usage]",
+        "x.h:9:1: remark:     ScratchSize [bytes/lane]: 188 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert build._scratch_kernels(log) == [("_Z2k2v", 188)]
