@@ -645,9 +645,9 @@ def main():
                        tiles_per_split=info["tiles_per_split"], cells_per_split=info["split_cells"]),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": (("split_mfma_kernel<%d,rows %d,%s,%s>" % (
+                     "kernel": (("split_mfma_kernel<%d,rows %d,%s,%s,%d waves>" % (
                          wl.d, wl.hq // wl.hkv * getattr(wl, "n_q", 1), KIND[wl.kind],
-                         KIND[getattr(wl, "v_kind", wl.kind)])) if info.get("matrix_cores") else
+                         KIND[getattr(wl, "v_kind", wl.kind)], info.get("waves", 4))) if info.get("matrix_cores") else
                          ("split_kernel<%d,%d,%s,%s,%d waves>" % (wl.d, wl.hq // wl.hkv, KIND[wl.kind],
                                                                   KIND[getattr(wl, "v_kind", wl.kind)],
                                                                   info.get("waves", 4)))),

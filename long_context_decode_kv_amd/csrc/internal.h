@@ -104,7 +104,7 @@ struct SplitArgs {
     uint32_t* tickets;       // one per (slot, KV head)
     uint32_t* ctickets;      // one per cluster of splits
     int32_t crec_base;       // record index of cluster 0's record
-    int32_t waves;           // vector-ALU kernel: 4 or 8 waves per workgroup
+    int32_t waves;           // waves per workgroup of either kernel: 4 or 8
     float* out;              // [slots][Hq][D] or null
     float* lse;              // [slots][Hq] or null
     float* pm;               // whole-call partial (m natural units, l, o) or null
@@ -195,7 +195,7 @@ struct kvdec_plan {
     int32_t max_tiles_per_split = 0;
     int32_t split_unit = 0;        // positions per split unit: 32 (vector-ALU kernel) or 128
     int32_t max_split_cells = 0;   // largest split, in positions
-    int32_t waves = 4;             // waves per vector-ALU workgroup (4 or 8)
+    int32_t waves = 4;             // waves per split workgroup (4 or 8)
     bool mfma = false;             // served by the matrix-core kernel
     int64_t n_tiles = 0;
     std::vector<int32_t> cells;      // indirect entries (host-built plans)

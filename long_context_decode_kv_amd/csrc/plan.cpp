@@ -270,8 +270,15 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
         // The matrix-core kernel likewise: short splits of at most two tiles
         // double to four when that still gives 3/4 to one workgroup per
         // compute unit (fewer, wider records to merge; 4-query Qwen3-8B-shaped
-        // layer 28.5 -> 26.6 us).
-        if (mfma && tps <= 2 && one_round(wgs_for(4 * kTile))) ups = 4 * upt;
+        // layer 28.5 -> 26.6 us).  With 16-row records at head_dim 128 the
+        // four tiles are two steps of an eight-wave workgroup, whose 512
+        // threads also publish and merge the wider records in fewer passes
+        // (4-query layer 25.4 -> 24.8 us, 16-head groups 24.7 -> 23.7 us;
+        // 8-row records measured 3% slower, so they keep four waves).
+        if (mfma && tps <= 2 && one_round(wgs_for(4 * kTile))) {
+            ups = 4 * upt;
+            if (rec_rows == 16 && p.head_dim == 128) plan.waves = 8;
+        }
     }
     int64_t wgs = 0;
     plan.max_tiles_per_split = 0;

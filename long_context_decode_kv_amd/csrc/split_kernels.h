@@ -991,8 +991,8 @@ __device__ __forceinline__ uint16_t scale_of(const Chunk<SB>& r, int j, int lq) 
     }
 }
 
-template <int D, int RM, int KT, int VT, bool IND, bool MQ>
-__global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a) {
+template <int D, int RM, int KT, int VT, bool IND, bool MQ, int W>
+__global__ __launch_bounds__(64 * W) void split_mfma_kernel(const SplitArgs a) {
     // RM: rows of a split record (8 or 16); the G * n_q real query rows of
     // the (slot, KV head) are padded to RM and to the 16-row tile.
     static_assert(RM == 8 || RM == 16, "record rows");
@@ -1005,8 +1005,9 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
     constexpr int NB = D / kBlock;                 // scales per row
     constexpr int SB = NB * 2;                     // bytes of one row of scales
     constexpr int VSTR = 2 * D + 32;               // bytes per staged V row (padded)
-    constexpr int STAGE = 4 * 32 * VSTR;           // V staging of the 4 waves
-    constexpr int MERGE = 4 * G * 4 * 2 + 4 * G * D * 4;
+    constexpr int STAGE = W * 32 * VSTR;           // V staging of the W waves
+    constexpr int MERGE = W * G * 4 * 2 + W * G * D * 4;
+    constexpr int SC = 32 * W;                     // cells per workgroup step (32 per wave)
     constexpr int SMEM = STAGE > MERGE ? STAGE : MERGE;
     __shared__ __align__(16) unsigned char smem[SMEM];
     __shared__ int sm_last;
@@ -1078,8 +1079,8 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
     unsigned char* vst = smem + wave * 32 * VSTR;
     const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     const int64_t pos_end = span_end < sa.n ? span_end : sa.n;
-    // one step per 128 positions: 32 cells per wave
-    const int n_steps = pos_end > base0 ? (int)((pos_end - base0 + kTile - 1) / kTile) : 0;
+    // one step per SC positions: 32 cells per wave
+    const int n_steps = pos_end > base0 ? (int)((pos_end - base0 + SC - 1) / SC) : 0;
 
     // Cells of a step: lane li owns cell li of the wave's two 16-cell blocks.
     // Loads never branch: an invalid cell reads row 0 of the cache instead,
@@ -1148,7 +1149,7 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             resolve(base0, mb, fetch(base0, mb), cell[mb], valid[mb]);
-            raw_next[mb] = fetch(base0 + kTile, mb);
+            raw_next[mb] = fetch(base0 + SC, mb);
         }
         fetch_pos(cell, praw);
         load_k(cell);
@@ -1176,15 +1177,15 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
     }
 
     for (int st = 0; st < n_steps; ++st) {
-        const int64_t base = base0 + (int64_t)st * kTile;
+        const int64_t base = base0 + (int64_t)st * SC;
         const uint64_t vm0 = __ballot(valid[0]), vm1 = __ballot(valid[1]);
         int32_t raw2[2];
         int64_t ncell[2];
         bool nvalid[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-            raw2[mb] = fetch(base + 2 * kTile, mb);
-            resolve(base + kTile, mb, raw_next[mb], ncell[mb], nvalid[mb]);
+            raw2[mb] = fetch(base + 2 * SC, mb);
+            resolve(base + SC, mb, raw_next[mb], ncell[mb], nvalid[mb]);
         }
         int32_t npraw[2] = {0, 0};
         fetch_pos(ncell, npraw);
@@ -1337,8 +1338,8 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
     // Each wave is one stream: (m2, l, o) of heads < G -> LDS, then merge.
     __syncthreads();  // the V staging area is reused for the merge arrays
     float (*sm_m)[G] = reinterpret_cast<float (*)[G]>(smem);
-    float (*sm_l)[G] = reinterpret_cast<float (*)[G]>(smem + 4 * G * 4);
-    float (*sm_o)[G][D] = reinterpret_cast<float (*)[G][D]>(smem + 4 * G * 4 * 2);
+    float (*sm_l)[G] = reinterpret_cast<float (*)[G]>(smem + W * G * 4);
+    float (*sm_o)[G][D] = reinterpret_cast<float (*)[G][D]>(smem + W * G * 4 * 2);
     if (lq == 0 && li < G) {
         sm_m[wave][li] = m_h;
         sm_l[wave][li] = l_h * kMPOffInv;
@@ -1351,7 +1352,7 @@ __global__ __launch_bounds__(kThreads) void split_mfma_kernel(const SplitArgs a)
             if (h < G) sm_o[wave][h][16 * nb + li] = oacc[nb][e] * kMPOffInv;
         }
     __syncthreads();
-    finish_split<D, G, 4, D>(a, sa, s, g, split, rm, sm_m, sm_l, sm_o, sm_last);
+    finish_split<D, G, W, D, 64 * W>(a, sa, s, g, split, rm, sm_m, sm_l, sm_o, sm_last);
 }
 
 template <int D, int G, int KT, int VT>
@@ -1371,11 +1372,24 @@ int launch_valu(const SplitArgs& a, void* stream) {
 
 template <int D, int RM, int KT, int VT, bool MQ>
 int launch_mfma(const SplitArgs& a, void* stream) {
+    // eight-wave workgroups for 16-row records at head_dim 128 (at 256 they
+    // would spill registers)
+    if constexpr (D == 128 && RM == 16) {
+        if (a.waves == 8) {
+            if (a.plan)
+                hipLaunchKernelGGL((split_mfma_kernel<D, RM, KT, VT, true, MQ, 8>), dim3(a.n_workgroups), dim3(512), 0,
+                                   (hipStream_t)stream, a);
+            else
+                hipLaunchKernelGGL((split_mfma_kernel<D, RM, KT, VT, false, MQ, 8>), dim3(a.n_workgroups), dim3(512),
+                                   0, (hipStream_t)stream, a);
+            return (int)hipGetLastError();
+        }
+    }
     if (a.plan)
-        hipLaunchKernelGGL((split_mfma_kernel<D, RM, KT, VT, true, MQ>), dim3(a.n_workgroups), dim3(kThreads), 0,
+        hipLaunchKernelGGL((split_mfma_kernel<D, RM, KT, VT, true, MQ, 4>), dim3(a.n_workgroups), dim3(kThreads), 0,
                            (hipStream_t)stream, a);
     else
-        hipLaunchKernelGGL((split_mfma_kernel<D, RM, KT, VT, false, MQ>), dim3(a.n_workgroups), dim3(kThreads), 0,
+        hipLaunchKernelGGL((split_mfma_kernel<D, RM, KT, VT, false, MQ, 4>), dim3(a.n_workgroups), dim3(kThreads), 0,
                            (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }

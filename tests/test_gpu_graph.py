@@ -25,6 +25,7 @@ CASES = {
     "f16 G4 two-level merge": dict(args=(62, 16, 4, 128), kw=dict(occupied=[20000]), plan=dict(tiles_per_split=1)),
     "q8 G6 indirect matrix cores": dict(args=(63, 24, 4, 256), kw=dict(kind=O.Q8_B32, indirect_lengths=[3000, 700, 1],
                                                                         shuffle=True, duplicates=5), plan={}),
+    "f16 G16 eight-wave matrix cores": dict(args=(65, 128, 8, 128), kw=dict(occupied=[13100]), plan={}),
     "f16 G5 long staged splits": dict(args=(64, 10, 2, 128), kw=dict(kind=O.F16, occupied=[30000]),
                                       plan=dict(split_cells=4096)),
 }

@@ -100,7 +100,8 @@ def test_eight_wave_workgroups(K, d, g, hkv, occ):
     check(*c.run(K, plan=p), *c.oracle())
 
 
-@pytest.mark.parametrize("hq,kind", [(48, O.F16), (64, O.F16), (48, O.Q8_B32), (40, O.F16)])
+@pytest.mark.parametrize("hq,kind", [(48, O.F16), (64, O.F16), (48, O.Q8_B32), (40, O.F16), (128, O.F16),
+                                     (128, O.Q4_B32)])
 def test_matrix_core_four_tile_splits(K, hq, kind):
     """Wide groups on a 13100-cell layer: two-tile splits doubled to four
     (208 workgroups at 256 CUs); ragged last split.  Five f16 rows per KV
@@ -108,6 +109,27 @@ def test_matrix_core_four_tile_splits(K, hq, kind):
     c = Case(600 + hq + kind, hq, 8, 128, kind=kind, occupied=[13100])
     p = c.plan(K, n_cu=256)
     assert p.info()["matrix_cores"] == 1 and p.info()["tiles_per_split"] == 4
+    assert p.info()["waves"] == (8 if hq == 128 else 4)
+    check(*c.run(K, plan=p), *c.oracle())
+
+
+@pytest.mark.parametrize("kind,vkind,indirect", [(O.F16, O.F16, False), (O.F16, O.F16, True),
+                                                 (O.Q8_B32, O.Q4_B32, False), (O.Q8_B32, O.Q8_B32, True)])
+def test_matrix_core_eight_wave_splits(K, kind, vkind, indirect):
+    """16-head groups at head_dim 128 over short contexts: four-tile splits
+    as two steps of an eight-wave workgroup; ragged slots (a ragged last
+    step, a slot of one cell), contiguous or an indirect plan with shuffled
+    records, duplicates and holes."""
+    occ = [6000, 5000, 2100, 1]
+    if indirect:
+        c = Case(640 + kind + vkind, 128, 8, 128, kind=kind, v_kind=vkind, indirect_lengths=occ, shuffle=True,
+                 duplicates=9)
+    else:
+        c = Case(650 + kind + vkind, 128, 8, 128, kind=kind, v_kind=vkind, occupied=occ,
+                 begins=[0, 6100, 11200, 13400])
+    p = c.plan(K, n_cu=256)
+    info = p.info()
+    assert info["matrix_cores"] == 1 and info["waves"] == 8 and info["tiles_per_split"] == 4
     check(*c.run(K, plan=p), *c.oracle())
 
 

@@ -165,9 +165,14 @@ def test_auto_split_fills_device():
     assert K.plan(16, 8, 256, 1, 16384, n_occupied=[13100], n_cu=256).info()["waves"] == 4
     # matrix-core kernel, short splits: two tiles double to four when that
     # still gives at most one workgroup per compute unit
-    for hq, nq in ((48, 1), (32, 4)):
+    # (eight waves, two steps of 256 cells each, for 16-row records at head_dim 128)
+    for hq, nq, waves in ((48, 1, 4), (64, 1, 4), (32, 4, 8), (128, 1, 8)):
         info = K.plan(hq, 8, 128, 1, 16384, n_occupied=[13100], n_queries=nq, n_cu=256).info()
         assert info["matrix_cores"] == 1 and info["n_workgroups"] == 208 and info["tiles_per_split"] == 4
+        assert info["waves"] == waves
+    assert K.plan(32, 8, 128, 1, 16384, n_occupied=[13100], n_queries=4, n_cu=256,
+                  split_cells=512).info()["waves"] == 4
+    assert K.plan(64, 4, 256, 1, 16384, n_occupied=[13100], n_cu=256).info()["waves"] == 4
     assert K.plan(48, 8, 128, 1, 16384, n_occupied=[8192], n_cu=256).info()["n_workgroups"] == 512
     # five f16 rows: matrix-core kernel for short contexts, vector-ALU for long ones
     short = K.plan(40, 8, 128, 1, 16384, n_occupied=[13100], n_cu=256).info()
