@@ -452,16 +452,44 @@ WORKLOADS = {
 
 # ---------------------------------------------------------------- traffic from committed counters
 
+def strip_c_comments(text):
+    """C / C++ source without its comments and with runs of whitespace
+    collapsed, string and character literals kept as they are."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def kernel_source_hash():
-    """Hash of every source the split and merge kernels are compiled from."""
+    """Hash of the code (comments and layout ignored) of every source that
+    decides what the split and merge kernels do: the kernels, the planner
+    that picks their launch shape, and the dispatch."""
     import glob
     csrc = os.path.join(ROOT, "long_context_decode_kv_amd", "csrc")
     files = sorted(glob.glob(os.path.join(csrc, "*.hip"))) + [os.path.join(csrc, f) for f in
-                                                              ("split_kernels.h", "internal.h")]
+                                                              ("split_kernels.h", "internal.h", "plan.cpp",
+                                                               "api.cpp")]
     h = hashlib.sha256()
     for f in files:
         if os.path.basename(f) != "probe.hip":
-            h.update(open(f, "rb").read())
+            h.update(strip_c_comments(open(f, encoding="utf-8").read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -4,10 +4,10 @@
 // (so the instances compile in parallel), and by kernels.hip for the shared
 // helpers.
 //
-// Split kernel.  One workgroup (4 waves) streams a contiguous range of
-// 128-cell tiles of one (slot, KV head), in steps where each lane holds 4
-// cells and each wave a contiguous run of cells.  R consecutive lanes share
-// one cell and split its head_dim
+// Split kernel.  One workgroup (4 or 8 waves) streams a contiguous range of
+// positions of one (slot, KV head), cut on 32-cell boundaries, in steps where
+// each lane holds 4 cells and each wave's cells spread over the step.  R
+// consecutive lanes share one cell and split its head_dim
 // elements into R slices of D/R; every 16-byte (8-byte for 4-bit rows) load
 // of a wave covers whole 128-byte lines of consecutive cells, so the KV
 // stream is read with coalesced 128-bit loads.  The G query rows of the KV
@@ -17,7 +17,7 @@
 // query rows).  Scores are reduced over the R lanes of a cell with DPP
 // moves; each group of lanes that shares a cell stream keeps its own online
 // softmax state (m, l, o), and the states are merged at the end of the split
-// with the log-sum-exp rule, first across the wave, then across the 4 waves
+// with the log-sum-exp rule, first across the wave, then across the waves
 // through LDS.
 //
 // Partials are written as (m2 = running max in log2 units, l, o).  When a
@@ -198,14 +198,13 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
 
 // Lane geometry.  Per-lane d-slice DL: 16 elements for groups up to 5, 8
 // above (register budget).  R lanes per cell, CPW cells per wave per load,
-// NB cells per lane per step, so a workgroup step covers 4 * CPW * NB cells.
+// NB cells per lane per step, so a step of W waves covers W * CPW * NB cells.
 template <int D, int G>
 struct Geo {
     static constexpr int DL = (G <= 5) ? 16 : 8;
     static constexpr int R = D / DL;
     static constexpr int CPW = 64 / R;
     static constexpr int NB = 4;
-    static constexpr int STEP = 4 * CPW * NB;
     static_assert(R >= 4 && R <= 32, "lane geometry");
 };
 
@@ -941,7 +940,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 // V^ is dequantised (d * code rounded to f16) into a per-wave LDS tile of 32
 // rows and read back column-wise with ds_read_b64_tr_b16, whose 16-lane 4x4
 // transpose delivers the B operand.  Each wave is one online-softmax stream;
-// the four waves are merged at the end like the VALU path's streams.
+// the waves (four, or eight for 16-row records at head_dim 128) are merged at
+// the end like the VALU path's streams.
 // ---------------------------------------------------------------------------
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));

@@ -43,3 +43,12 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode != 0 and "one GPU" in (r.stdout + r.stderr)
+
+
+def test_kernel_hash_ignores_comments_only():
+    src = 'int f(int x) {  // twice\n  return 2 * x; /* "doubled" */ }\nconst char* s = "a // b";\n'
+    same = '// leading note\nint f(int x) {\n    return 2 * x;\n}\nconst char* s = "a // b";\n'
+    other = 'int f(int x) { return 3 * x; }\nconst char* s = "a // b";\n'
+    assert bench.strip_c_comments(src) == bench.strip_c_comments(same)
+    assert bench.strip_c_comments(src) != bench.strip_c_comments(other)
+    assert '"a // b"' in bench.strip_c_comments(src)
