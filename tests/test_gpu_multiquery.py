@@ -95,6 +95,24 @@ def test_indirect_with_cell_positions(K, kind, vkind):
     check(out, lse, *oracle_mq(c, q, qp, cell_pos))
 
 
+@pytest.mark.parametrize("kind,vkind,n_q,g", [(O.F16, O.F16, 4, 4), (O.Q8_B32, O.Q4_B32, 2, 8)])
+def test_eight_wave_indirect_with_cell_positions(K, kind, vkind, n_q, g):
+    """16-row records at head_dim 128 over a short context: the planner's
+    four-tile splits on eight-wave workgroups, with a shuffled record plan
+    (duplicates, holes) and explicit cell positions."""
+    c = Case(280 + n_q, 8 * g, 8, 128, kind=kind, v_kind=vkind, indirect_lengths=[9000, 3000, 1], shuffle=True,
+             duplicates=11)
+    p = c.plan(K, n_queries=n_q, n_cu=256)
+    assert p.info()["waves"] == 8 and p.info()["tiles_per_split"] == 4
+    r = np.random.default_rng(8)
+    cell_pos = r.permutation(c.capacity).astype(np.int32)
+    q = mq_q(9, c, n_q)
+    qp = r.integers(-10, c.capacity + 10, size=(c.n_slots, n_q)).astype(np.int32)
+    qp[0, 0] = c.capacity  # a row that sees every cell
+    out, lse = run_mq(K, c, n_q, q, qp, cell_pos, n_cu=256)
+    check(out, lse, *oracle_mq(c, q, qp, cell_pos))
+
+
 @pytest.mark.parametrize("d,kind", [(256, O.Q8_B32), (128, O.F16)])
 def test_two_level_merge_of_16_row_records(K, d, kind):
     """One-tile splits: 16-row records merged through clusters."""
