@@ -3,6 +3,7 @@ the C ABI (via the ctypes binding), and evaluate the float64 oracle on the
 same host arrays."""
 
 import math
+import os
 
 import numpy as np
 
@@ -98,14 +99,22 @@ class Case:
         return res
 
 
+# (test, max |out err|, out RMSE, max |lse err|) of every comparison in this
+# process; the session summary prints the worst of them.
+REPORT = []
+
+
 def check(got_out, got_lse, want_out, want_lse, tol=TOL):
     """Element-wise comparison; returns (max |err| of out, of lse)."""
     assert got_out.shape == want_out.shape
     assert np.all(np.isfinite(got_out)), "non-finite output"
     err = float(np.max(np.abs(got_out - want_out))) if got_out.size else 0.0
+    rmse = float(np.sqrt(np.mean((got_out.astype(np.float64) - want_out) ** 2))) if got_out.size else 0.0
+    REPORT.append([os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0], err, rmse, None])
     assert err <= tol, f"max |out err| = {err:.3e}"
     empty = np.isneginf(want_lse)
     assert np.array_equal(np.isneginf(got_lse), empty), "lse -inf pattern differs"
     lerr = float(np.max(np.abs(got_lse[~empty] - want_lse[~empty]))) if (~empty).any() else 0.0
+    REPORT[-1][3] = lerr
     assert lerr <= tol, f"max |lse err| = {lerr:.3e}"
     return err, lerr
