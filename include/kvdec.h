@@ -186,7 +186,9 @@ typedef struct kvdec_plan kvdec_plan_t;
  * q: device fp32 [n_slots][n_queries][n_q_heads][head_dim] (n_queries = 1:
  *   [n_slots][n_q_heads][head_dim]); out, lse and the partial triple below
  *   carry the same [n_queries] axis after the slot.
- * k, v: device code arrays.  Row (cell c, KV head g) starts at byte
+ * k, v: device code arrays, non-null even when no cell is attended (the
+ *   matrix-core kernel reads row 0 in place of hole entries).  Row (cell c,
+ *   KV head g) starts at byte
  *   c * cell_stride + g * head_stride; a row holds head_dim f16 values,
  *   head_dim int8 codes, or head_dim / 2 bytes of 4-bit codes.  A stride of 0
  *   means the dense layout [cell][kv head][row].  Base pointers and strides

@@ -139,7 +139,9 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
     // ---- cells of each slot
     if (device_cells) {
         // entries come from kvdec_build_cells: max_records[s] segments per slot
-        const int64_t rec_cap = ceil_div(std::max<int64_t>(p.capacity_cells, 1), kTile);
+        // (none without cells: the matrix-core kernel reads row 0 of the
+        // cache in place of a hole, so a segment needs a cache of >= 1 cell)
+        const int64_t rec_cap = ceil_div(p.capacity_cells, kTile);
         plan.cells_off.assign(p.n_slots + 1, 0);
         plan.max_records.assign(p.n_slots, 0);
         for (int s = 0; s < p.n_slots; ++s) {

@@ -350,6 +350,9 @@ def test_device_built_plan_shape_and_errors():
     assert _status(lambda: K.plan(24, 4, 256, 1, 5000, k_type=K.Q8_B32, v_type=K.Q8_B32, max_records=[41],
                                   n_cu=256)) == K.E_INVALID                    # > ceil(5000 / 128)
     assert _status(lambda: K.plan(24, 4, 256, 1, 5000, max_records=[-1], n_cu=256)) == K.E_INVALID
+    # no cells, no segments (a hole would read row 0 of an empty cache)
+    assert _status(lambda: K.plan(24, 4, 256, 1, 0, max_records=[1], n_cu=256)) == K.E_INVALID
+    assert K.plan(24, 4, 256, 1, 0, max_records=[0], n_cu=256).info()["n_entries"] == 0
     ws = (FAKE, p.workspace_bytes)
     assert _status(lambda: K.build_cells(p, FAKE, FAKE, FAKE, (FAKE, 16), stream=0)) == K.E_WORKSPACE
     assert _status(lambda: K.build_cells(p, FAKE, FAKE + 4, FAKE, ws, stream=0)) == K.E_INVALID  # raw_off align
