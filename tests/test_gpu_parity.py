@@ -37,6 +37,23 @@ def test_ragged_lengths_multi_slot(K):
     check(*c.run(K), *c.oracle())
 
 
+@pytest.mark.parametrize("d,g,kind,indirect", [(128, 4, O.F16, False), (128, 4, O.F16, True),
+                                               (256, 6, O.Q8_B32, False), (256, 6, O.Q4_B32, True)])
+def test_maximum_slot_count(K, d, g, kind, indirect):
+    """KVDEC_MAX_SLOTS (64) slots in one launch, lengths 0 .. 1500 (empty
+    slots, single cells, tile edges), contiguous or an indirect plan with
+    shuffled records and duplicates; planner splits at 256 CUs."""
+    r = np.random.default_rng(31 + d + kind)
+    occ = [int(x) for x in r.choice([0, 1, 2, 127, 128, 129, 300, 700, 1500], size=64)]
+    if indirect:
+        c = Case(32 + d + kind, 2 * g, 2, d, kind=kind, indirect_lengths=occ, shuffle=True, duplicates=9)
+    else:
+        c = Case(33 + d + kind, 2 * g, 2, d, kind=kind, occupied=occ,
+                 begins=[int(b) for b in np.cumsum([0] + occ[:-1])])
+    assert c.n_slots == 64
+    check(*c.run(K, n_cu=256), *c.oracle())
+
+
 @pytest.mark.parametrize("d,g", [(64, 1), (64, 4), (64, 8), (128, 1), (128, 2), (128, 3), (128, 5), (128, 6),
                                  (128, 7), (128, 8), (256, 2), (256, 4), (256, 5), (256, 6), (256, 8),
                                  (128, 12), (128, 16), (256, 9), (256, 16)])
