@@ -20,7 +20,7 @@ Sources (web pages, cited by title and section):
   rows, which needs an attention mask) and item 9 (partial windows keep the
   running maximum, numerator and denominator and are merged afterwards).
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 
 * query head h reads KV head floor(h / G), G = n_q_heads / n_kv_heads;
 * scores are ``scale * q . k``; exponentials are natural (e^x); a partial's m
