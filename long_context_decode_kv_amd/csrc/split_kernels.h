@@ -56,6 +56,39 @@ __device__ __forceinline__ float dpp(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+// Values of x in the two 16-lane rows (S = 16) or 32-lane halves (S = 32)
+// that lane and lane ^ S sit in, lower one first, for every lane: one VALU
+// row swap instead of a trip through the LDS crossbar.  Combining (lo, hi)
+// in that order gives every lane the same bits.
+template <int S>
+__device__ __forceinline__ void row_pair(float x, float& lo, float& hi) {
+    // (elements of the returned pair are read with __uint_as_float: a
+    // __builtin_bit_cast of element 1 was compiled as element 0)
+    const uint32_t u = __float_as_uint(x);
+    if constexpr (S == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        lo = __uint_as_float(r[0]);
+        hi = __uint_as_float(r[1]);
+    } else {
+        static_assert(S == 32, "row pair stride");
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        lo = __uint_as_float(r[0]);
+        hi = __uint_as_float(r[1]);
+    }
+}
+template <int S>
+__device__ __forceinline__ float pair_sum(float x) {
+    float lo, hi;
+    row_pair<S>(x, lo, hi);
+    return lo + hi;
+}
+template <int S>
+__device__ __forceinline__ float pair_max(float x) {
+    float lo, hi;
+    row_pair<S>(x, lo, hi);
+    return fmaxf(lo, hi);
+}
+
 // Sum over each group of R consecutive lanes; every lane receives its group's sum.
 template <int R>
 __device__ __forceinline__ float group_sum(float x) {
@@ -63,8 +96,8 @@ __device__ __forceinline__ float group_sum(float x) {
     if constexpr (R >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
     if constexpr (R >= 8) x += dpp<0x141>(x);  // row_half_mirror
     if constexpr (R >= 16) x += dpp<0x140>(x); // row_mirror
-    if constexpr (R >= 32) x += __shfl_xor(x, 16);
-    if constexpr (R >= 64) x += __shfl_xor(x, 32);
+    if constexpr (R >= 32) x = pair_sum<16>(x);
+    if constexpr (R >= 64) x = pair_sum<32>(x);
     return x;
 }
 
@@ -74,8 +107,8 @@ __device__ __forceinline__ float wave_max(float x) {
     x = fmaxf(x, dpp<0x4E>(x));
     x = fmaxf(x, dpp<0x141>(x));
     x = fmaxf(x, dpp<0x140>(x));
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+    x = pair_max<16>(x);
+    return pair_max<32>(x);
 }
 __device__ __forceinline__ float wave_sum(float x) { return group_sum<64>(x); }
 
@@ -473,8 +506,9 @@ __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& 
         float M = kNegInf;
 #pragma unroll
         for (int k = part; k < NS; k += P) M = fmaxf(M, sm_m[k][h]);
-#pragma unroll
-        for (int o = 1; o < P; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+        // the P threads of a column are adjacent lanes of one quad: DPP
+        if constexpr (P >= 2) M = fmaxf(M, dpp<0xB1>(M));  // lane ^ 1
+        if constexpr (P >= 4) M = fmaxf(M, dpp<0x4E>(M));  // lane ^ 2
         float L = 0.f;
         float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -488,13 +522,19 @@ __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& 
             O.z = fmaf(ok.z, f, O.z);
             O.w = fmaf(ok.w, f, O.w);
         }
-#pragma unroll
-        for (int o = 1; o < P; o <<= 1) {
-            L += __shfl_xor(L, o);
-            O.x += __shfl_xor(O.x, o);
-            O.y += __shfl_xor(O.y, o);
-            O.z += __shfl_xor(O.z, o);
-            O.w += __shfl_xor(O.w, o);
+        if constexpr (P >= 2) {
+            L += dpp<0xB1>(L);
+            O.x += dpp<0xB1>(O.x);
+            O.y += dpp<0xB1>(O.y);
+            O.z += dpp<0xB1>(O.z);
+            O.w += dpp<0xB1>(O.w);
+        }
+        if constexpr (P >= 4) {
+            L += dpp<0x4E>(L);
+            O.x += dpp<0x4E>(O.x);
+            O.y += dpp<0x4E>(O.y);
+            O.z += dpp<0x4E>(O.z);
+            O.w += dpp<0x4E>(O.w);
         }
         if (part != 0) continue;
         if (single) {
@@ -1202,12 +1242,20 @@ __global__ __launch_bounds__(64 * W) void split_mfma_kernel(const SplitArgs a) {
         if constexpr (MQ) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
-                const int64_t mine = a.cell_pos ? (int64_t)praw[mb] : cell[mb] + a.pos_offset;
                 uint32_t bits = 0;
+                if (!IND && !a.cell_pos) {
+                    // contiguous cells without explicit positions: the
+                    // position of cell 4 * lq + e of the block is known here
+                    const int64_t p0 = sa.first + base + (mb * W + wave) * 16 + 4 * lq + a.pos_offset;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int64_t p = __shfl(mine, 4 * lq + e);
-                    bits |= (p <= qpos ? 1u : 0u) << e;
+                    for (int e = 0; e < 4; ++e) bits |= (p0 + e <= qpos ? 1u : 0u) << e;
+                } else {
+                    const int64_t mine = a.cell_pos ? (int64_t)praw[mb] : cell[mb] + a.pos_offset;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int64_t p = __shfl(mine, 4 * lq + e);
+                        bits |= (p <= qpos ? 1u : 0u) << e;
+                    }
                 }
                 vis[mb] = bits;
             }
@@ -1248,8 +1296,7 @@ __global__ __launch_bounds__(64 * W) void split_mfma_kernel(const SplitArgs a) {
         float mt = sc[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sc[e]);
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = pair_max<32>(pair_max<16>(mt));
         const bool bump = mt > m_h + kLazy;  // also the first finite score
         const float mn = bump ? mt : m_h;
         const float alpha = bump ? exp2_fast(m_h - mn) : 1.f;
@@ -1266,8 +1313,7 @@ __global__ __launch_bounds__(64 * W) void split_mfma_kernel(const SplitArgs a) {
             pa[e + 1] = pp.y;
             lsum = __builtin_amdgcn_fdot2(pp, ones, lsum, false);
         }
-        lsum += __shfl_xor(lsum, 16);
-        lsum += __shfl_xor(lsum, 32);
+        lsum = pair_sum<32>(pair_sum<16>(lsum));
         l_h = l_h * alpha + lsum;
         // O rows held by this lane are heads 4*lq + e: rescale with their alphas.
         if (__ballot(rescale) != 0) {
