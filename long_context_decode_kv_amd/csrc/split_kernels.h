@@ -1286,12 +1286,15 @@ __global__ __launch_bounds__(64 * W) void split_mfma_kernel(const SplitArgs a) {
         __builtin_amdgcn_sched_barrier(0);
 
         // Scores of head li for cells 4*lq + e of each block (log2 units).
+        // bit e: cell 4 * lq + e of the block is valid (the ballot's bit of
+        // the lane that loaded it) and visible to this lane's query row
+        const uint32_t live0 = (uint32_t)(vm0 >> (4 * lq)) & vis[0] & 0xFu;
+        const uint32_t live1 = (uint32_t)(vm1 >> (4 * lq)) & vis[1] & 0xFu;
         float sc[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int c = 4 * lq + e;
-            sc[e] = (((vm0 >> c) & 1) && ((vis[0] >> e) & 1)) ? sacc[0][e] * a.scale_log2 : kNegInf;
-            sc[4 + e] = (((vm1 >> c) & 1) && ((vis[1] >> e) & 1)) ? sacc[1][e] * a.scale_log2 : kNegInf;
+            sc[e] = ((live0 >> e) & 1u) ? sacc[0][e] * a.scale_log2 : kNegInf;
+            sc[4 + e] = ((live1 >> e) & 1u) ? sacc[1][e] * a.scale_log2 : kNegInf;
         }
         float mt = sc[0];
 #pragma unroll
