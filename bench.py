@@ -535,6 +535,8 @@ def main():
         sys.exit(2)
 
     import torch
+    from long_context_decode_kv_amd.build import ensure_built
+    ensure_built()
     from long_context_decode_kv_amd import kvdec as K
     torch.cuda.set_device(0)
     if args.copy_probe_mib:

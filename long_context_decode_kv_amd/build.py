@@ -100,5 +100,12 @@ def build(verbose=False, extra=()):
     return LIB
 
 
+def ensure_built():
+    """Build once if the libraries are missing (a fresh checkout); a built
+    tree is used as it is -- rebuild after changing a source."""
+    if not (os.path.exists(LIB) and os.path.exists(PROBE_LIB)):
+        build()
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -8,6 +8,8 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    from long_context_decode_kv_amd.build import ensure_built
+    ensure_built()
 
 
 def pytest_terminal_summary(terminalreporter):
