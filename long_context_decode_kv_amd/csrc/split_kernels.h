@@ -1428,8 +1428,8 @@ int launch_valu(const SplitArgs& a, void* stream) {
 
 template <int D, int RM, int KT, int VT, bool MQ>
 int launch_mfma(const SplitArgs& a, void* stream) {
-    // eight-wave workgroups for 16-row records at head_dim 128 (at 256 they
-    // would spill registers)
+    // eight-wave workgroups for 16-row records at head_dim 128 (at 256 the
+    // f16 and int8 instances would spill registers)
     if constexpr (D == 128 && RM == 16) {
         if (a.waves == 8) {
             if (a.plan)
