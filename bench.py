@@ -143,6 +143,7 @@ def algorithmic_bytes(n_cells_attended, hkv, d, kind, n_slots, hq, plan_entries=
 
 class ContiguousModel(Workload):
     split_cells = 0  # planner's choice unless --split-cells
+    kernel = 0       # vector-ALU split kernel: planner's choice unless --kernel
 
     def __init__(self, name, layers, hq, hkv, d, capacity, occupied, n_q=1):
         self.name, self.layers, self.hq, self.hkv, self.d = name, layers, hq, hkv, d
@@ -154,6 +155,8 @@ class ContiguousModel(Workload):
              "batch": 1, "kv_dtype": "f16", "cells_per_tile": 128}
         if self.split_cells:
             c["split_cells"] = self.split_cells
+        if self.kernel:
+            c["kernel_forced"] = {1: "streamed", 2: "one-shot"}[self.kernel]
         if self.n_q > 1:
             c.update({"query_rows_per_slot": self.n_q, "mask": "causal: row t at the position of occupied cell "
                                                                 "n - n_q + t (speculative verification)"})
@@ -175,7 +178,7 @@ class ContiguousModel(Workload):
             if layer % 8 == 7:
                 log(f"  generated {layer + 1}/{self.layers} layers")
         self.plan = K.plan(self.hq, self.hkv, self.d, 1, self.capacity, n_occupied=[self.occupied],
-                           n_queries=self.n_q, split_cells=self.split_cells)
+                           n_queries=self.n_q, split_cells=self.split_cells, kernel=self.kernel)
         self.ws = K.workspace(self.plan)
         self.q_pos = None
         if self.n_q > 1:
@@ -508,6 +511,20 @@ def committed_traffic(workload):
     return float(t.group(1))
 
 
+def kernel_label(wl, info):
+    """Name of the split-kernel instance a workload's plan launches."""
+    kv, vv = KIND[wl.kind], KIND[getattr(wl, "v_kind", wl.kind)]
+    g = wl.hq // wl.hkv
+    if info.get("matrix_cores"):
+        return "split_mfma_kernel<%d,rows %d,%s,%s,%d waves>" % (wl.d, g * getattr(wl, "n_q", 1), kv, vv,
+                                                                 info.get("waves", 4))
+    if info.get("kernel") == 2:
+        cw = (-(-info["split_cells"] // 8) + 1) & ~1
+        jm = -(-cw // 8)
+        return "split_oneshot_kernel<%d,%d>" % (g, 2 if jm <= 2 else (4 if jm <= 4 else 7))
+    return "split_kernel<%d,%d,%s,%s,%d waves>" % (wl.d, g, kv, vv, info.get("waves", 4))
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -522,6 +539,8 @@ def main():
     ap.add_argument("--no-read-ceiling", action="store_true", help="skip the streaming-read ceiling (profiling runs)")
     ap.add_argument("--split-cells", type=int, default=0,
                     help="cells per split for the contiguous-model workloads (multiple of 32; 0: planner)")
+    ap.add_argument("--kernel", default="auto", choices=["auto", "streamed", "oneshot"],
+                    help="vector-ALU split kernel for the contiguous-model workloads (default: the planner's choice)")
     ap.add_argument("--tail-chunk", type=int, default=0,
                     help="host-tail cells per chunk (rolling workloads; 0: the whole tail in one chunk)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -548,6 +567,7 @@ def main():
         del src, dst
     RollingWindow.chunk = args.tail_chunk
     ContiguousModel.split_cells = args.split_cells
+    ContiguousModel.kernel = {"auto": 0, "streamed": 1, "oneshot": 2}[args.kernel]
     wl = WORKLOADS[args.workload]()
     log(f"[bench] workload {wl.name}: generating inputs on the device")
     wl.setup(K, torch, 1001)
@@ -675,12 +695,7 @@ def main():
                        tiles_per_split=info["tiles_per_split"], cells_per_split=info["split_cells"]),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": (("split_mfma_kernel<%d,rows %d,%s,%s,%d waves>" % (
-                         wl.d, wl.hq // wl.hkv * getattr(wl, "n_q", 1), KIND[wl.kind],
-                         KIND[getattr(wl, "v_kind", wl.kind)], info.get("waves", 4))) if info.get("matrix_cores") else
-                         ("split_kernel<%d,%d,%s,%s,%d waves>" % (wl.d, wl.hq // wl.hkv, KIND[wl.kind],
-                                                                  KIND[getattr(wl, "v_kind", wl.kind)],
-                                                                  info.get("waves", 4)))),
+                     "kernel": kernel_label(wl, info),
                      "algorithmic_bytes_per_launch": bytes_launch, "launches_per_step": launches_per_step,
                      "avg_launch_us": round(avg_us, 3), "isolated_launch_event_us": round(bracketed_us, 3),
                      "read_ceiling": ceiling},

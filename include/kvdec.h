@@ -77,6 +77,11 @@ extern "C" {
 /* Largest slot count a single plan accepts. */
 #define KVDEC_MAX_SLOTS 64
 
+/* kvdec_problem.kernel */
+#define KVDEC_KERNEL_AUTO 0
+#define KVDEC_KERNEL_STREAMED 1
+#define KVDEC_KERNEL_ONESHOT 2
+
 /*
  * Problem description, read by kvdec_plan (host memory only; nothing is
  * retained after the call returns).
@@ -142,6 +147,16 @@ extern "C" {
  *   32-cell split boundaries itself for the vector-ALU kernel, so that a
  *   short context can still give every compute unit one equal split.
  *
+ * kernel: which split kernel serves a one-query-row problem on the vector
+ *   ALU (G <= 5).  KVDEC_KERNEL_AUTO lets the planner choose;
+ *   KVDEC_KERNEL_STREAMED forces the kernel that streams a split in steps;
+ *   KVDEC_KERNEL_ONESHOT asks for the one-shot kernel, which issues every
+ *   load of a split at workgroup entry and needs head_dim 128, f16 K and V,
+ *   contiguous cells and splits of at most 448 cells (KVDEC_E_UNSUPPORTED
+ *   otherwise).  The planner picks the one-shot kernel when those hold and
+ *   one split per compute unit covers the cache; results differ between
+ *   the kernels only in floating-point summation order.
+ *
  * n_queries: query rows per slot, 1..8 (0 means 1).  Several rows per slot
  *   are the verification step of speculative decoding: split decoding serves
  *   up to 8 query rows, and such a call carries an attention mask ("KVARN KV
@@ -175,6 +190,8 @@ typedef struct kvdec_problem {
     int32_t tail_zero_copy; /* 1: kernels read the host tail in place */
     int32_t split_cells;    /* cells per split, multiple of 32; 0: tiles_per_split */
     const int32_t* max_records; /* [n_slots]: device-built indirect plan, see kvdec_build_cells */
+    int32_t kernel;         /* KVDEC_KERNEL_AUTO (0), _STREAMED (1) or _ONESHOT (2) */
+    int32_t pad0;
 } kvdec_problem;
 
 /* Opaque, immutable plan. */
@@ -318,6 +335,8 @@ typedef struct kvdec_plan_info {
     int32_t split_cells;      /* largest position count of any split */
     int32_t split_unit;       /* split boundaries fall on multiples of this many positions */
     int32_t waves;            /* waves per workgroup of the resident launch (4 or 8) */
+    int32_t kernel;           /* KVDEC_KERNEL_STREAMED or _ONESHOT for the vector-ALU kernels, 0 on matrix cores */
+    int32_t pad0;
 } kvdec_plan_info;
 
 int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info);

@@ -43,6 +43,7 @@ void common_args(const kvdec_plan_t& p, const kvdec_io& io, kvdec::SplitArgs& a)
     a.group = p.group;
     a.split_unit = p.split_unit;
     a.waves = p.waves;
+    a.oneshot = p.oneshot;
     // positions are used with several query rows per slot only
     a.q_pos = p.n_q > 1 ? io.q_pos : nullptr;
     a.cell_pos = p.n_q > 1 ? io.cell_pos : nullptr;
@@ -131,6 +132,8 @@ int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info) {
     info->split_cells = plan->max_split_cells;
     info->split_unit = plan->split_unit;
     info->waves = plan->waves;
+    info->kernel = plan->mfma ? 0 : (plan->oneshot > 0 ? KVDEC_KERNEL_ONESHOT : KVDEC_KERNEL_STREAMED);
+    info->pad0 = 0;
     return KVDEC_OK;
 }
 
@@ -379,6 +382,7 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
             t.slot[0].n_units = tiles;  // whole-tile splits
             t.split_unit = kvdec::kTile;
             t.waves = 4;
+            t.oneshot = 0;
             t.slot[0].n_splits = splits;
             t.slot[0].wg_begin = 0;
             t.slot[0].part_begin = 0;

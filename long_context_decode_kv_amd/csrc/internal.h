@@ -72,6 +72,13 @@ constexpr int merge_clusters(int n_splits, int chunk) {
     return n_splits <= 2 * chunk ? 1 : (n_splits + chunk - 1) / chunk;
 }
 
+// Running partial of the window + tail chain: m2 [rows], l [rows], then o
+// [rows][D] at this float offset -- 2 * rows rounded up to a multiple of 4,
+// so the o rows stay 16-byte aligned (they are read and written as float4)
+// whatever the row count.
+inline constexpr int64_t acc_o_offset(int64_t rows) { return (2 * rows + 3) / 4 * 4; }
+inline constexpr int64_t acc_floats(int64_t rows, int64_t head_dim) { return acc_o_offset(rows) + rows * head_dim; }
+
 // Per-slot launch description, passed to the split kernel by value.
 struct SlotArg {
     int64_t first;       // contiguous: first cell; indirect: first plan entry
@@ -112,7 +119,8 @@ struct SplitArgs {
     float* po;
     const float* acc_in;     // running partial merged in by the last workgroup, or null
     float* acc_out;          // running partial written for slots with to_acc
-    int32_t acc_rows;        // rows of a running partial: m2 [rows], l [rows], o [rows][D]
+    int32_t acc_rows;        // rows of a running partial: m2 [rows], l [rows], o [rows][D] at acc_o_offset(rows)
+    int32_t oneshot;         // > 0: the one-shot kernel with this many 8-cell loads per lane (planner's choice)
     int32_t n_q;             // query rows per slot (q, out, lse rows: [slot][n_q][Hq])
     const int32_t* q_pos;    // [slots][n_q] positions of the query rows (n_q > 1)
     const int32_t* cell_pos; // [capacity] positions of device cells, or null: cell index + pos_offset
@@ -196,6 +204,7 @@ struct kvdec_plan {
     int32_t split_unit = 0;        // positions per split unit: 32 (vector-ALU kernel) or 128
     int32_t max_split_cells = 0;   // largest split, in positions
     int32_t waves = 4;             // waves per split workgroup (4 or 8)
+    int32_t oneshot = 0;           // resident launch on the one-shot kernel: 8-cell loads per lane (2, 4 or 7)
     bool mfma = false;             // served by the matrix-core kernel
     int64_t n_tiles = 0;
     std::vector<int32_t> cells;      // indirect entries (host-built plans)

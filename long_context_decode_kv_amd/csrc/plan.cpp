@@ -215,13 +215,46 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
     };
     auto one_round = [&](int64_t w) { return 4 * w >= 3 * (int64_t)n_cu && w <= n_cu; };
     const bool auto_split = p.split_cells == 0 && p.tiles_per_split == 0;
+    if (p.kernel != KVDEC_KERNEL_AUTO && p.kernel != KVDEC_KERNEL_STREAMED && p.kernel != KVDEC_KERNEL_ONESHOT) {
+        err = "kernel must be KVDEC_KERNEL_AUTO, _STREAMED or _ONESHOT";
+        return KVDEC_E_INVALID;
+    }
+    // One-shot kernel: head_dim 128, f16 K and V, G <= 5, one query row,
+    // contiguous cells, splits of at most kOneShotCells.  Chosen when one
+    // split per compute unit covers the cache: the split length that spreads
+    // every (slot, KV head) over the compute units, on 32-cell boundaries,
+    // at least 64 cells.
+    constexpr int64_t kOneShotCells = 448;
+    const bool oneshot_ok = !mfma && !indirect && n_q == 1 && group <= 5 && p.head_dim == 128 &&
+                            p.k_type == KVDEC_F16 && p.v_type == KVDEC_F16;
+    int64_t oneshot_cells = 0;
+    if (oneshot_ok && p.kernel != KVDEC_KERNEL_STREAMED) {
+        if (p.split_cells > 0 || p.tiles_per_split > 0) {
+            oneshot_cells = p.split_cells > 0 ? p.split_cells : (int64_t)p.tiles_per_split * kTile;
+        } else {
+            int64_t cells = 0;
+            for (auto& sa : plan.slots) cells += sa.n;
+            const int64_t c = std::max<int64_t>(64, ceil_div(ceil_div(cells * p.n_kv_heads, n_cu), kSplitUnit) * kSplitUnit);
+            oneshot_cells = c;
+        }
+        const bool fits = oneshot_cells <= kOneShotCells && wgs_for(oneshot_cells) <= std::max<int64_t>(n_cu, p.n_kv_heads);
+        if (p.kernel == KVDEC_KERNEL_AUTO && !(auto_split && fits)) oneshot_cells = 0;
+        if (p.kernel == KVDEC_KERNEL_ONESHOT && oneshot_cells > kOneShotCells) {
+            err = "the one-shot kernel needs splits of at most 448 cells";
+            return KVDEC_E_UNSUPPORTED;
+        }
+    }
+    if (p.kernel == KVDEC_KERNEL_ONESHOT && !oneshot_ok) {
+        err = "the one-shot kernel needs head_dim 128, f16 K and V, G <= 5, one query row and contiguous cells";
+        return KVDEC_E_UNSUPPORTED;
+    }
     // Five f16 query rows at head_dim 128 over short contexts (splits of at
     // most two tiles at two workgroups per CU) run faster on the matrix-core
     // kernel with four-tile splits (16384-cell layer 22.6 -> 20.8 us); long
     // splits stay on the vector-ALU kernel, whose LDS staging wins there.
-    if (!mfma && group == 5 && n_q == 1 && p.head_dim == 128 && p.k_type == KVDEC_F16 &&
-        p.v_type == KVDEC_F16 && auto_split && ceil_div(total_tiles, 2 * (int64_t)n_cu) <= 2 &&
-        one_round(wgs_for(4 * kTile)))
+    if (!mfma && oneshot_cells == 0 && p.kernel == KVDEC_KERNEL_AUTO && group == 5 && n_q == 1 &&
+        p.head_dim == 128 && p.k_type == KVDEC_F16 && p.v_type == KVDEC_F16 && auto_split &&
+        ceil_div(total_tiles, 2 * (int64_t)n_cu) <= 2 && one_round(wgs_for(4 * kTile)))
         mfma = true;
     plan.mfma = mfma;
     const int rec_rows = record_rows_of(mfma, group, n_q);
@@ -237,7 +270,10 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
     for (auto& sa : plan.slots) sa.n_units = (int32_t)ceil_div(sa.n, unit);
     plan.n_tiles = total_tiles;
     int64_t ups = 0;  // units per split
-    if (p.split_cells > 0) {
+    if (oneshot_cells > 0) {
+        ups = ceil_div(oneshot_cells, unit);
+        plan.waves = 8;
+    } else if (p.split_cells > 0) {
         ups = ceil_div((int64_t)p.split_cells, unit);
     } else if (p.tiles_per_split > 0) {
         ups = (int64_t)p.tiles_per_split * upt;
@@ -300,6 +336,13 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
         plan.max_split_cells = std::max<int32_t>(plan.max_split_cells, (int32_t)longest);
     }
     plan.max_tiles_per_split = (int32_t)ceil_div((int64_t)plan.max_split_cells, kTile);
+    if (oneshot_cells > 0) {
+        // 8-cell loads per lane: a wave takes an even number of cells, at
+        // most 8 of them per load
+        const int64_t cw = (ceil_div(plan.max_split_cells, 8) + 1) & ~1ll;
+        const int64_t jm = ceil_div(cw, 8);
+        plan.oneshot = jm <= 2 ? 2 : (jm <= 4 ? 4 : 7);
+    }
     plan.n_workgroups = (int32_t)wgs;
     plan.n_part_records = (int32_t)wgs;
     int64_t clusters = 0;
@@ -381,9 +424,9 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
     if (has_tail) {
         const size_t rows = (size_t)p.n_slots * n_q * p.n_q_heads;
         plan.off_acc0 = off;
-        off = align_up(off + sizeof(float) * rows * (D + 2), 256);
+        off = align_up(off + sizeof(float) * (size_t)acc_floats((int64_t)rows, (int64_t)D), 256);
         plan.off_acc1 = off;
-        off = align_up(off + sizeof(float) * rows * (D + 2), 256);
+        off = align_up(off + sizeof(float) * (size_t)acc_floats((int64_t)rows, (int64_t)D), 256);
         const size_t cc = (size_t)plan.chunk_cells * p.n_kv_heads;
         plan.ring_k = 0;
         size_t r = align_up(cc * (size_t)row_bytes(p.k_type, p.head_dim), 256);

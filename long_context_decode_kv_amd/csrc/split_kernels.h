@@ -264,7 +264,7 @@ __device__ __forceinline__ void emit4(const SplitArgs& a, int to_acc, int64_t ro
             acc[row] = M2;
             acc[a.acc_rows + row] = L;
         }
-        *reinterpret_cast<float4*>(acc + 2 * (int64_t)a.acc_rows + row * D + d0) = O;
+        *reinterpret_cast<float4*>(acc + acc_o_offset(a.acc_rows) + row * D + d0) = O;
         return;
     }
     const bool empty = !(L > 0.f);
@@ -286,7 +286,7 @@ __device__ __forceinline__ void emit4(const SplitArgs& a, int to_acc, int64_t ro
 __device__ __forceinline__ void merge_acc_in(const SplitArgs& a, int64_t row, int d0, int D, float& M, float& L,
                                              float4& O) {
     if (!a.acc_in) return;
-    const float4 ob = *reinterpret_cast<const float4*>(a.acc_in + 2 * (int64_t)a.acc_rows + row * D + d0);
+    const float4 ob = *reinterpret_cast<const float4*>(a.acc_in + acc_o_offset(a.acc_rows) + row * D + d0);
     merge4(M, L, O, a.acc_in[row], a.acc_in[a.acc_rows + row], ob);
 }
 
@@ -481,6 +481,10 @@ __device__ __forceinline__ bool last_arrival(uint32_t* ticket, int expected, int
     return sm_last != 0;
 }
 
+template <int D, int G, int NT>
+__device__ __forceinline__ void arrive_and_merge(const SplitArgs& a, const SlotArg& sa, int s, int g, int split,
+                                                 const RowMap& rm, int& sm_last);
+
 // End of a split: merge the NS cell streams left in LDS (m2, l, o per
 // stream and head) into the split's result; a single-split group writes its
 // output directly, otherwise the split's record is published and the last
@@ -551,7 +555,16 @@ __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& 
         }
     }
     if (single) return;
+    arrive_and_merge<D, G, NT>(a, sa, s, g, split, rm, sm_last);
+}
 
+// After a split's record stores: count the arrival and, in the last
+// workgroup of the (slot, KV head) -- or of its cluster, then of the cluster
+// records -- merge the records into the outputs.
+template <int D, int G, int NT>
+__device__ __forceinline__ void arrive_and_merge(const SplitArgs& a, const SlotArg& sa, int s, int g, int split,
+                                                 const RowMap& rm, int& sm_last) {
+    const int n_splits = sa.n_splits;
     // Records are published (stores complete) before the arrival is counted.
     wait_stores();
     __syncthreads();
@@ -957,6 +970,320 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 
     const RowMap rm{row0, G, a.n_q_heads, G};
     finish_split<D, G, NS, D + 16, 64 * W>(a, sa, s, g, split, rm, sm_m, sm_l, sm_o, sm_last);
+}
+
+// Output of one column d of a row after the merge (the scalar form of emit4).
+__device__ __forceinline__ void emit1(const SplitArgs& a, int to_acc, int64_t row, int d, int D, float M2, float L,
+                                      float O) {
+    if (to_acc) {
+        float* acc = a.acc_out;
+        if (d == 0) {
+            acc[row] = M2;
+            acc[a.acc_rows + row] = L;
+        }
+        acc[acc_o_offset(a.acc_rows) + row * D + d] = O;
+        return;
+    }
+    const bool empty = !(L > 0.f);
+    if (a.out) a.out[row * D + d] = empty ? 0.f : O / L;
+    if (d == 0) {
+        if (a.lse) a.lse[row] = empty ? kNegInf : (M2 + log2f(L)) * kLn2;
+        if (a.pm) {
+            a.pm[row] = empty ? kNegInf : M2 * kLn2;
+            a.pl[row] = L;
+        }
+    }
+    if (a.po) a.po[row * D + d] = O;
+}
+
+__device__ __forceinline__ void merge_acc_in1(const SplitArgs& a, int64_t row, int d, int D, float& M, float& L,
+                                              float& O) {
+    if (!a.acc_in) return;
+    const float mb = a.acc_in[row], lb = a.acc_in[a.acc_rows + row];
+    const float ob = a.acc_in[acc_o_offset(a.acc_rows) + row * D + d];
+    const float mn = fmaxf(M, mb);
+    const float fa = (M == kNegInf) ? 0.f : exp2_fast(M - mn);
+    const float fb = (mb == kNegInf) ? 0.f : exp2_fast(mb - mn);
+    L = L * fa + lb * fb;
+    O = O * fa + ob * fb;
+    M = mn;
+}
+
+// ---------------------------------------------------------------------------
+// One-shot split kernel (head_dim 128, f16 K and V, G <= 5 query rows per KV
+// head, contiguous cells) for splits short enough that a workgroup's whole
+// share of the cache fits in its registers.  Every load of the split is
+// issued at workgroup entry -- the query rows, then K, then V, all 16-byte
+// loads into registers -- so each compute unit's whole share is requested at
+// once and no load waits on an earlier step's arithmetic.  (Plain loads only:
+// they complete in order, so each use waits for exactly its own data.)  Wave
+// w owns a contiguous block of the split's cells:
+//   * scores: 8 lanes per cell, 16 elements each (two 16-byte chunks of the
+//     row), combined with DPP; all of the wave's scores are known before any
+//     weight is formed, so the wave's maximum per head is exact and the wave
+//     is a single softmax stream;
+//   * weights 2^(s - m + 15), rounded to f16, go to LDS as pairs of
+//     consecutive cells;
+//   * V rows go to a per-wave LDS tile as their loads land, and P.V reads
+//     them column-wise: lane l owns output columns 2l and 2l+1 of every head
+//     and walks the wave's cells in pairs, so a wave's P.V needs no
+//     reduction across lanes;
+//   * the eight wave streams are merged through LDS, one output column per
+//     thread, and the split's record is published as by the other kernels.
+// ---------------------------------------------------------------------------
+template <int G, int JM>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void split_oneshot_kernel(const SplitArgs a) {
+    constexpr int D = 128, W = 8;
+    constexpr int R = 8;                 // lanes per cell for the scores
+    constexpr int CPL = 64 / R;          // cells per wave load
+    constexpr int NC = 2;                // 16-byte chunks per lane and cell row
+    constexpr int CW = JM * CPL;         // most cells per wave
+    constexpr int VSTR = 2 * D + 16;     // bytes per staged V row (padded against bank conflicts)
+    constexpr int GP = (G + 3) / 4 * 4;  // dwords per weight-pair entry
+    constexpr int VBYTES = W * CW * VSTR;
+    constexpr int MBYTES = W * G * D * 4;
+    static_assert(MBYTES <= VBYTES, "merge area inside the V tiles");
+
+    // V tiles of the waves; after the last P.V, the waves' o rows for the merge
+    __shared__ __align__(16) unsigned char v_lds[VBYTES];
+    __shared__ __align__(16) uint32_t p_lds[W][CW / 2][GP];
+    __shared__ __align__(16) uint32_t q_lds[W][G * D / 2];  // each wave's copy of the query rows, f16 pairs
+    __shared__ float mg_m[W][G], mg_l[W][G];
+    __shared__ int sm_last;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int sub = lane % R;
+    const int cl = lane / R;
+
+    const int wg = blockIdx.x;
+    int s = 0;
+    while (s + 1 < a.n_slots && a.slot[s + 1].wg_begin <= wg) ++s;
+    const SlotArg sa = a.slot[s];
+    const int local = wg - sa.wg_begin;
+    const int split = local / a.n_kv_heads;
+    const int g = local - split * a.n_kv_heads;
+    const int64_t pos_begin = (((int64_t)split * sa.n_units) / sa.n_splits) * a.split_unit;
+    const int64_t span_end = (((int64_t)(split + 1) * sa.n_units) / sa.n_splits) * a.split_unit;
+    const int64_t pos_end = span_end < sa.n ? span_end : sa.n;
+    const int n = pos_end > pos_begin ? (int)(pos_end - pos_begin) : 0;
+    // wave w: cells w * cw ... of the split, cw even and at most CW (the
+    // planner keeps splits within W * CW cells; the clamp only keeps LDS
+    // accesses in bounds)
+    int cw = ((n + W - 1) / W + 1) & ~1;
+    cw = cw < CW ? cw : CW;
+    const int w0 = wave * cw;
+    const int cnt = n - w0 <= 0 ? 0 : (n - w0 > cw ? cw : n - w0);
+    const int hq0 = g * G;
+    const int64_t row0 = (int64_t)(a.slot_base + s) * a.n_q_heads + hq0;
+    unsigned char* vt = v_lds + wave * CW * VSTR;
+
+    float m_w[G], l_w[G], o[G][2];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m_w[h] = kNegInf;
+        l_w[h] = 0.f;
+        o[h][0] = o[h][1] = 0.f;
+    }
+
+    if (cnt > 0) {
+        // the wave's first cell; loads past the wave's cells read it instead
+        const int64_t c0 = sa.first + pos_begin + w0;
+        const uint8_t* kbase = a.k + (int64_t)g * a.k_hs;
+        const uint8_t* vbase = a.v + (int64_t)g * a.v_hs;
+
+        // 1. loads: the group's G query rows (contiguous, 2G floats per lane,
+        // each element loaded once per wave), then the K and V chunks of the
+        // lane's cells 8j + cl
+        float2 qf[G];
+        {
+            const float2* qp = reinterpret_cast<const float2*>(a.q + row0 * D) + lane * G;
+#pragma unroll
+            for (int i = 0; i < G; ++i) qf[i] = qp[i];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        Chunk<16> kc[JM][NC], vc[JM][NC];
+#pragma unroll
+        for (int j = 0; j < JM; ++j) {
+            const int r = j * CPL + cl;
+            const uint8_t* kr = kbase + (c0 + (r < cnt ? r : 0)) * a.k_cs;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) kc[j][c] = load_chunk<16>(kr + (c * R + sub) * 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < JM; ++j) {
+            const int r = j * CPL + cl;
+            const uint8_t* vr = vbase + (c0 + (r < cnt ? r : 0)) * a.v_cs;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) vc[j][c] = load_chunk<16>(vr + (c * R + sub) * 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // 2. query rows -> f16 pairs in the wave's LDS copy, then this lane's
+        // pairs: elements (c * 8 + sub) * 8 .. + 8 of each row
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+            q_lds[wave][lane * G + i] = __builtin_bit_cast(uint32_t, h2{(_Float16)qf[i].x, (_Float16)qf[i].y});
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        h2 qh[G][NC * 4];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const uint4 x = *reinterpret_cast<const uint4*>(&q_lds[wave][h * (D / 2) + (c * R + sub) * 4]);
+                qh[h][c * 4 + 0] = as_h2(x.x);
+                qh[h][c * 4 + 1] = as_h2(x.y);
+                qh[h][c * 4 + 2] = as_h2(x.z);
+                qh[h][c * 4 + 3] = as_h2(x.w);
+            }
+
+        // 3. scores (log2 units) of the lane's cells, and the wave maximum
+        float sc[JM][G];
+#pragma unroll
+        for (int j = 0; j < JM; ++j) {
+            float acc[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) acc[h] = 0.f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const h2 kp = as_h2(kc[j][c].w[i]);
+#pragma unroll
+                    for (int h = 0; h < G; ++h) acc[h] = __builtin_amdgcn_fdot2(kp, qh[h][c * 4 + i], acc[h], false);
+                }
+            const bool live = j * CPL + cl < cnt;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float full = group_sum<R>(acc[h]);
+                sc[j][h] = live ? full * a.scale_log2 : kNegInf;
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float mx = sc[0][h];
+#pragma unroll
+            for (int j = 1; j < JM; ++j) mx = fmaxf(mx, sc[j][h]);
+            mx = fmaxf(mx, dpp<0x128>(mx));  // lane ^ 8: the other cell group of the row
+            m_w[h] = pair_max<32>(pair_max<16>(mx));
+        }
+
+        // 4. weights, rounded to f16 (toward zero); l from the rounded values;
+        // pairs of cells (8j + cl, 8j + cl + 1) to LDS from the even groups
+#pragma unroll
+        for (int j = 0; j < JM; ++j) {
+            uint32_t pk[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float p = (sc[j][h] == kNegInf) ? 0.f : exp2_fast(sc[j][h] - m_w[h] + kPOff);
+                const float pn = dpp<0x128>(p);
+                const h2 pp = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p, pn));
+                l_w[h] += (float)pp.x;
+                pk[h] = __builtin_bit_cast(uint32_t, pp);
+            }
+            if ((cl & 1) == 0 && sub == 0) {
+                uint32_t* dst = &p_lds[wave][j * (CPL / 2) + cl / 2][0];
+#pragma unroll
+                for (int h = 0; h < G; ++h) dst[h] = pk[h];
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float x = l_w[h];
+            x += dpp<0x128>(x);
+            l_w[h] = pair_sum<32>(pair_sum<16>(x));
+        }
+
+        // 5. per wave load j: its 8 V rows -> LDS, then P.V over them (lane
+        // owns columns 2 lane, 2 lane + 1), the four row pairs at once (rows
+        // past the wave's cells hold finite data of its first cell and carry
+        // weight 0), so the block's LDS reads all leave before its products
+#pragma unroll
+        for (int j = 0; j < JM; ++j) {
+            if (j * CPL >= cnt) break;  // uniform over the wave
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                *reinterpret_cast<uint4*>(vt + (j * CPL + cl) * VSTR + (c * R + sub) * 16) =
+                    make_uint4(vc[j][c].w[0], vc[j][c].w[1], vc[j][c].w[2], vc[j][c].w[3]);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            uint32_t va[CPL / 2], vb[CPL / 2];
+            uint4 pw[CPL / 2][GP / 4];
+#pragma unroll
+            for (int qq = 0; qq < CPL / 2; ++qq) {
+                const int pr = j * (CPL / 2) + qq;
+                va[qq] = *reinterpret_cast<const uint32_t*>(vt + (2 * pr) * VSTR + 4 * lane);
+                vb[qq] = *reinterpret_cast<const uint32_t*>(vt + (2 * pr + 1) * VSTR + 4 * lane);
+#pragma unroll
+                for (int x = 0; x < GP / 4; ++x) pw[qq][x] = *reinterpret_cast<const uint4*>(&p_lds[wave][pr][4 * x]);
+            }
+#pragma unroll
+            for (int qq = 0; qq < CPL / 2; ++qq) {
+                const h2 lo = as_h2(__builtin_amdgcn_perm(vb[qq], va[qq], 0x05040100u));
+                const h2 hi = as_h2(__builtin_amdgcn_perm(vb[qq], va[qq], 0x07060302u));
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const uint4& q4 = pw[qq][h / 4];
+                    const uint32_t wb = (h % 4 == 0) ? q4.x : (h % 4 == 1) ? q4.y : (h % 4 == 2) ? q4.z : q4.w;
+                    const h2 w2 = as_h2(wb);
+                    o[h][0] = __builtin_amdgcn_fdot2(lo, w2, o[h][0], false);
+                    o[h][1] = __builtin_amdgcn_fdot2(hi, w2, o[h][1], false);
+                }
+            }
+        }
+    }
+
+    // 6. merge the wave streams: thread t -> column t of the group's rows
+    __syncthreads();  // every wave is done with its V tile
+    float (*mg_o)[G][D] = reinterpret_cast<float (*)[G][D]>(v_lds);
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            mg_m[wave][h] = m_w[h];
+            mg_l[wave][h] = l_w[h] * kPOffInv;
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+        *reinterpret_cast<float2*>(&mg_o[wave][h][2 * lane]) = make_float2(o[h][0] * kPOffInv, o[h][1] * kPOffInv);
+    __syncthreads();
+
+    const RowMap rm{row0, G, a.n_q_heads, G};
+    const bool single = sa.n_splits == 1;
+    const int64_t rec = sa.part_begin + (int64_t)g * sa.n_splits + split;
+    const __amdgpu_buffer_rsrc_t rs = part_rsrc(a);
+    for (int t = tid; t < G * D; t += 64 * W) {
+        const int h = t / D, d = t - h * D;
+        float M = kNegInf;
+#pragma unroll
+        for (int w = 0; w < W; ++w) M = fmaxf(M, mg_m[w][h]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const float mw = mg_m[w][h];
+            const float f = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);
+            L = fmaf(mg_l[w][h], f, L);
+            O = fmaf(mg_o[w][h][d], f, O);
+        }
+        if (single) {
+            merge_acc_in1(a, rm.row(h), d, D, M, L, O);
+            emit1(a, sa.to_acc, rm.row(h), d, D, M, L, O);
+        } else {
+            // (the builtin takes the 32 bits as an unsigned int: pass them, not a converted value)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O), rs, (int)(((rec * G + h) * D + d) * 4), 0, 0x10);
+            if (d == 0) {
+                st_dev(a.part_m + rec * G + h, M);
+                st_dev(a.part_l + rec * G + h, L);
+            }
+        }
+    }
+    if (single) return;
+    arrive_and_merge<D, G, 64 * W>(a, sa, s, g, split, rm, sm_last);
 }
 
 // ---------------------------------------------------------------------------
@@ -1413,6 +1740,19 @@ __global__ __launch_bounds__(64 * W) void split_mfma_kernel(const SplitArgs a) {
 
 template <int D, int G, int KT, int VT>
 int launch_valu(const SplitArgs& a, void* stream) {
+    // one-shot splits: head_dim 128, f16 K and V, up to 5 query rows
+    if constexpr (D == 128 && G <= 5 && KT == KVDEC_F16 && VT == KVDEC_F16) {
+        if (a.oneshot > 0 && !a.plan) {
+            const hipStream_t st = (hipStream_t)stream;
+            if (a.oneshot <= 2)
+                hipLaunchKernelGGL((split_oneshot_kernel<G, 2>), dim3(a.n_workgroups), dim3(512), 0, st, a);
+            else if (a.oneshot <= 4)
+                hipLaunchKernelGGL((split_oneshot_kernel<G, 4>), dim3(a.n_workgroups), dim3(512), 0, st, a);
+            else
+                hipLaunchKernelGGL((split_oneshot_kernel<G, 7>), dim3(a.n_workgroups), dim3(512), 0, st, a);
+            return (int)hipGetLastError();
+        }
+    }
     // eight-wave workgroups: head_dim up to 128 (their stream-merge area fits LDS)
     if constexpr (D <= 128 && KT == KVDEC_F16 && VT == KVDEC_F16) {
         if (a.waves == 8) {

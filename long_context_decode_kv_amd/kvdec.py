@@ -27,6 +27,7 @@ LIB_PATH = _LIB_PATH
 F16, Q8_B32, Q4_B32 = 0, 1, 2
 OK, E_INVALID, E_RANGE, E_UNSUPPORTED, E_WORKSPACE, E_NOMEM, E_DEVICE = 0, -1, -2, -3, -4, -5, -6
 TILE_CELLS = 128
+KERNEL_AUTO, KERNEL_STREAMED, KERNEL_ONESHOT = 0, 1, 2
 MAX_SLOTS = 64
 
 _p = ctypes.c_void_p
@@ -43,7 +44,7 @@ class Problem(ctypes.Structure):
         ("tail_begin", _p), ("n_tail", _p),
         ("tail_capacity_cells", _i64), ("tail_chunk_cells", _i64),
         ("tail_ring_depth", _i32), ("n_queries", _i32), ("tail_zero_copy", _i32), ("split_cells", _i32),
-        ("max_records", _p),
+        ("max_records", _p), ("kernel", _i32), ("pad0", _i32),
     ]
 
 
@@ -67,7 +68,7 @@ class PlanInfo(ctypes.Structure):
         ("n_slots", _i32), ("group", _i32), ("n_workgroups", _i32), ("tiles_per_split", _i32),
         ("n_tiles", _i64), ("n_entries", _i64), ("n_tail_chunks", _i64), ("workspace_bytes", _i64),
         ("n_queries", _i32), ("matrix_cores", _i32), ("split_cells", _i32), ("split_unit", _i32),
-        ("waves", _i32),
+        ("waves", _i32), ("kernel", _i32), ("pad0", _i32),
     ]
 
 
@@ -185,11 +186,12 @@ class Plan:
 def plan(n_q_heads, n_kv_heads, head_dim, n_slots, capacity_cells, *, k_type=F16, v_type=F16, scale=None,
          n_occupied=None, cell_begin=None, cells=None, n_tail=None, tail_begin=None, tail_capacity_cells=0,
          tail_chunk_cells=0, tail_ring_depth=0, tiles_per_split=0, n_cu=0, n_queries=1, tail_zero_copy=False,
-         max_records=None, split_cells=0):
+         max_records=None, split_cells=0, kernel=KERNEL_AUTO):
     """Build a plan.  ``cells`` is a list of per-slot raw cell arrays
     (indirect mode); otherwise ``n_occupied`` (and optional ``cell_begin``)
     give contiguous ranges.  ``n_queries`` query rows per slot.  ``n_cu=0``
-    asks the current HIP device."""
+    asks the current HIP device.  ``kernel`` picks the vector-ALU split
+    kernel (KERNEL_AUTO, KERNEL_STREAMED, KERNEL_ONESHOT)."""
     keep = []
 
     def arr64(x):
@@ -205,6 +207,7 @@ def plan(n_q_heads, n_kv_heads, head_dim, n_slots, capacity_cells, *, k_type=F16
     p.scale = (1.0 / np.sqrt(head_dim)) if scale is None else scale
     p.tiles_per_split = tiles_per_split
     p.split_cells = split_cells
+    p.kernel = kernel
     p.capacity_cells = capacity_cells
     p.cell_begin = arr64(cell_begin)
     p.n_occupied = arr64(n_occupied)

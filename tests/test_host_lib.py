@@ -150,12 +150,20 @@ def test_split_cells_must_be_multiple_of_32(bad):
 
 
 def test_auto_split_fills_device():
-    p = K.plan(32, 8, 128, 1, 16384, n_occupied=[8192], n_cu=256)
+    # short f16 contexts at head_dim 128: the one-shot kernel, one split of
+    # at most 448 cells per compute unit, on 32-cell boundaries
+    for occ, cells in ((8192, 256), (13100, 416), (4096, 128), (1000, 64)):
+        info = K.plan(32, 8, 128, 1, 16384, n_occupied=[occ], n_cu=256).info()
+        assert info["kernel"] == K.KERNEL_ONESHOT and info["waves"] == 8 and info["split_cells"] == cells
+        assert info["n_workgroups"] == 8 * -(-occ // cells) <= 256
+    # too long for one split per compute unit: the streamed kernel
+    assert K.plan(32, 8, 128, 1, 16384, n_occupied=[16384], n_cu=256).info()["kernel"] == K.KERNEL_STREAMED
+    p = K.plan(32, 8, 128, 1, 16384, n_occupied=[8192], n_cu=256, kernel=K.KERNEL_STREAMED)
     info = p.info()
-    assert 256 <= info["n_workgroups"] <= 512 and info["waves"] == 4
-    # short f16 context: one eight-wave workgroup per compute unit at most,
-    # each split two of its 256-cell steps
-    p = K.plan(32, 8, 128, 1, 16384, n_occupied=[13100], n_cu=256)
+    assert 256 <= info["n_workgroups"] <= 512 and info["waves"] == 4 and info["kernel"] == K.KERNEL_STREAMED
+    # short f16 context on the streamed kernel: one eight-wave workgroup per
+    # compute unit at most, each split two of its 256-cell steps
+    p = K.plan(32, 8, 128, 1, 16384, n_occupied=[13100], n_cu=256, kernel=K.KERNEL_STREAMED)
     info = p.info()
     assert info["waves"] == 8 and info["n_workgroups"] == 208 and info["split_cells"] == 512
     # not for quantized caches, explicit split sizes or head_dim 256
@@ -174,8 +182,12 @@ def test_auto_split_fills_device():
                   split_cells=512).info()["waves"] == 4
     assert K.plan(64, 4, 256, 1, 16384, n_occupied=[13100], n_cu=256).info()["waves"] == 4
     assert K.plan(48, 8, 128, 1, 16384, n_occupied=[8192], n_cu=256).info()["n_workgroups"] == 512
-    # five f16 rows: matrix-core kernel for short contexts, vector-ALU for long ones
-    short = K.plan(40, 8, 128, 1, 16384, n_occupied=[13100], n_cu=256).info()
+    # five f16 rows: the one-shot kernel, else the matrix-core kernel for
+    # short contexts, vector-ALU for long ones
+    assert K.plan(40, 8, 128, 1, 16384, n_occupied=[13100], n_cu=256).info()["kernel"] == K.KERNEL_ONESHOT
+    assert K.plan(40, 8, 128, 1, 16384, n_occupied=[13100], n_cu=256,
+                  kernel=K.KERNEL_STREAMED).info()["matrix_cores"] == 0
+    short = K.plan(40, 8, 128, 1, 16384, n_occupied=[16384], n_cu=256).info()
     assert short["matrix_cores"] == 1 and short["tiles_per_split"] == 4
     long_ = K.plan(40, 8, 128, 1, 524288, n_occupied=[524288], n_cu=256).info()
     assert long_["matrix_cores"] == 0 and long_["n_workgroups"] == 256
