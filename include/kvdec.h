@@ -336,14 +336,18 @@ typedef struct kvdec_plan_info {
     int32_t split_unit;       /* split boundaries fall on multiples of this many positions */
     int32_t waves;            /* waves per workgroup of the resident launch (4 or 8) */
     int32_t kernel;           /* KVDEC_KERNEL_STREAMED or _ONESHOT for the vector-ALU kernels, 0 on matrix cores */
-    int32_t pad0;
+    int32_t split_interleave; /* U > 0: split s of a (slot, KV head) holds the U-cell units s, s + n_splits,
+                                 s + 2 n_splits, ... of its positions; 0: each split is a contiguous run */
 } kvdec_plan_info;
 
 int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info);
 
 /* Split table: for each workgroup of the resident launch, in launch order, 4 int64 values
  * (slot, kv head, first position, position count), positions clipped to the
- * slot's cells (contiguous) or plan entries (indirect).  With splits_out ==
+ * slot's cells (contiguous) or plan entries (indirect).  For an interleaved
+ * plan (kvdec_plan_info.split_interleave = U) the positions of a split are
+ * its U-cell units first, first + U * n_splits, ... (n_splits = the slot's
+ * splits per KV head) and the count is their total.  With splits_out ==
  * NULL only *n_splits is written. */
 int kvdec_plan_splits(const kvdec_plan_t* plan, int64_t* splits_out, int64_t* n_splits);
 

@@ -44,6 +44,7 @@ void common_args(const kvdec_plan_t& p, const kvdec_io& io, kvdec::SplitArgs& a)
     a.split_unit = p.split_unit;
     a.waves = p.waves;
     a.oneshot = p.oneshot;
+    a.interleave = p.interleave ? 1 : 0;
     // positions are used with several query rows per slot only
     a.q_pos = p.n_q > 1 ? io.q_pos : nullptr;
     a.cell_pos = p.n_q > 1 ? io.cell_pos : nullptr;
@@ -133,7 +134,7 @@ int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info) {
     info->split_unit = plan->split_unit;
     info->waves = plan->waves;
     info->kernel = plan->mfma ? 0 : (plan->oneshot > 0 ? KVDEC_KERNEL_ONESHOT : KVDEC_KERNEL_STREAMED);
-    info->pad0 = 0;
+    info->split_interleave = plan->interleave ? plan->split_unit : 0;
     return KVDEC_OK;
 }
 
@@ -146,14 +147,23 @@ int kvdec_plan_splits(const kvdec_plan_t* plan, int64_t* splits_out, int64_t* n_
         const kvdec::SlotArg& sa = plan->slots[s];
         for (int sp = 0; sp < sa.n_splits; ++sp)  // workgroup order: split-major
             for (int g = 0; g < plan->n_kv_heads; ++g) {
-                const int64_t u0 = (int64_t)sp * sa.n_units / sa.n_splits;
-                const int64_t u1 = (int64_t)(sp + 1) * sa.n_units / sa.n_splits;
-                const int64_t p0 = std::min<int64_t>(u0 * plan->split_unit, sa.n);
-                const int64_t p1 = std::min<int64_t>(u1 * plan->split_unit, sa.n);
+                int64_t p0, count;
+                if (plan->interleave) {
+                    // units sp, sp + n_splits, ...: first position and cell count
+                    const int64_t nu = sp < sa.n_units ? (sa.n_units - sp + sa.n_splits - 1) / sa.n_splits : 0;
+                    p0 = std::min<int64_t>((int64_t)sp * plan->split_unit, sa.n);
+                    const int64_t last = nu > 0 ? ((int64_t)sp + (nu - 1) * sa.n_splits) * plan->split_unit : 0;
+                    count = nu > 0 ? (nu - 1) * plan->split_unit + std::min<int64_t>(plan->split_unit, sa.n - last) : 0;
+                } else {
+                    const int64_t u0 = (int64_t)sp * sa.n_units / sa.n_splits;
+                    const int64_t u1 = (int64_t)(sp + 1) * sa.n_units / sa.n_splits;
+                    p0 = std::min<int64_t>(u0 * plan->split_unit, sa.n);
+                    count = std::min<int64_t>(u1 * plan->split_unit, sa.n) - p0;
+                }
                 splits_out[4 * i + 0] = s;
                 splits_out[4 * i + 1] = g;
                 splits_out[4 * i + 2] = p0;
-                splits_out[4 * i + 3] = p1 - p0;
+                splits_out[4 * i + 3] = count;
                 ++i;
             }
     }
@@ -383,6 +393,7 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
             t.split_unit = kvdec::kTile;
             t.waves = 4;
             t.oneshot = 0;
+            t.interleave = 0;
             t.slot[0].n_splits = splits;
             t.slot[0].wg_begin = 0;
             t.slot[0].part_begin = 0;

@@ -121,6 +121,7 @@ struct SplitArgs {
     float* acc_out;          // running partial written for slots with to_acc
     int32_t acc_rows;        // rows of a running partial: m2 [rows], l [rows], o [rows][D] at acc_o_offset(rows)
     int32_t oneshot;         // > 0: the one-shot kernel with this many 8-cell loads per lane (planner's choice)
+    int32_t interleave;      // one-shot kernel: split s holds split units s, s + n_splits, ... (else a contiguous run)
     int32_t n_q;             // query rows per slot (q, out, lse rows: [slot][n_q][Hq])
     const int32_t* q_pos;    // [slots][n_q] positions of the query rows (n_q > 1)
     const int32_t* cell_pos; // [capacity] positions of device cells, or null: cell index + pos_offset
@@ -205,6 +206,7 @@ struct kvdec_plan {
     int32_t max_split_cells = 0;   // largest split, in positions
     int32_t waves = 4;             // waves per split workgroup (4 or 8)
     int32_t oneshot = 0;           // resident launch on the one-shot kernel: 8-cell loads per lane (2, 4 or 7)
+    bool interleave = false;       // one-shot splits hold every n_splits-th unit of 32 cells
     bool mfma = false;             // served by the matrix-core kernel
     int64_t n_tiles = 0;
     std::vector<int32_t> cells;      // indirect entries (host-built plans)

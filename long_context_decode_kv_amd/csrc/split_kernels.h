@@ -1064,10 +1064,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int local = wg - sa.wg_begin;
     const int split = local / a.n_kv_heads;
     const int g = local - split * a.n_kv_heads;
-    const int64_t pos_begin = (((int64_t)split * sa.n_units) / sa.n_splits) * a.split_unit;
-    const int64_t span_end = (((int64_t)(split + 1) * sa.n_units) / sa.n_splits) * a.split_unit;
-    const int64_t pos_end = span_end < sa.n ? span_end : sa.n;
-    const int n = pos_end > pos_begin ? (int)(pos_end - pos_begin) : 0;
+    // The split's positions: a contiguous run, or (interleaved) the split
+    // units split, split + n_splits, ...; position p of the split is slot
+    // position pos(p).
+    const int U = a.split_unit;
+    int64_t pos_begin = 0;
+    int n = 0;
+    if (a.interleave) {
+        const int nu = split < sa.n_units ? (sa.n_units - split + sa.n_splits - 1) / sa.n_splits : 0;
+        if (nu > 0) {
+            const int64_t last = ((int64_t)split + (int64_t)(nu - 1) * sa.n_splits) * U;
+            n = (nu - 1) * U + (int)((sa.n - last) < U ? (sa.n - last) : U);
+        }
+    } else {
+        pos_begin = (((int64_t)split * sa.n_units) / sa.n_splits) * U;
+        const int64_t span_end = (((int64_t)(split + 1) * sa.n_units) / sa.n_splits) * U;
+        const int64_t pos_end = span_end < sa.n ? span_end : sa.n;
+        n = pos_end > pos_begin ? (int)(pos_end - pos_begin) : 0;
+    }
+    auto pos = [&](int p) -> int64_t {
+        return a.interleave ? ((int64_t)split + (int64_t)(p / U) * sa.n_splits) * U + p % U : pos_begin + p;
+    };
     // wave w: cells w * cw ... of the split, cw even and at most CW (the
     // planner keeps splits within W * CW cells; the clamp only keeps LDS
     // accesses in bounds)
@@ -1088,8 +1105,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     }
 
     if (cnt > 0) {
-        // the wave's first cell; loads past the wave's cells read it instead
-        const int64_t c0 = sa.first + pos_begin + w0;
+        // cell of the wave's row r; rows past the wave's cells read its first cell instead
+        auto cell = [&](int r) -> int64_t { return sa.first + pos(w0 + (r < cnt ? r : 0)); };
         const uint8_t* kbase = a.k + (int64_t)g * a.k_hs;
         const uint8_t* vbase = a.v + (int64_t)g * a.v_hs;
 
@@ -1106,16 +1123,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
         Chunk<16> kc[JM][NC], vc[JM][NC];
 #pragma unroll
         for (int j = 0; j < JM; ++j) {
-            const int r = j * CPL + cl;
-            const uint8_t* kr = kbase + (c0 + (r < cnt ? r : 0)) * a.k_cs;
+            const uint8_t* kr = kbase + cell(j * CPL + cl) * a.k_cs;
 #pragma unroll
             for (int c = 0; c < NC; ++c) kc[j][c] = load_chunk<16>(kr + (c * R + sub) * 16);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < JM; ++j) {
-            const int r = j * CPL + cl;
-            const uint8_t* vr = vbase + (c0 + (r < cnt ? r : 0)) * a.v_cs;
+            const uint8_t* vr = vbase + cell(j * CPL + cl) * a.v_cs;
 #pragma unroll
             for (int c = 0; c < NC; ++c) vc[j][c] = load_chunk<16>(vr + (c * R + sub) * 16);
         }

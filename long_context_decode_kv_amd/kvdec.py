@@ -68,7 +68,7 @@ class PlanInfo(ctypes.Structure):
         ("n_slots", _i32), ("group", _i32), ("n_workgroups", _i32), ("tiles_per_split", _i32),
         ("n_tiles", _i64), ("n_entries", _i64), ("n_tail_chunks", _i64), ("workspace_bytes", _i64),
         ("n_queries", _i32), ("matrix_cores", _i32), ("split_cells", _i32), ("split_unit", _i32),
-        ("waves", _i32), ("kernel", _i32), ("pad0", _i32),
+        ("waves", _i32), ("kernel", _i32), ("split_interleave", _i32),
     ]
 
 

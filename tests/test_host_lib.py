@@ -93,13 +93,29 @@ def test_compact_plan_gqa6_workload_shape():
     assert list(np.diff(off) // 128) == [1024, 512, 157, 7]
 
 
+def _split_positions(p, sp):
+    """Positions of each row of the split table: a contiguous run, or for an
+    interleaved plan the units first, first + U * n_splits, ... of U cells."""
+    u = p.info()["split_interleave"]
+    if not u:
+        return [range(int(p0), int(p0 + n)) for _, _, p0, n in sp]
+    per = {}
+    for s, g, _, _ in sp:
+        per[(int(s), int(g))] = per.get((int(s), int(g)), 0) + 1
+    out = []
+    for s, g, p0, n in sp:
+        stride = u * per[(int(s), int(g))]
+        out.append([int(p0) + (i // u) * stride + i % u for i in range(int(n))])
+    return out
+
+
 def _coverage(p, n_per_slot, n_kv):
     """The split table covers every position [0, n) of every (slot, KV head)
-    exactly once, in contiguous ascending pieces."""
+    exactly once (contiguous runs, or interleaved units)."""
     sp = p.splits()
     seen = {}
-    for s, g, p0, n in sp:
-        for t in range(p0, p0 + n):
+    for (s, g, _, _), ts in zip(sp, _split_positions(p, sp)):
+        for t in ts:
             key = (int(s), int(g), int(t))
             assert key not in seen
             seen[key] = 1
@@ -158,6 +174,13 @@ def test_auto_split_fills_device():
         assert info["n_workgroups"] == 8 * -(-occ // cells) <= 256
     # too long for one split per compute unit: the streamed kernel
     assert K.plan(32, 8, 128, 1, 16384, n_occupied=[16384], n_cu=256).info()["kernel"] == K.KERNEL_STREAMED
+    # one-shot splits take every n_splits-th 32-cell unit, covering every position once
+    for occ in ([13100], [4096], [1000], [900, 5000, 1, 0, 129]):
+        p = K.plan(32, 8, 128, len(occ), 16384 * len(occ), n_occupied=occ, n_cu=256,
+                   cell_begin=[16384 * i for i in range(len(occ))])
+        assert p.info()["kernel"] == K.KERNEL_ONESHOT and p.info()["split_interleave"] == 32
+        sp = _coverage(p, occ, 8)
+        assert max(len(ts) for ts in _split_positions(p, sp)) <= p.info()["split_cells"]
     p = K.plan(32, 8, 128, 1, 16384, n_occupied=[8192], n_cu=256, kernel=K.KERNEL_STREAMED)
     info = p.info()
     assert 256 <= info["n_workgroups"] <= 512 and info["waves"] == 4 and info["kernel"] == K.KERNEL_STREAMED
