@@ -9,6 +9,8 @@ in HBM before the timed region.  Prints one JSON line on stdout; progress
 goes to stderr.
 
 Workloads (synthetic N(0, 1) data of the named model's attention shape):
+  single-4096       one layer (32 q heads, 8 KV heads, head_dim 128, 4096
+                    f16 cells) per step, rotated over 32 cache copies
   qwen3-8b-ctx16k   36 layers x (32 q heads, 8 KV heads, head_dim 128),
                     13100 occupied cells of a 16384-cell f16 cache (default)
   qwen2.5-14b-1m    48 layers x (40 q / 8 KV heads, head_dim 128), 524288
@@ -188,31 +190,41 @@ class ContiguousModel(Workload):
         K.attend(self.plan, self.q[layer], self.k[layer], self.v[layer], self.ws, out=self.out[layer],
                  lse=self.lse[layer], q_pos=self.q_pos)
 
+    def stored_layer(self, layer):
+        """The stored tensors of one layer: (q, K, V) device views of the
+        attended cells."""
+        return self.q[layer], self.k[layer][:self.occupied], self.v[layer][:self.occupied]
+
     def oracle_sample(self, budget_s, max_layers=None):
-        """Time the float64 oracle on host copies of the workload's shape:
-        whole layers until the budget is spent (at least one)."""
-        max_layers = max_layers or self.layers
+        """Time the float64 oracle on host copies of the exact stored tensors
+        (device-to-host copies timed apart): whole layers, in order, until
+        the budget is spent (at least one).  Returns (layers, oracle seconds,
+        description, copy seconds)."""
         import numpy as np
+        import torch
         import oracle as O
-        from long_context_decode_kv_amd import synth
-        r = synth.rng(99)
-        q = synth.gen_q(r, self.n_q, self.hq, self.d)
-        kc = synth.gen_f16_cache(r, self.occupied, self.hkv, self.d)
-        vc = synth.gen_f16_cache(r, self.occupied, self.hkv, self.d)
-        cells = [np.arange(self.occupied)]
-        regions = [((O.F16, kc, None), (O.F16, vc, None), cells)]
-        done, t0 = 0, time.perf_counter()
+        max_layers = max_layers or self.layers
+        done, el, d2h = 0, 0.0, 0.0
         while True:
+            t0 = time.perf_counter()
+            qd, kd, vd = self.stored_layer(done % self.layers)
+            q = qd.cpu().numpy()
+            kc = kd.cpu().numpy().view(np.uint16)
+            vc = vd.cpu().numpy().view(np.uint16)
+            torch.cuda.synchronize()
+            d2h += time.perf_counter() - t0
+            regions = [((O.F16, kc, None), (O.F16, vc, None), [np.arange(kc.shape[0])])]
+            t0 = time.perf_counter()
             if self.n_q > 1:
                 qp = np.arange(self.occupied - self.n_q, self.occupied)[None]
                 O.decode_attention_multi(q[None], regions, self.hkv, 1 / math.sqrt(self.d), qp)
             else:
                 O.decode_attention(q, regions, self.hkv, 1 / math.sqrt(self.d))
+            el += time.perf_counter() - t0
             done += 1
-            el = time.perf_counter() - t0
             if el >= budget_s or done >= max_layers:
-                return done, el, f"{done} of {max_layers} layers (full layer each: {self.occupied} cells x " \
-                                 f"{self.hkv} KV heads x {self.hq} q heads)"
+                return done, el, f"{done} of {max_layers} layers, host copies of the stored tensors (full layer " \
+                                 f"each: {self.occupied} cells x {self.hkv} KV heads x {self.hq} q heads)", d2h
 
 
 class Gqa6Quant(Workload):
@@ -289,14 +301,24 @@ class Gqa6Quant(Workload):
                  k_scales=self.k[i][1], v_scales=self.v[i][1], plan_cells=self.plan_cells)
 
     def oracle_sample(self, budget_s):
+        """The oracle on host copies of the stored cache rows of the
+        20000-cell slot (gathered on the device through the plan's entries,
+        copy timed apart), scaled by cell count to all four slots."""
         import numpy as np
+        import torch
         import oracle as O
-        from long_context_decode_kv_amd import synth
-        r = synth.rng(98)
-        n = self.lengths[2]  # the 20000-cell slot, all four KV heads
-        q = synth.gen_q(r, 1, 24, 256)
-        kc, ks = synth.gen_quant_cache(r, self.kind, n, 4, 256)
-        vc, vs = synth.gen_quant_cache(r, self.v_kind, n, 4, 256)
+        entries, offs = self.plan.cells()
+        cells = entries[offs[2]:offs[3]]
+        cells = cells[cells >= 0]
+        n = len(cells)
+        t0 = time.perf_counter()
+        idx = torch.from_numpy(cells.astype(np.int64)).cuda()
+        q = self.q[0][2:3].cpu().numpy()
+        kc, ks = (t.index_select(0, idx).cpu().numpy() for t in self.k[0])
+        vc, vs = (t.index_select(0, idx).cpu().numpy() for t in self.v[0])
+        torch.cuda.synchronize()
+        d2h = time.perf_counter() - t0
+        ks, vs = ks.view(np.uint16), vs.view(np.uint16)
         t0 = time.perf_counter()
         done = 0
         while True:
@@ -305,10 +327,9 @@ class Gqa6Quant(Workload):
             el = time.perf_counter() - t0
             if el >= budget_s or done >= 4:
                 break
-        per_cell = el / (done * n)
-        total = per_cell * sum(self.lengths)
-        return 1, total, f"slot of {n} cells x 4 KV heads x 24 q heads timed {done}x ({el:.1f} s), scaled by " \
-                         f"cell count to all {sum(self.lengths)} attended cells"
+        total = el / (done * n) * sum(self.lengths)
+        return 1, total, f"the {n}-cell slot x 4 KV heads x 24 q heads, host copies of its stored rows, timed " \
+                         f"{done}x ({el:.1f} s), scaled by cell count to all {sum(self.lengths)} attended cells", d2h
 
 
 class RollingWindow(ContiguousModel):
@@ -432,12 +453,37 @@ class ContiguousModelOneLaunch(ContiguousModel):
         self.ws = K.workspace(self.plan)
         self.q_pos = None
 
+    def stored_layer(self, layer):
+        cap = self.capacity
+        return self.q[0][layer:layer + 1], self.k[0][layer * cap:layer * cap + self.occupied], \
+            self.v[0][layer * cap:layer * cap + self.occupied]
+
     def oracle_sample(self, budget_s):
-        done, el, sample = super().oracle_sample(budget_s, self.model_layers)
-        return done / self.model_layers, el, sample
+        saved, self.layers = self.layers, self.model_layers
+        try:
+            done, el, sample, d2h = super().oracle_sample(budget_s, self.model_layers)
+        finally:
+            self.layers = saved
+        return done / self.model_layers, el, sample, d2h
+
+
+class RotatedLayer(ContiguousModel):
+    """One layer per step, rotated over ``copies`` independent caches (over
+    the 256 MB MALL in total) so that repeated steps read HBM."""
+
+    def __init__(self, name, copies, hq, hkv, d, occupied):
+        super().__init__(name, copies, hq, hkv, d, occupied, occupied)
+        self.cycle = copies
+
+    def config(self):
+        c = super().config()
+        c.update({"layers": 1, "rotated_cache_copies": self.layers,
+                  "rotated_bytes": self.layers * self.occupied * self.hkv * self.d * 4})
+        return c
 
 
 WORKLOADS = {
+    "single-4096": lambda: RotatedLayer("single-4096", 32, 32, 8, 128, 4096),
     "qwen3-8b-ctx16k": lambda: ContiguousModel("qwen3-8b-ctx16k", 36, 32, 8, 128, 16384, 13100),
     "qwen2.5-14b-1m": lambda: ContiguousModel("qwen2.5-14b-1m", 48, 40, 8, 128, 524288, 524288),
     "gqa6-q8": lambda: Gqa6Quant("gqa6-q8", 1),
@@ -656,7 +702,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_info
-        layers_done, el, sample = wl.oracle_sample(args.cpu_budget)
+        layers_done, el, sample, d2h = wl.oracle_sample(args.cpu_budget)
         pools = threadpool_info()
         threads = max([p.get("num_threads", 1) for p in pools] + [1])
         blas = ", ".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in pools
@@ -664,12 +710,14 @@ def main():
         cpu = {"value": round(bytes_launch * layers_done / el / 1e9, 4), "unit": "GB/s", "cores": threads,
                "kind": "oracle", "sample": sample + f"; {el:.1f} s float64 numpy on the host",
                "blas": blas or None, "host_cpus": os.cpu_count(),
-               "us_per_step_extrapolated": round(el / layers_done * wl.layers * 1e6, 1)}
+               "us_per_step_extrapolated": round(el / layers_done * launches_per_step * 1e6, 1),
+               "d2h_copy_s": round(d2h, 4),
+               "d2h_note": "device-to-host copies of the stored tensors, timed apart from the oracle"}
         # the same oracle on one thread, where one unit of the sample stays short
         if el / layers_done * threads < 20.0:
             from threadpoolctl import threadpool_limits
             with threadpool_limits(limits=1):
-                d1, e1, s1 = wl.oracle_sample(min(4.0, args.cpu_budget / 3))
+                d1, e1, s1, _ = wl.oracle_sample(min(4.0, args.cpu_budget / 3))
             cpu["value_1thread"] = round(bytes_launch * d1 / e1 / 1e9, 4)
             cpu["sample_1thread"] = s1 + f"; {e1:.1f} s on 1 thread"
 
@@ -702,6 +750,7 @@ def main():
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall_s, 4),
         "kernel_source_sha256_16": kernel_source_hash(),
+        "library_source_hash": K.LIB_SOURCE_HASH,
     }
     if hasattr(wl, "extra"):
         res.update(wl.extra())

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_VERSION 10400 /* 1.4.0: 32-cell split boundaries */
+#define KVDEC_VERSION 10500 /* 1.5.0: one-shot split kernel, kernel choice, split interleave */
 
 /* Status codes. */
 #define KVDEC_OK 0
@@ -390,6 +390,12 @@ const char* kvdec_last_error(void);
 
 /* KVDEC_VERSION of the built library. */
 int kvdec_version(void);
+
+/* Hash (16 hex digits) of the source files and compiler flags the library
+ * was built from, fixed at build time; the build script writes the same
+ * value of the current sources, so a caller can detect a stale binary.
+ * Static storage, never NULL. */
+const char* kvdec_source_hash(void);
 
 #ifdef __cplusplus
 }

@@ -43,6 +43,24 @@ FLAGS = [
 ]
 
 
+def source_hash():
+    """16 hex digits of sha256 over every source the libraries are built
+    from (csrc/, include/) and the compiler flags: the value the library
+    embeds and the binding checks at import."""
+    import hashlib
+    h = hashlib.sha256()
+    files = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC))]
+    inc = os.path.join(ROOT, "include")
+    files += [os.path.join(inc, f) for f in sorted(os.listdir(inc))]
+    for f in files:
+        if os.path.isfile(f) and f.endswith((".h", ".hip", ".cpp")):
+            h.update(os.path.basename(f).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    h.update(" ".join(FLAGS[:-4]).encode())  # the flags without the two -I paths
+    return h.hexdigest()[:16]
+
+
 def hipcc():
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -81,11 +99,16 @@ def _compile(src, extra):
     return obj, log
 
 
+HASH_FILE = LIB + ".srchash"
+
+
 def build(verbose=False, extra=()):
     os.makedirs(BUILD, exist_ok=True)
     srcs = SOURCES + PROBE_SOURCES
+    digest = source_hash()
+    hash_def = ['-DKVDEC_SOURCE_HASH="%s"' % digest]
     with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
-        results = dict(zip(srcs, ex.map(lambda s: _compile(s, list(extra)), srcs)))
+        results = dict(zip(srcs, ex.map(lambda s: _compile(s, list(extra) + hash_def), srcs)))
     if verbose:
         for _, log in results.values():
             if log.strip():
@@ -97,13 +120,24 @@ def build(verbose=False, extra=()):
         if r.returncode != 0:
             raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
         os.replace(tmp, lib)
+    with open(HASH_FILE, "w") as fh:
+        fh.write(digest + "\n")
     return LIB
 
 
+def built_hash():
+    """The source hash recorded beside the built library, or None."""
+    try:
+        with open(HASH_FILE) as fh:
+            return fh.read().strip()
+    except OSError:
+        return None
+
+
 def ensure_built():
-    """Build once if the libraries are missing (a fresh checkout); a built
-    tree is used as it is -- rebuild after changing a source."""
-    if not (os.path.exists(LIB) and os.path.exists(PROBE_LIB)):
+    """Build when the libraries are missing or were built from other
+    sources than the current ones (the recorded source hash differs)."""
+    if not (os.path.exists(LIB) and os.path.exists(PROBE_LIB)) or built_hash() != source_hash():
         build()
 
 

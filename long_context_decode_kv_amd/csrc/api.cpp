@@ -57,6 +57,11 @@ extern "C" {
 
 int kvdec_version(void) { return KVDEC_VERSION; }
 
+#ifndef KVDEC_SOURCE_HASH
+#error "KVDEC_SOURCE_HASH is set by the build script"
+#endif
+const char* kvdec_source_hash(void) { return KVDEC_SOURCE_HASH; }
+
 const char* kvdec_strerror(int status) {
     switch (status) {
         case KVDEC_OK: return "ok";

@@ -18,11 +18,20 @@ import numpy as np
 # same runtime instance the kernels are launched through.
 import torch  # noqa: F401
 
+from long_context_decode_kv_amd.build import source_hash as _source_hash
+
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvdec.so")
 if not os.path.exists(_LIB_PATH):
     raise ImportError(f"{_LIB_PATH} is not built; run: python -m long_context_decode_kv_amd.build")
 lib = ctypes.CDLL(_LIB_PATH)
 LIB_PATH = _LIB_PATH
+lib.kvdec_source_hash.argtypes = []
+lib.kvdec_source_hash.restype = ctypes.c_char_p
+LIB_SOURCE_HASH = lib.kvdec_source_hash().decode()
+# a library built from other sources than the ones beside it is never used
+if LIB_SOURCE_HASH != _source_hash():
+    raise ImportError(f"{_LIB_PATH} was built from other sources (library {LIB_SOURCE_HASH}, sources "
+                      f"{_source_hash()}); rebuild: python -m long_context_decode_kv_amd.build")
 
 F16, Q8_B32, Q4_B32 = 0, 1, 2
 OK, E_INVALID, E_RANGE, E_UNSUPPORTED, E_WORKSPACE, E_NOMEM, E_DEVICE = 0, -1, -2, -3, -4, -5, -6
@@ -98,6 +107,7 @@ lib.kvdec_version.restype = ctypes.c_int
 EXPORTED = [
     "kvdec_plan", "kvdec_plan_cells", "kvdec_plan_get_info", "kvdec_plan_splits", "kvdec_plan_free",
     "kvdec_attend", "kvdec_merge", "kvdec_build_cells", "kvdec_strerror", "kvdec_last_error", "kvdec_version",
+    "kvdec_source_hash",
 ]
 
 

@@ -52,3 +52,20 @@ def test_kernel_hash_ignores_comments_only():
     assert bench.strip_c_comments(src) == bench.strip_c_comments(same)
     assert bench.strip_c_comments(src) != bench.strip_c_comments(other)
     assert '"a // b"' in bench.strip_c_comments(src)
+
+
+def test_bytes_single_layer_4096_and_rotation():
+    # 4096 cells x 8 KV heads x 512 B + q and out; one launch per step over
+    # 32 rotated copies (more than the 256 MB memory-side cache holds)
+    wl = bench.WORKLOADS["single-4096"]()
+    assert wl.algorithmic_bytes_per_launch() == 4096 * 8 * 512 + 2 * 4 * 32 * 128 == 16809984
+    assert wl.layers // wl.cycle == 1
+    assert wl.config()["rotated_bytes"] == 32 * 4096 * 8 * 128 * 4 > 256 * 2 ** 20
+
+
+def test_library_hash_matches_sources():
+    """The built library carries the hash of the sources beside it (a stale
+    library is refused at import)."""
+    from long_context_decode_kv_amd import build, kvdec
+    assert kvdec.LIB_SOURCE_HASH == build.source_hash() == build.built_hash()
+    assert len(kvdec.LIB_SOURCE_HASH) == 16

@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
     for name in names:
         assert hasattr(K.lib, name), name
     assert set(names) == set(K.EXPORTED)
-    assert K.version() == 10400
+    assert K.version() == 10500
 
 
 def test_probe_library_exports_and_rejects_bad_arguments():
