@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_VERSION 10500 /* 1.5.0: one-shot split kernel, kernel choice, split interleave */
+#define KVDEC_VERSION 10600 /* 1.6.0: kvdec_attend_static */
 
 /* Status codes. */
 #define KVDEC_OK 0
@@ -81,6 +81,13 @@ extern "C" {
 #define KVDEC_KERNEL_AUTO 0
 #define KVDEC_KERNEL_STREAMED 1
 #define KVDEC_KERNEL_ONESHOT 2
+
+/* kvdec_attend_static: the library's own per-device scratch array holds a
+ * merge-ticket area of KVDEC_STATIC_TICKET_BYTES followed by a workspace of
+ * KVDEC_STATIC_WORKSPACE_BYTES (16 MiB + 64 KiB of device memory per GPU the
+ * library runs on, held until the process ends). */
+#define KVDEC_STATIC_TICKET_BYTES (64 * 1024)
+#define KVDEC_STATIC_WORKSPACE_BYTES (16 * 1024 * 1024)
 
 /*
  * Problem description, read by kvdec_plan (host memory only; nothing is
@@ -365,6 +372,31 @@ void kvdec_plan_free(kvdec_plan_t* plan);
  */
 int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, size_t workspace_bytes,
                  void* stream, void* copy_stream);
+
+/*
+ * kvdec_attend without a caller workspace, for callers that cannot allocate
+ * device memory: code recorded under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It enqueues exactly what kvdec_attend
+ * enqueues for the same plan and io, with the workspace taken from a
+ * file-scope device array of the library (KVDEC_STATIC_TICKET_BYTES of merge
+ * tickets, then KVDEC_STATIC_WORKSPACE_BYTES of workspace, one copy per GPU);
+ * it calls no allocating routine.  The first call on a device looks up that
+ * device's copy and enqueues a clear of its ticket area on `stream` (a call
+ * made under stream capture records the clear into the graph, and the next
+ * call outside capture clears again); every completed call leaves the
+ * tickets at zero.  All calls on one GPU share its array, so calls that may
+ * overlap on one GPU (different streams, or a graph replay beside an eager
+ * call) race and must be ordered by the caller.  The outputs never alias the
+ * array; partial records from the previous call stay in it and are
+ * overwritten before they are read.
+ * Errors: as kvdec_attend, and KVDEC_E_WORKSPACE when the plan's
+ * workspace_bytes exceed KVDEC_STATIC_WORKSPACE_BYTES or its merge tickets
+ * (n_slots * n_kv_heads plus its cluster tickets) exceed the ticket area,
+ * KVDEC_E_UNSUPPORTED for a plan with a copied host tail (its ring ordering
+ * needs per-call events; a tail_zero_copy plan is accepted), KVDEC_E_DEVICE
+ * when the device's array cannot be looked up.
+ */
+int kvdec_attend_static(const kvdec_plan_t* plan, const kvdec_io* io, void* stream);
 
 /*
  * Log-sum-exp merge of n_parts partial sets over the same n_rows rows

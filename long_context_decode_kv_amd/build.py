@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvdec.so")
 
 SOURCES = ["kernels.hip", "split_f16.hip", "split_q8.hip", "split_q4.hip", "split_f16_q8.hip", "split_f16_q4.hip",
-           "split_q8_q4.hip", "plan_device.hip", "api.cpp", "plan.cpp"]
+           "split_q8_q4.hip", "plan_device.hip", "static_scratch.hip", "api.cpp", "plan.cpp"]
 # the streaming-read probe (bandwidth ceiling for the benchmark) is a library of its own
 PROBE_SOURCES = ["probe.hip"]
 PROBE_LIB = os.path.join(PKG, "libkvprobe.so")

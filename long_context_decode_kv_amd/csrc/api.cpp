@@ -53,139 +53,12 @@ void common_args(const kvdec_plan_t& p, const kvdec_io& io, kvdec::SplitArgs& a)
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-int kvdec_version(void) { return KVDEC_VERSION; }
-
-#ifndef KVDEC_SOURCE_HASH
-#error "KVDEC_SOURCE_HASH is set by the build script"
-#endif
-const char* kvdec_source_hash(void) { return KVDEC_SOURCE_HASH; }
-
-const char* kvdec_strerror(int status) {
-    switch (status) {
-        case KVDEC_OK: return "ok";
-        case KVDEC_E_INVALID: return "invalid argument";
-        case KVDEC_E_RANGE: return "cell index out of range";
-        case KVDEC_E_UNSUPPORTED: return "unsupported configuration";
-        case KVDEC_E_WORKSPACE: return "workspace missing or too small";
-        case KVDEC_E_NOMEM: return "host out of memory";
-        case KVDEC_E_DEVICE: return "HIP runtime error";
-        default: return "unknown status";
-    }
-}
-
-const char* kvdec_last_error(void) { return g_last_error.c_str(); }
-
-int kvdec_plan(const kvdec_problem* problem, int32_t n_cu, kvdec_plan_t** out, size_t* workspace_bytes) {
-    g_last_error.clear();
-    if (!problem || !out) return fail(KVDEC_E_INVALID, "problem and out must be non-null");
-    *out = nullptr;
-    if (n_cu < 0) return fail(KVDEC_E_INVALID, "n_cu must be >= 0");
-    if (n_cu == 0) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e != hipSuccess) return device_fail(e, "hipGetDevice");
-        e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return device_fail(e, "hipDeviceGetAttribute");
-    }
-    kvdec_plan_t* plan = nullptr;
-    try {
-        plan = new kvdec_plan_t();
-        std::string err;
-        const int st = kvdec::build_plan(*problem, n_cu, *plan, err);
-        if (st != KVDEC_OK) {
-            delete plan;
-            return fail(st, err);
-        }
-    } catch (const std::bad_alloc&) {
-        delete plan;
-        return fail(KVDEC_E_NOMEM, "host allocation failed while planning");
-    }
-    *out = plan;
-    if (workspace_bytes) *workspace_bytes = plan->workspace_bytes;
-    return KVDEC_OK;
-}
-
-int kvdec_plan_cells(const kvdec_plan_t* plan, int32_t* cells_out, int64_t* offsets_out, int64_t* n_entries) {
-    if (!plan || !n_entries) return fail(KVDEC_E_INVALID, "plan and n_entries must be non-null");
-    if (plan->device_cells) {
-        if (cells_out) return fail(KVDEC_E_INVALID, "a device-built plan's entries come from kvdec_build_cells");
-        *n_entries = plan->n_device_entries;
-    } else {
-        *n_entries = (int64_t)plan->cells.size();
-        if (cells_out && !plan->cells.empty()) std::memcpy(cells_out, plan->cells.data(), plan->cells.size() * 4);
-    }
-    if (offsets_out) {
-        for (int s = 0; s <= plan->n_slots; ++s)
-            offsets_out[s] = plan->indirect ? plan->cells_off[s] : 0;
-    }
-    return KVDEC_OK;
-}
-
-int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info) {
-    if (!plan || !info) return fail(KVDEC_E_INVALID, "plan and info must be non-null");
-    info->n_slots = plan->n_slots;
-    info->group = plan->group;
-    info->n_workgroups = plan->n_workgroups;
-    info->tiles_per_split = plan->max_tiles_per_split;
-    info->n_tiles = plan->n_tiles;
-    info->n_entries = plan->device_cells ? plan->n_device_entries : (int64_t)plan->cells.size();
-    info->n_tail_chunks = plan->n_tail_chunks;
-    info->workspace_bytes = (int64_t)plan->workspace_bytes;
-    info->n_queries = plan->n_q;
-    info->matrix_cores = plan->mfma ? 1 : 0;
-    info->split_cells = plan->max_split_cells;
-    info->split_unit = plan->split_unit;
-    info->waves = plan->waves;
-    info->kernel = plan->mfma ? 0 : (plan->oneshot > 0 ? KVDEC_KERNEL_ONESHOT : KVDEC_KERNEL_STREAMED);
-    info->split_interleave = plan->interleave ? plan->split_unit : 0;
-    return KVDEC_OK;
-}
-
-int kvdec_plan_splits(const kvdec_plan_t* plan, int64_t* splits_out, int64_t* n_splits) {
-    if (!plan || !n_splits) return fail(KVDEC_E_INVALID, "plan and n_splits must be non-null");
-    *n_splits = plan->n_workgroups;
-    if (!splits_out) return KVDEC_OK;
-    int64_t i = 0;
-    for (int s = 0; s < plan->n_slots; ++s) {
-        const kvdec::SlotArg& sa = plan->slots[s];
-        for (int sp = 0; sp < sa.n_splits; ++sp)  // workgroup order: split-major
-            for (int g = 0; g < plan->n_kv_heads; ++g) {
-                int64_t p0, count;
-                if (plan->interleave) {
-                    // units sp, sp + n_splits, ...: first position and cell count
-                    const int64_t nu = sp < sa.n_units ? (sa.n_units - sp + sa.n_splits - 1) / sa.n_splits : 0;
-                    p0 = std::min<int64_t>((int64_t)sp * plan->split_unit, sa.n);
-                    const int64_t last = nu > 0 ? ((int64_t)sp + (nu - 1) * sa.n_splits) * plan->split_unit : 0;
-                    count = nu > 0 ? (nu - 1) * plan->split_unit + std::min<int64_t>(plan->split_unit, sa.n - last) : 0;
-                } else {
-                    const int64_t u0 = (int64_t)sp * sa.n_units / sa.n_splits;
-                    const int64_t u1 = (int64_t)(sp + 1) * sa.n_units / sa.n_splits;
-                    p0 = std::min<int64_t>(u0 * plan->split_unit, sa.n);
-                    count = std::min<int64_t>(u1 * plan->split_unit, sa.n) - p0;
-                }
-                splits_out[4 * i + 0] = s;
-                splits_out[4 * i + 1] = g;
-                splits_out[4 * i + 2] = p0;
-                splits_out[4 * i + 3] = count;
-                ++i;
-            }
-    }
-    return KVDEC_OK;
-}
-
-void kvdec_plan_free(kvdec_plan_t* plan) { delete plan; }
-
-int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, size_t workspace_bytes, void* stream,
-                 void* copy_stream) {
-    g_last_error.clear();
-    if (!plan || !io) return fail(KVDEC_E_INVALID, "plan and io must be non-null");
-    const kvdec_plan_t& p = *plan;
+// The checks of kvdec_io against a plan shared by kvdec_attend and
+// kvdec_attend_static (everything but the workspace); no device calls.
+int check_io(const kvdec_plan_t& p, const kvdec_io* io) {
     const int D = p.head_dim;
-    if (!workspace || workspace_bytes < p.workspace_bytes)
-        return fail(KVDEC_E_WORKSPACE, "workspace needs " + std::to_string(p.workspace_bytes) + " bytes");
-    if (!aligned(workspace, 256)) return fail(KVDEC_E_INVALID, "workspace must be 256-byte aligned");
     if (!io->q || !aligned(io->q, 8)) return fail(KVDEC_E_INVALID, "q must be non-null and 8-byte aligned");
     if (!io->k || !io->v) return fail(KVDEC_E_INVALID, "k and v must be non-null");
     const int64_t krow = kvdec::row_bytes(p.k_type, D), vrow = kvdec::row_bytes(p.v_type, D);
@@ -222,8 +95,22 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
     if (!aligned(io->cell_pos, 4)) return fail(KVDEC_E_INVALID, "cell_pos must be 4-byte aligned");
     if (!kvdec::split_instance_exists(D, p.group, p.n_q, p.k_type, p.v_type, p.mfma))
         return fail(KVDEC_E_UNSUPPORTED, "no kernel for this configuration");
+    return KVDEC_OK;
+}
 
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
+// Enqueue the evaluation on a checked plan and io.  ws: the plan's workspace
+// layout starts here; tickets: the merge ticket words (slot tickets, then
+// cluster tickets), or NULL for the plan's own ticket region inside ws.
+int attend_checked(const kvdec_plan_t& p, const kvdec_io* io, uint8_t* ws, uint32_t* tickets, void* stream,
+                   void* copy_stream) {
+    const int D = p.head_dim;
+    const int64_t krow = kvdec::row_bytes(p.k_type, D), vrow = kvdec::row_bytes(p.v_type, D);
+    const int64_t k_cs = io->k_cell_stride ? io->k_cell_stride : krow * p.n_kv_heads;
+    const int64_t k_hs = io->k_head_stride ? io->k_head_stride : krow;
+    const int64_t v_cs = io->v_cell_stride ? io->v_cell_stride : vrow * p.n_kv_heads;
+    const int64_t v_hs = io->v_head_stride ? io->v_head_stride : vrow;
+    const size_t kal = p.k_type == KVDEC_Q4_B32 ? 8 : 16, val = p.v_type == KVDEC_Q4_B32 ? 8 : 16;
+    const size_t sal = std::min<size_t>(16, (size_t)p.head_dim / 16);
     kvdec::SplitArgs a;
     common_args(p, *io, a);
     a.k = static_cast<const uint8_t*>(io->k);
@@ -240,7 +127,7 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
     a.part_m = reinterpret_cast<float*>(ws + p.off_parts_m);
     a.part_l = reinterpret_cast<float*>(ws + p.off_parts_l);
     a.part_o_bytes = (int64_t)p.parts_o_bytes;
-    a.tickets = reinterpret_cast<uint32_t*>(ws + p.off_tickets);
+    a.tickets = tickets ? tickets : reinterpret_cast<uint32_t*>(ws + p.off_tickets);
     a.ctickets = a.tickets + (size_t)p.n_slots * p.n_kv_heads;
     a.crec_base = p.crec_base;
     a.n_slots = p.n_slots;
@@ -423,6 +310,167 @@ int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, 
     destroy();
     if (e != hipSuccess) return device_fail(e, "tail streaming");
     return KVDEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvdec_version(void) { return KVDEC_VERSION; }
+
+#ifndef KVDEC_SOURCE_HASH
+#error "KVDEC_SOURCE_HASH is set by the build script"
+#endif
+const char* kvdec_source_hash(void) { return KVDEC_SOURCE_HASH; }
+
+const char* kvdec_strerror(int status) {
+    switch (status) {
+        case KVDEC_OK: return "ok";
+        case KVDEC_E_INVALID: return "invalid argument";
+        case KVDEC_E_RANGE: return "cell index out of range";
+        case KVDEC_E_UNSUPPORTED: return "unsupported configuration";
+        case KVDEC_E_WORKSPACE: return "workspace missing or too small";
+        case KVDEC_E_NOMEM: return "host out of memory";
+        case KVDEC_E_DEVICE: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* kvdec_last_error(void) { return g_last_error.c_str(); }
+
+int kvdec_plan(const kvdec_problem* problem, int32_t n_cu, kvdec_plan_t** out, size_t* workspace_bytes) {
+    g_last_error.clear();
+    if (!problem || !out) return fail(KVDEC_E_INVALID, "problem and out must be non-null");
+    *out = nullptr;
+    if (n_cu < 0) return fail(KVDEC_E_INVALID, "n_cu must be >= 0");
+    if (n_cu == 0) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+        e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return device_fail(e, "hipDeviceGetAttribute");
+    }
+    kvdec_plan_t* plan = nullptr;
+    try {
+        plan = new kvdec_plan_t();
+        std::string err;
+        const int st = kvdec::build_plan(*problem, n_cu, *plan, err);
+        if (st != KVDEC_OK) {
+            delete plan;
+            return fail(st, err);
+        }
+    } catch (const std::bad_alloc&) {
+        delete plan;
+        return fail(KVDEC_E_NOMEM, "host allocation failed while planning");
+    }
+    *out = plan;
+    if (workspace_bytes) *workspace_bytes = plan->workspace_bytes;
+    return KVDEC_OK;
+}
+
+int kvdec_plan_cells(const kvdec_plan_t* plan, int32_t* cells_out, int64_t* offsets_out, int64_t* n_entries) {
+    if (!plan || !n_entries) return fail(KVDEC_E_INVALID, "plan and n_entries must be non-null");
+    if (plan->device_cells) {
+        if (cells_out) return fail(KVDEC_E_INVALID, "a device-built plan's entries come from kvdec_build_cells");
+        *n_entries = plan->n_device_entries;
+    } else {
+        *n_entries = (int64_t)plan->cells.size();
+        if (cells_out && !plan->cells.empty()) std::memcpy(cells_out, plan->cells.data(), plan->cells.size() * 4);
+    }
+    if (offsets_out) {
+        for (int s = 0; s <= plan->n_slots; ++s)
+            offsets_out[s] = plan->indirect ? plan->cells_off[s] : 0;
+    }
+    return KVDEC_OK;
+}
+
+int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info) {
+    if (!plan || !info) return fail(KVDEC_E_INVALID, "plan and info must be non-null");
+    info->n_slots = plan->n_slots;
+    info->group = plan->group;
+    info->n_workgroups = plan->n_workgroups;
+    info->tiles_per_split = plan->max_tiles_per_split;
+    info->n_tiles = plan->n_tiles;
+    info->n_entries = plan->device_cells ? plan->n_device_entries : (int64_t)plan->cells.size();
+    info->n_tail_chunks = plan->n_tail_chunks;
+    info->workspace_bytes = (int64_t)plan->workspace_bytes;
+    info->n_queries = plan->n_q;
+    info->matrix_cores = plan->mfma ? 1 : 0;
+    info->split_cells = plan->max_split_cells;
+    info->split_unit = plan->split_unit;
+    info->waves = plan->waves;
+    info->kernel = plan->mfma ? 0 : (plan->oneshot > 0 ? KVDEC_KERNEL_ONESHOT : KVDEC_KERNEL_STREAMED);
+    info->split_interleave = plan->interleave ? plan->split_unit : 0;
+    return KVDEC_OK;
+}
+
+int kvdec_plan_splits(const kvdec_plan_t* plan, int64_t* splits_out, int64_t* n_splits) {
+    if (!plan || !n_splits) return fail(KVDEC_E_INVALID, "plan and n_splits must be non-null");
+    *n_splits = plan->n_workgroups;
+    if (!splits_out) return KVDEC_OK;
+    int64_t i = 0;
+    for (int s = 0; s < plan->n_slots; ++s) {
+        const kvdec::SlotArg& sa = plan->slots[s];
+        for (int sp = 0; sp < sa.n_splits; ++sp)  // workgroup order: split-major
+            for (int g = 0; g < plan->n_kv_heads; ++g) {
+                int64_t p0, count;
+                if (plan->interleave) {
+                    // units sp, sp + n_splits, ...: first position and cell count
+                    const int64_t nu = sp < sa.n_units ? (sa.n_units - sp + sa.n_splits - 1) / sa.n_splits : 0;
+                    p0 = std::min<int64_t>((int64_t)sp * plan->split_unit, sa.n);
+                    const int64_t last = nu > 0 ? ((int64_t)sp + (nu - 1) * sa.n_splits) * plan->split_unit : 0;
+                    count = nu > 0 ? (nu - 1) * plan->split_unit + std::min<int64_t>(plan->split_unit, sa.n - last) : 0;
+                } else {
+                    const int64_t u0 = (int64_t)sp * sa.n_units / sa.n_splits;
+                    const int64_t u1 = (int64_t)(sp + 1) * sa.n_units / sa.n_splits;
+                    p0 = std::min<int64_t>(u0 * plan->split_unit, sa.n);
+                    count = std::min<int64_t>(u1 * plan->split_unit, sa.n) - p0;
+                }
+                splits_out[4 * i + 0] = s;
+                splits_out[4 * i + 1] = g;
+                splits_out[4 * i + 2] = p0;
+                splits_out[4 * i + 3] = count;
+                ++i;
+            }
+    }
+    return KVDEC_OK;
+}
+
+void kvdec_plan_free(kvdec_plan_t* plan) { delete plan; }
+
+int kvdec_attend(const kvdec_plan_t* plan, const kvdec_io* io, void* workspace, size_t workspace_bytes, void* stream,
+                 void* copy_stream) {
+    g_last_error.clear();
+    if (!plan || !io) return fail(KVDEC_E_INVALID, "plan and io must be non-null");
+    const kvdec_plan_t& p = *plan;
+    if (!workspace || workspace_bytes < p.workspace_bytes)
+        return fail(KVDEC_E_WORKSPACE, "workspace needs " + std::to_string(p.workspace_bytes) + " bytes");
+    if (!aligned(workspace, 256)) return fail(KVDEC_E_INVALID, "workspace must be 256-byte aligned");
+    const int rc = check_io(p, io);
+    if (rc != KVDEC_OK) return rc;
+    return attend_checked(p, io, static_cast<uint8_t*>(workspace), nullptr, stream, copy_stream);
+}
+
+int kvdec_attend_static(const kvdec_plan_t* plan, const kvdec_io* io, void* stream) {
+    g_last_error.clear();
+    if (!plan || !io) return fail(KVDEC_E_INVALID, "plan and io must be non-null");
+    const kvdec_plan_t& p = *plan;
+    if (p.workspace_bytes > (size_t)KVDEC_STATIC_WORKSPACE_BYTES)
+        return fail(KVDEC_E_WORKSPACE, "the plan's workspace needs " + std::to_string(p.workspace_bytes) +
+                                           " bytes, the static scratch holds " +
+                                           std::to_string((size_t)KVDEC_STATIC_WORKSPACE_BYTES));
+    const int64_t words = (int64_t)p.n_slots * p.n_kv_heads + p.n_cluster_capacity;
+    if (words * 4 > (int64_t)KVDEC_STATIC_TICKET_BYTES)
+        return fail(KVDEC_E_WORKSPACE, "the plan needs " + std::to_string(words) + " merge tickets, the static scratch holds " +
+                                           std::to_string(KVDEC_STATIC_TICKET_BYTES / 4));
+    if (p.has_tail && !p.tail_zero_copy)
+        return fail(KVDEC_E_UNSUPPORTED, "a copied tail needs per-call events; use tail_zero_copy or kvdec_attend");
+    const int rc = check_io(p, io);
+    if (rc != KVDEC_OK) return rc;
+    uint8_t* base = nullptr;
+    const hipError_t e = (hipError_t)kvdec::static_scratch(stream, reinterpret_cast<void**>(&base));
+    if (e != hipSuccess) return device_fail(e, "static scratch set-up");
+    return attend_checked(p, io, base + KVDEC_STATIC_TICKET_BYTES, reinterpret_cast<uint32_t*>(base), stream, nullptr);
 }
 
 int kvdec_build_cells(const kvdec_plan_t* plan, const int32_t* raw_cells, const int64_t* raw_off, int32_t* plan_cells,

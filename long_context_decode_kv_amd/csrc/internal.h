@@ -184,6 +184,10 @@ SplitLaunchFn pick_split_q8_q4(int head_dim, int group, int n_q, bool mfma);
 int launch_split(int head_dim, int group, int n_q, int k_type, int v_type, bool mfma, const SplitArgs& a,
                  void* stream);
 int launch_merge(const MergeArgs& a, void* stream);
+// The calling thread's current device's copy of the static scratch array of
+// kvdec_attend_static (set up on first use per device; the first use also
+// enqueues a clear of the ticket area on `stream`).
+int static_scratch(void* stream, void** base);  // a hipError_t
 bool split_instance_exists(int head_dim, int group, int n_q, int k_type, int v_type, bool mfma);
 
 }  // namespace kvdec

@@ -93,6 +93,8 @@ lib.kvdec_plan_free.argtypes = [_p]
 lib.kvdec_plan_free.restype = None
 lib.kvdec_attend.argtypes = [_p, ctypes.POINTER(IO), _p, ctypes.c_size_t, _p, _p]
 lib.kvdec_attend.restype = ctypes.c_int
+lib.kvdec_attend_static.argtypes = [_p, ctypes.POINTER(IO), _p]
+lib.kvdec_attend_static.restype = ctypes.c_int
 lib.kvdec_merge.argtypes = [_i32, ctypes.POINTER(PartialC), _i64, _i32, _p, _p, _p, _p, _p, _p]
 lib.kvdec_merge.restype = ctypes.c_int
 lib.kvdec_build_cells.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
@@ -107,8 +109,12 @@ lib.kvdec_version.restype = ctypes.c_int
 EXPORTED = [
     "kvdec_plan", "kvdec_plan_cells", "kvdec_plan_get_info", "kvdec_plan_splits", "kvdec_plan_free",
     "kvdec_attend", "kvdec_merge", "kvdec_build_cells", "kvdec_strerror", "kvdec_last_error", "kvdec_version",
-    "kvdec_source_hash",
+    "kvdec_source_hash", "kvdec_attend_static",
 ]
+
+# capacity of the library's static scratch array (kvdec_attend_static)
+STATIC_TICKET_BYTES = 64 * 1024
+STATIC_WORKSPACE_BYTES = 16 * 1024 * 1024
 
 
 class KvdecError(RuntimeError):
@@ -255,16 +261,8 @@ def workspace(plan_, device="cuda"):
     return torch.zeros(max(plan_.workspace_bytes, 256), dtype=torch.uint8, device=device)
 
 
-def attend(plan_, q, k, v, ws, *, out=None, lse=None, part=None, k_scales=None, v_scales=None, plan_cells=None,
-           k_cell_stride=0, k_head_stride=0, v_cell_stride=0, v_head_stride=0, k_tail=None, v_tail=None,
-           k_tail_scales=None, v_tail_scales=None, q_pos=None, cell_pos=None, stream=None, copy_stream=None,
-           copy_after=None):
-    """Enqueue one evaluation (see kvdec_attend in include/kvdec.h).
-    ``part`` is an optional (m, l, o) tuple of output tensors; ``q_pos``
-    (int32 [slots][n_queries]) and ``cell_pos`` (int32 [capacity]) are the
-    positions of the multi-query mask.  ``copy_after`` (a torch.cuda.Event
-    or raw hipEvent_t) orders the tail copies after that event instead of
-    after all earlier work on the stream."""
+def _io(q, k, v, out, lse, part, k_scales, v_scales, plan_cells, k_cell_stride, k_head_stride, v_cell_stride,
+        v_head_stride, k_tail, v_tail, k_tail_scales, v_tail_scales, q_pos, cell_pos, copy_after):
     io = IO()
     io.q, io.k, io.v = _ptr(q), _ptr(k), _ptr(v)
     io.k_scales, io.v_scales = _ptr(k_scales), _ptr(v_scales)
@@ -279,11 +277,37 @@ def attend(plan_, q, k, v, ws, *, out=None, lse=None, part=None, k_scales=None, 
     io.q_pos, io.cell_pos = _ptr(q_pos), _ptr(cell_pos)
     if copy_after is not None:
         io.copy_after = copy_after.cuda_event if hasattr(copy_after, "cuda_event") else int(copy_after)
+    return io
+
+
+def attend(plan_, q, k, v, ws, *, out=None, lse=None, part=None, k_scales=None, v_scales=None, plan_cells=None,
+           k_cell_stride=0, k_head_stride=0, v_cell_stride=0, v_head_stride=0, k_tail=None, v_tail=None,
+           k_tail_scales=None, v_tail_scales=None, q_pos=None, cell_pos=None, stream=None, copy_stream=None,
+           copy_after=None):
+    """Enqueue one evaluation (see kvdec_attend in include/kvdec.h).
+    ``part`` is an optional (m, l, o) tuple of output tensors; ``q_pos``
+    (int32 [slots][n_queries]) and ``cell_pos`` (int32 [capacity]) are the
+    positions of the multi-query mask.  ``copy_after`` (a torch.cuda.Event
+    or raw hipEvent_t) orders the tail copies after that event instead of
+    after all earlier work on the stream."""
+    io = _io(q, k, v, out, lse, part, k_scales, v_scales, plan_cells, k_cell_stride, k_head_stride, v_cell_stride,
+             v_head_stride, k_tail, v_tail, k_tail_scales, v_tail_scales, q_pos, cell_pos, copy_after)
     nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else int(ws[1])
     wptr = _ptr(ws) if hasattr(ws, "numel") else int(ws[0])
     st = _stream_handle(stream)
     cst = None if copy_stream is None else _stream_handle(copy_stream)
     _check(lib.kvdec_attend(plan_.handle, ctypes.byref(io), wptr, nbytes, st, cst), "kvdec_attend")
+
+
+def attend_static(plan_, q, k, v, *, out=None, lse=None, part=None, k_scales=None, v_scales=None, plan_cells=None,
+                  k_cell_stride=0, k_head_stride=0, v_cell_stride=0, v_head_stride=0, k_tail=None, v_tail=None,
+                  k_tail_scales=None, v_tail_scales=None, q_pos=None, cell_pos=None, stream=None):
+    """attend() with the library's static per-device scratch in place of a
+    workspace (see kvdec_attend_static in include/kvdec.h): allocates
+    nothing; calls that may overlap on one GPU race."""
+    io = _io(q, k, v, out, lse, part, k_scales, v_scales, plan_cells, k_cell_stride, k_head_stride, v_cell_stride,
+             v_head_stride, k_tail, v_tail, k_tail_scales, v_tail_scales, q_pos, cell_pos, None)
+    _check(lib.kvdec_attend_static(plan_.handle, ctypes.byref(io), _stream_handle(stream)), "kvdec_attend_static")
 
 
 def build_cells(plan_, raw_cells, raw_off, plan_cells, ws, *, n_records=None, stream=None):

@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
     for name in names:
         assert hasattr(K.lib, name), name
     assert set(names) == set(K.EXPORTED)
-    assert K.version() == 10500
+    assert K.version() == 10600
 
 
 def test_probe_library_exports_and_rejects_bad_arguments():
@@ -305,6 +305,39 @@ def test_attend_validation_before_device_work():
     pt = K.plan(32, 8, 128, 1, 4096, n_occupied=[10], n_tail=[10], tail_capacity_cells=10, n_cu=256)
     wst = (FAKE, pt.workspace_bytes)
     assert _status(lambda: K.attend(pt, FAKE, FAKE, FAKE, wst, out=FAKE, stream=0)) == K.E_INVALID      # tail arrays missing
+
+
+def test_attend_static_validation_before_device_work():
+    """kvdec_attend_static refuses, before it touches a device, a plan whose
+    workspace or merge tickets do not fit the static scratch, a copied tail,
+    and bad io; the limits are the header's."""
+    hdr = open(os.path.join(ROOT, "include", "kvdec.h")).read()
+    assert "#define KVDEC_STATIC_TICKET_BYTES (64 * 1024)" in hdr and K.STATIC_TICKET_BYTES == 64 * 1024
+    assert "#define KVDEC_STATIC_WORKSPACE_BYTES (16 * 1024 * 1024)" in hdr
+    assert K.STATIC_WORKSPACE_BYTES == 16 * 1024 * 1024
+    args = dict(out=FAKE, stream=0)
+    big = K.plan(32, 8, 128, 1, 262144, n_occupied=[262144], split_cells=64, n_cu=256)
+    assert big.workspace_bytes > K.STATIC_WORKSPACE_BYTES
+    assert _status(lambda: K.attend_static(big, FAKE, FAKE, FAKE, **args)) == K.E_WORKSPACE
+    assert "static scratch" in K.lib.kvdec_last_error().decode()
+    # 16 slots x 2048 KV heads: 32768 slot tickets, a workspace that fits
+    many = K.plan(2048, 2048, 64, 16, 64, n_occupied=[1] * 16, cell_begin=list(range(16)), n_cu=256)
+    assert many.workspace_bytes <= K.STATIC_WORKSPACE_BYTES
+    assert _status(lambda: K.attend_static(many, FAKE, FAKE, FAKE, **args)) == K.E_WORKSPACE
+    assert "tickets" in K.lib.kvdec_last_error().decode()
+    copied = K.plan(32, 8, 128, 1, 4096, n_occupied=[10], n_tail=[10], tail_capacity_cells=10, n_cu=256,
+                    tail_chunk_cells=128)
+    assert copied.workspace_bytes <= K.STATIC_WORKSPACE_BYTES
+    assert _status(lambda: K.attend_static(copied, FAKE, FAKE, FAKE, k_tail=FAKE, v_tail=FAKE, **args)) \
+        == K.E_UNSUPPORTED
+    ok = K.plan(32, 8, 128, 1, 4096, n_occupied=[4096], n_cu=256)
+    assert _status(lambda: K.attend_static(ok, 0, FAKE, FAKE, **args)) == K.E_INVALID          # no q
+    assert _status(lambda: K.attend_static(ok, FAKE, FAKE + 8, FAKE, **args)) == K.E_INVALID   # misaligned k
+    assert _status(lambda: K.attend_static(ok, FAKE, FAKE, FAKE, stream=0)) == K.E_INVALID     # no output
+    zc = K.plan(32, 8, 128, 1, 4096, n_occupied=[10], n_tail=[10], tail_capacity_cells=10, n_cu=256,
+                tail_zero_copy=True)
+    assert _status(lambda: K.attend_static(zc, FAKE, FAKE, FAKE, **args)) == K.E_INVALID       # tail arrays missing
+    assert K.lib.kvdec_attend_static(None, None, None) == K.E_INVALID
 
 
 def test_merge_validation():
