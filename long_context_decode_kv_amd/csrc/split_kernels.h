@@ -1647,16 +1647,26 @@ __global__ __launch_bounds__(64 * W) void split_mfma_kernel(const SplitArgs a) {
         const float alpha = bump ? exp2_fast(m_h - mn) : 1.f;
         const bool rescale = bump && m_h != kNegInf;
         m_h = mn;
-        h8 pa;
+        // Each weight as an f16 pair hi + lo: hi is p rounded toward zero,
+        // lo the residual p - hi (exact in f32) rounded again, so hi + lo
+        // carries p to about 2^-21 of itself.  A single f16 weight would
+        // re-weight the cells by up to 2^-10 of their weights -- on two cells
+        // of near-equal score and values v1, v2 an error of up to
+        // 2^-12 |v1 - v2| in the output.
+        h8 pa, pl;
         float lsum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
             const float p0 = (sc[e] == kNegInf) ? 0.f : exp2_fast(sc[e] - mn + kMPOff);
             const float p1 = (sc[e + 1] == kNegInf) ? 0.f : exp2_fast(sc[e + 1] - mn + kMPOff);
             const h2 pp = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+            const h2 pr = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p0 - (float)pp.x, p1 - (float)pp.y));
             pa[e] = pp.x;
             pa[e + 1] = pp.y;
+            pl[e] = pr.x;
+            pl[e + 1] = pr.y;
             lsum = __builtin_amdgcn_fdot2(pp, ones, lsum, false);
+            lsum = __builtin_amdgcn_fdot2(pr, ones, lsum, false);
         }
         lsum = pair_sum<32>(pair_sum<16>(lsum));
         l_h = l_h * alpha + lsum;
@@ -1719,6 +1729,7 @@ __global__ __launch_bounds__(64 * W) void split_mfma_kernel(const SplitArgs a) {
                 vb[4 + e] = (_Float16)v1[e];
             }
             oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, oacc[nb], 0, 0, 0);
+            oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, vb, oacc[nb], 0, 0, 0);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();

@@ -82,18 +82,20 @@ def test_qwen25_14b_1m_layer_524288(K):
         check(got_o[:, g * 5:(g + 1) * 5], got_l[:, g * 5:(g + 1) * 5], wo, wl)
 
 
-@pytest.mark.parametrize("kind", [O.Q8_B32, O.Q4_B32])
-def test_gqa6_quantized_four_slots(K, kind):
+@pytest.mark.parametrize("kind,v_kind", [(O.Q8_B32, O.Q8_B32), (O.Q4_B32, O.Q4_B32), (O.Q8_B32, O.Q4_B32)])
+def test_gqa6_quantized_four_slots(K, kind, v_kind):
     """24 q heads, 4 KV heads, head_dim 256, slots of 131072 / 65536 / 20000 /
     777 cells in 1700 interleaved 128-cell records (215 holes), all four
-    slots in one launch.  Slots 2 and 3 checked whole, slot 0 on KV head 1."""
+    slots in one launch, the benchmark's plan.  Slots 1, 2 and 3 checked
+    whole, slot 0 on each of its four KV heads."""
     import torch
     lengths = [131072, 65536, 20000, 777]
     lists, cap = synth.interleaved_record_lists(lengths)
     kc, ks = synth.device_quant_cache(3000 + kind, kind, cap, 4, 256)
-    vc, vs = synth.device_quant_cache(3100 + kind, kind, cap, 4, 256)
+    vc, vs = synth.device_quant_cache(3100 + v_kind, v_kind, cap, 4, 256)
     q = synth.device_q(3002, 4, 24, 256)
-    p = K.plan(24, 4, 256, 4, cap, k_type=kind, v_type=kind, cells=lists)
+    p = K.plan(24, 4, 256, 4, cap, k_type=kind, v_type=v_kind, cells=lists)
+    assert p.info()["matrix_cores"] == 1
     entries, off = p.cells()
     assert len(entries) == cap and int((entries == -1).sum()) == 215
     plan_cells = torch.from_numpy(entries).cuda()
@@ -103,15 +105,23 @@ def test_gqa6_quantized_four_slots(K, kind):
     torch.cuda.synchronize()
     go, gl = out.cpu().numpy(), lse.cpu().numpy()
     scale = 1 / 16
-    kh, vh, ksh, vsh = kc.cpu().numpy(), vc.cpu().numpy(), bits(ks), bits(vs)
-    for s in (2, 3):
+    for s in (1, 2, 3):
         seg = entries[off[s]:off[s + 1]]
-        wo, wl = O.decode_attention(q[s:s + 1].cpu().numpy(), [((kind, kh, ksh), (kind, vh, vsh), [seg])], 4, scale)
+        live = torch.from_numpy(seg[seg >= 0].astype(np.int64)).cuda()
+        # only the slot's own rows travel to the host; holes dropped
+        sub = [t.index_select(0, live).cpu().numpy() for t in (kc, vc)]
+        ssub = [bits(t.index_select(0, live)) for t in (ks, vs)]
+        wo, wl = O.decode_attention(q[s:s + 1].cpu().numpy(), [((kind, sub[0], ssub[0]), (v_kind, sub[1], ssub[1]),
+                                                                [np.arange(len(live))])], 4, scale)
         check(go[s:s + 1], gl[s:s + 1], wo, wl)
     seg0 = entries[off[0]:off[1]]
-    res = oracle_heads(K, q[0:1], kc, vc, (1,), 6, scale, kind=kind, ks=ks, vs=vs, cells=[seg0])
-    wo, wl = res[1]
-    check(go[0:1, 6:12], gl[0:1, 6:12], wo, wl)
+    live0 = torch.from_numpy(seg0[seg0 >= 0].astype(np.int64)).cuda()
+    for g in range(4):
+        k0, v0 = (t.index_select(0, live0)[:, g:g + 1].cpu().numpy() for t in (kc, vc))
+        ks0, vs0 = (bits(t.index_select(0, live0)[:, g:g + 1]) for t in (ks, vs))
+        wo, wl = O.decode_attention(q[0:1, 6 * g:6 * g + 6].cpu().numpy(),
+                                    [((kind, k0, ks0), (v_kind, v0, vs0), [np.arange(len(live0))])], 1, scale)
+        check(go[0:1, 6 * g:6 * g + 6], gl[0:1, 6 * g:6 * g + 6], wo, wl)
 
 
 def test_rolling_window_ctx40960_layer(K):
@@ -140,6 +150,48 @@ def test_rolling_window_ctx40960_layer(K):
                               8, 1 / math.sqrt(128))
     check(out.cpu().numpy(), lse.cpu().numpy(), *want)
     check(out.cpu().numpy(), lse.cpu().numpy(), ro.cpu().numpy(), rl.cpu().numpy(), tol=TOL_SPLITS)
+
+
+@pytest.mark.parametrize("mode", ["staged", "zerocopy", "prefetch"])
+def test_rolling_window_ctx40960_bench_plan(K, mode):
+    """The rolling-window layer as the benchmark plans it: the whole
+    26960-cell tail in one 27008-cell chunk, ring depth 4 (clamped to the one
+    chunk); staged through the ring, read in place, or two layers on two
+    workspaces with the tail copies ordered after the previous layer's event
+    (cross-layer prefetch).  Every layer checked whole against the oracle."""
+    import torch
+    ctx, win = 40960, 14000
+    tail = ctx - win
+    chunk = -(-tail // 128) * 128
+    assert chunk == 27008
+    layers = 2 if mode == "prefetch" else 1
+    pt = K.plan(32, 8, 128, 1, ctx, n_occupied=[win], cell_begin=[tail], n_tail=[tail], tail_capacity_cells=tail,
+                tail_chunk_cells=chunk, tail_ring_depth=4, tail_zero_copy=mode == "zerocopy")
+    assert pt.info()["n_tail_chunks"] == 1
+    ws = [K.workspace(pt) for _ in range(layers)]
+    ev = [torch.cuda.Event() for _ in range(layers)]
+    cs = torch.cuda.Stream()
+    data = []
+    for layer in range(layers):
+        k = synth.device_f16_cache(5100 + 3 * layer, ctx, 8, 128)
+        v = synth.device_f16_cache(5101 + 3 * layer, ctx, 8, 128)
+        q = synth.device_q(5102 + 3 * layer, 1, 32, 128)
+        hk = torch.empty((tail, 8, 128), dtype=torch.float16, pin_memory=True)
+        hv = torch.empty((tail, 8, 128), dtype=torch.float16, pin_memory=True)
+        hk.copy_(k[:tail])
+        hv.copy_(v[:tail])
+        out, lse = torch.empty(1, 32, 128, device="cuda"), torch.empty(1, 32, device="cuda")
+        data.append((k, v, q, hk, hv, out, lse))
+    torch.cuda.synchronize()
+    for layer, (k, v, q, hk, hv, out, lse) in enumerate(data):
+        K.attend(pt, q, k, v, ws[layer], out=out, lse=lse, k_tail=hk, v_tail=hv, copy_stream=cs,
+                 copy_after=ev[layer - 1] if mode == "prefetch" and layer > 0 else None)
+        ev[layer].record()
+    torch.cuda.synchronize()
+    for k, v, q, hk, hv, out, lse in data:
+        want = O.decode_attention(q.cpu().numpy(), [((O.F16, bits(k), None), (O.F16, bits(v), None),
+                                                     [np.arange(ctx)])], 8, 1 / math.sqrt(128))
+        check(out.cpu().numpy(), lse.cpu().numpy(), *want)
 
 
 def test_qwen3_8b_verify4_layer(K):
