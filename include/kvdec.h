@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_VERSION 10600 /* 1.6.0: kvdec_attend_static */
+#define KVDEC_VERSION 10700 /* 1.7.0: kvdec_io.live_records */
 
 /* Status codes. */
 #define KVDEC_OK 0
@@ -245,6 +245,13 @@ typedef struct kvdec_plan kvdec_plan_t;
  *   that alternates two workspaces between consecutive layers can record an
  *   event after call l and pass it to call l + 2: the copies of layer l + 1
  *   then overlap layer l's kernels (cross-layer tail prefetch).
+ * live_records: device int32 [n_slots] or NULL, indirect plans only: slot s
+ *   uses only its first live_records[s] 128-entry segments of entries (values
+ *   below 0 read as 0, above the slot's segments as all of them); the rest
+ *   are never read.  The first n_slots values of kvdec_build_cells'
+ *   n_records output fit: the -1 segments that pad a device-built plan up
+ *   to max_records are then skipped instead of scanned (the result is the
+ *   same either way: a hole contributes nothing).
  */
 typedef struct kvdec_io {
     const float* q;
@@ -269,6 +276,7 @@ typedef struct kvdec_io {
     const int32_t* q_pos;
     const int32_t* cell_pos;
     void* copy_after;
+    const int32_t* live_records;
 } kvdec_io;
 
 /* One partial result set for kvdec_merge: rows are (slot, query head) pairs,

@@ -93,6 +93,8 @@ int check_io(const kvdec_plan_t& p, const kvdec_io* io) {
     if (p.n_q > 1 && (!io->q_pos || !aligned(io->q_pos, 4)))
         return fail(KVDEC_E_INVALID, "several query rows per slot need q_pos (device int32 [n_slots][n_queries])");
     if (!aligned(io->cell_pos, 4)) return fail(KVDEC_E_INVALID, "cell_pos must be 4-byte aligned");
+    if (io->live_records && (!p.indirect || !aligned(io->live_records, 4)))
+        return fail(KVDEC_E_INVALID, "live_records needs an indirect plan and 4-byte alignment");
     if (!kvdec::split_instance_exists(D, p.group, p.n_q, p.k_type, p.v_type, p.mfma))
         return fail(KVDEC_E_UNSUPPORTED, "no kernel for this configuration");
     return KVDEC_OK;
@@ -122,6 +124,7 @@ int attend_checked(const kvdec_plan_t& p, const kvdec_io* io, uint8_t* ws, uint3
     a.v_cs = v_cs;
     a.v_hs = v_hs;
     a.plan = p.indirect ? io->plan_cells : nullptr;
+    a.live_records = p.indirect ? io->live_records : nullptr;
     a.capacity = p.capacity;
     a.part_o = reinterpret_cast<float*>(ws + p.off_parts);
     a.part_m = reinterpret_cast<float*>(ws + p.off_parts_m);

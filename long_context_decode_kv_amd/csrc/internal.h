@@ -103,6 +103,7 @@ struct SplitArgs {
     int64_t k_cs, k_hs;      // byte strides (cell, head) of K rows
     int64_t v_cs, v_hs;
     const int32_t* plan;     // indirect entries, or null for contiguous cells
+    const int32_t* live_records;  // [slots] 128-entry records in use at the front of each slot's entries, or null
     int64_t capacity;        // cells addressable through k / v (indirect bound check)
     float* part_o;           // split partial records: o [record][G][D]
     float* part_m;           //   running max in log2 units [record][G]

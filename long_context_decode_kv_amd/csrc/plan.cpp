@@ -327,6 +327,11 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
     for (auto& sa : plan.slots) {
         const int64_t ns = std::max<int64_t>(1, ceil_div(sa.n_units, ups));
         sa.n_splits = (int32_t)ns;
+        // A device-built plan's entries are a record budget: its splits are
+        // fixed runs of ups units (the last one ragged; positions past the
+        // slot's entries are clipped), so the records in use split the same
+        // way -- and give the same result, bit for bit -- whatever the budget.
+        if (device_cells) sa.n_units = ns * ups;
         sa.wg_begin = (int32_t)wgs;
         sa.part_begin = (int32_t)wgs;
         sa.to_acc = 0;

@@ -229,6 +229,29 @@ __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
     return (float)__builtin_bit_cast(_Float16, b);
 }
 
+// End of the positions of slot s worth reading: all of them, or for an
+// indirect plan given the records in use per slot, the first
+// live_records[s] 128-entry segments -- a device-built plan fills the rest
+// of its record budget with segments of holes, which are then never visited.
+__device__ __forceinline__ int64_t live_end(const SplitArgs& a, const SlotArg& sa, int s) {
+    if (!a.plan || !a.live_records) return sa.n;
+    const int64_t r = a.live_records[a.slot_base + s];
+    const int64_t e = (r > 0 ? r : 0) * (int64_t)kTile;
+    return e < sa.n ? e : sa.n;
+}
+
+// Splits of slot s whose positions start below live_end (split sp starts
+// at floor(sp n_units / n_splits) units): with live_records the others hold
+// only entries out of use, and their workgroups leave at once -- they
+// publish nothing and the slot's merge neither waits for nor reads them.
+// At least one, so a slot with nothing in use still writes its outputs.
+__device__ __forceinline__ int live_splits(const SplitArgs& a, const SlotArg& sa, int s) {
+    if (!a.plan || !a.live_records || sa.n_units <= 0) return sa.n_splits;
+    const int64_t e = (live_end(a, sa, s) + a.split_unit - 1) / a.split_unit;  // units in use
+    const int64_t n = (e * sa.n_splits + sa.n_units - 1) / sa.n_units;
+    return n < 1 ? 1 : (n > sa.n_splits ? sa.n_splits : (int)n);
+}
+
 // Lane geometry.  Per-lane d-slice DL: 16 elements for groups up to 5, 8
 // above (register budget).  R lanes per cell, CPW cells per wave per load,
 // NB cells per lane per step, so a step of W waves covers W * CPW * NB cells.
@@ -331,7 +354,7 @@ struct RowMap {
 // not normalised, to record `dest` (a cluster record).
 template <int D, int G, int NT = kThreads>
 __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMap& rm, int64_t rec0, int count,
-                              int64_t dest) {
+                              int64_t dest, int chunk) {
     constexpr int NV = G * D / 4;                           // float4 columns of o
     constexpr int TS = NV >= NT ? 1 : NT / NV;              // threads per column
     constexpr int COLS = (NV + NT - 1) / NT;                // columns per thread
@@ -339,7 +362,7 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMa
     constexpr int UB = (SPC_MAX + TS - 1) / TS;             // records per thread per round
     static_assert(SPC_MAX <= 64 && UB * COLS <= 56, "merge chunk");
     // this slot's round (a constant where the kernel has no choice)
-    const int SPC = SPC_MAX == merge_chunk(D, G) ? SPC_MAX : sa.chunk;
+    const int SPC = SPC_MAX == merge_chunk(D, G) ? SPC_MAX : chunk;
     constexpr int NW = NT / 64;                             // waves
     __shared__ float f_m[64 * G];
     __shared__ float run_m[G], run_l[G], scale_old[G];
@@ -501,8 +524,8 @@ __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& 
     constexpr int PQ = NT / NV;
     constexpr int P = (NS % 4 == 0 && PQ >= 4) ? 4 : ((NS % 2 == 0 && PQ >= 2) ? 2 : 1);
     const int part = tid % P;
-    const int n_splits = sa.n_splits;
-    const bool single = (n_splits == 1);
+    const int n_splits = sa.n_splits;  // record stride of the (slot, KV head)
+    const bool single = live_splits(a, sa, s) == 1;
     const int64_t rec = sa.part_begin + (int64_t)g * n_splits + split;
     const __amdgpu_buffer_rsrc_t rs = part_rsrc(a);
     for (int v = tid / P; v < NV; v += NT / P) {
@@ -564,32 +587,36 @@ __device__ __forceinline__ void finish_split(const SplitArgs& a, const SlotArg& 
 template <int D, int G, int NT>
 __device__ __forceinline__ void arrive_and_merge(const SplitArgs& a, const SlotArg& sa, int s, int g, int split,
                                                  const RowMap& rm, int& sm_last) {
-    const int n_splits = sa.n_splits;
+    // the splits taking part (all, or those holding entries in use) and the
+    // merge shape the planner gives that many splits
+    const int n_splits = live_splits(a, sa, s);
+    const int chunk = merge_chunk_for(D, G, n_splits);
+    const int ncl = merge_clusters(n_splits, chunk);
     // Records are published (stores complete) before the arrival is counted.
     wait_stores();
     __syncthreads();
     uint32_t* gticket = a.tickets + (int64_t)(a.slot_base + s) * a.n_kv_heads + g;
-    const int64_t srec0 = sa.part_begin + (int64_t)g * n_splits;
-    const int ncl = sa.n_clusters;
+    const int64_t srec0 = sa.part_begin + (int64_t)g * sa.n_splits;
     if (ncl <= 1) {
         // the last workgroup of the (slot, KV head) merges every split
         if (!last_arrival(gticket, n_splits, sm_last)) return;
-        merge_records<D, G, NT>(a, sa, rm, srec0, n_splits, -1);
+        merge_records<D, G, NT>(a, sa, rm, srec0, n_splits, -1, chunk);
         return;
     }
     // two levels: the last of each cluster of splits merges the cluster into
     // a cluster record; the last cluster merger merges the cluster records
-    const int CH = merge_chunk_max(D, G) == merge_chunk(D, G) ? merge_chunk(D, G) : sa.chunk;
+    // (record slots of the plan's sa.n_clusters clusters; ncl <= that)
+    const int CH = merge_chunk_max(D, G) == merge_chunk(D, G) ? merge_chunk(D, G) : chunk;
     const int cid = split / CH;
     const int c0 = cid * CH;
     const int cn = (n_splits - c0) < CH ? (n_splits - c0) : CH;
-    const int64_t cidx = sa.cl_begin + (int64_t)g * ncl + cid;
+    const int64_t cidx = sa.cl_begin + (int64_t)g * sa.n_clusters + cid;
     if (!last_arrival(a.ctickets + cidx, cn, sm_last)) return;
-    merge_records<D, G, NT>(a, sa, rm, srec0 + c0, cn, a.crec_base + cidx);
+    merge_records<D, G, NT>(a, sa, rm, srec0 + c0, cn, a.crec_base + cidx, chunk);
     wait_stores();
     __syncthreads();
     if (!last_arrival(gticket, ncl, sm_last)) return;
-    merge_records<D, G, NT>(a, sa, rm, a.crec_base + sa.cl_begin + (int64_t)g * ncl, ncl, -1);
+    merge_records<D, G, NT>(a, sa, rm, a.crec_base + sa.cl_begin + (int64_t)g * sa.n_clusters, ncl, -1, chunk);
 }
 
 
@@ -641,6 +668,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     // cell row.
     const int split = local / a.n_kv_heads;
     const int g = local - split * a.n_kv_heads;
+    if (split >= live_splits(a, sa, s)) return;  // nothing in use: not part of the merge
     // Positions [pos_begin, pos_end) of the slot: split boundaries fall on
     // multiples of a.split_unit.
     const int64_t pos_begin = (((int64_t)split * sa.n_units) / sa.n_splits) * a.split_unit;
@@ -678,7 +706,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const uint8_t* kbase = a.k + (int64_t)g * a.k_hs;
     const uint8_t* vbase = a.v + (int64_t)g * a.v_hs;
     const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-    const int64_t pos_end = span_end < sa.n ? span_end : sa.n;
+    const int64_t slot_end = live_end(a, sa, s);
+    const int64_t pos_end = span_end < slot_end ? span_end : slot_end;
 
     // One step: NCW cells per lane.  Buffers of a step in flight.
     struct Step {
@@ -1404,13 +1433,18 @@ __global__ __launch_bounds__(64 * W) void split_mfma_kernel(const SplitArgs a) {
     const int li = lane & 15;  // row / column index inside a 16-lane group
     const int lq = lane >> 4;  // lane group
 
-    const int wg = xcd_logical_index(blockIdx.x, a.n_workgroups);
+    // With live_records the splits in use are a prefix of each slot's
+    // range: the dispatch order itself (workgroup b on XCD b % 8) spreads
+    // them evenly over the XCDs, where per-XCD blocks of the renumbering
+    // could leave one XCD all of them.
+    const int wg = a.live_records ? (int)blockIdx.x : xcd_logical_index(blockIdx.x, a.n_workgroups);
     int s = 0;
     while (s + 1 < a.n_slots && a.slot[s + 1].wg_begin <= wg) ++s;
     const SlotArg sa = a.slot[s];
     const int local = wg - sa.wg_begin;
     const int split = local / a.n_kv_heads;
     const int g = local - split * a.n_kv_heads;
+    if (split >= live_splits(a, sa, s)) return;  // nothing in use: not part of the merge
     const int64_t base0 = (((int64_t)split * sa.n_units) / sa.n_splits) * a.split_unit;
     const int64_t span_end = (((int64_t)(split + 1) * sa.n_units) / sa.n_splits) * a.split_unit;
     // Record row r = t * grp + hh is query row t of the slot, head g * grp + hh.
@@ -1464,7 +1498,8 @@ __global__ __launch_bounds__(64 * W) void split_mfma_kernel(const SplitArgs a) {
     const uint8_t* vbase = a.v + (int64_t)g * a.v_hs;
     unsigned char* vst = smem + wave * 32 * VSTR;
     const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-    const int64_t pos_end = span_end < sa.n ? span_end : sa.n;
+    const int64_t slot_end = live_end(a, sa, s);
+    const int64_t pos_end = span_end < slot_end ? span_end : slot_end;
     // one step per SC positions: 32 cells per wave
     const int n_steps = pos_end > base0 ? (int)((pos_end - base0 + SC - 1) / SC) : 0;
 

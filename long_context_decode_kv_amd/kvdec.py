@@ -64,7 +64,7 @@ class IO(ctypes.Structure):
         ("plan_cells", _p),
         ("k_tail", _p), ("v_tail", _p), ("k_tail_scales", _p), ("v_tail_scales", _p),
         ("out", _p), ("lse", _p), ("part_m", _p), ("part_l", _p), ("part_o", _p),
-        ("q_pos", _p), ("cell_pos", _p), ("copy_after", _p),
+        ("q_pos", _p), ("cell_pos", _p), ("copy_after", _p), ("live_records", _p),
     ]
 
 
@@ -262,8 +262,9 @@ def workspace(plan_, device="cuda"):
 
 
 def _io(q, k, v, out, lse, part, k_scales, v_scales, plan_cells, k_cell_stride, k_head_stride, v_cell_stride,
-        v_head_stride, k_tail, v_tail, k_tail_scales, v_tail_scales, q_pos, cell_pos, copy_after):
+        v_head_stride, k_tail, v_tail, k_tail_scales, v_tail_scales, q_pos, cell_pos, copy_after, live_records):
     io = IO()
+    io.live_records = _ptr(live_records)
     io.q, io.k, io.v = _ptr(q), _ptr(k), _ptr(v)
     io.k_scales, io.v_scales = _ptr(k_scales), _ptr(v_scales)
     io.k_cell_stride, io.k_head_stride = k_cell_stride, k_head_stride
@@ -283,15 +284,17 @@ def _io(q, k, v, out, lse, part, k_scales, v_scales, plan_cells, k_cell_stride, 
 def attend(plan_, q, k, v, ws, *, out=None, lse=None, part=None, k_scales=None, v_scales=None, plan_cells=None,
            k_cell_stride=0, k_head_stride=0, v_cell_stride=0, v_head_stride=0, k_tail=None, v_tail=None,
            k_tail_scales=None, v_tail_scales=None, q_pos=None, cell_pos=None, stream=None, copy_stream=None,
-           copy_after=None):
+           copy_after=None, live_records=None):
     """Enqueue one evaluation (see kvdec_attend in include/kvdec.h).
     ``part`` is an optional (m, l, o) tuple of output tensors; ``q_pos``
     (int32 [slots][n_queries]) and ``cell_pos`` (int32 [capacity]) are the
     positions of the multi-query mask.  ``copy_after`` (a torch.cuda.Event
     or raw hipEvent_t) orders the tail copies after that event instead of
-    after all earlier work on the stream."""
+    after all earlier work on the stream.  ``live_records`` (int32 [slots],
+    indirect plans) limits each slot to its first segments of entries, e.g.
+    the n_records output of build_cells."""
     io = _io(q, k, v, out, lse, part, k_scales, v_scales, plan_cells, k_cell_stride, k_head_stride, v_cell_stride,
-             v_head_stride, k_tail, v_tail, k_tail_scales, v_tail_scales, q_pos, cell_pos, copy_after)
+             v_head_stride, k_tail, v_tail, k_tail_scales, v_tail_scales, q_pos, cell_pos, copy_after, live_records)
     nbytes = ws.numel() * ws.element_size() if hasattr(ws, "numel") else int(ws[1])
     wptr = _ptr(ws) if hasattr(ws, "numel") else int(ws[0])
     st = _stream_handle(stream)
@@ -301,12 +304,12 @@ def attend(plan_, q, k, v, ws, *, out=None, lse=None, part=None, k_scales=None, 
 
 def attend_static(plan_, q, k, v, *, out=None, lse=None, part=None, k_scales=None, v_scales=None, plan_cells=None,
                   k_cell_stride=0, k_head_stride=0, v_cell_stride=0, v_head_stride=0, k_tail=None, v_tail=None,
-                  k_tail_scales=None, v_tail_scales=None, q_pos=None, cell_pos=None, stream=None):
+                  k_tail_scales=None, v_tail_scales=None, q_pos=None, cell_pos=None, stream=None, live_records=None):
     """attend() with the library's static per-device scratch in place of a
     workspace (see kvdec_attend_static in include/kvdec.h): allocates
     nothing; calls that may overlap on one GPU race."""
     io = _io(q, k, v, out, lse, part, k_scales, v_scales, plan_cells, k_cell_stride, k_head_stride, v_cell_stride,
-             v_head_stride, k_tail, v_tail, k_tail_scales, v_tail_scales, q_pos, cell_pos, None)
+             v_head_stride, k_tail, v_tail, k_tail_scales, v_tail_scales, q_pos, cell_pos, None, live_records)
     _check(lib.kvdec_attend_static(plan_.handle, ctypes.byref(io), _stream_handle(stream)), "kvdec_attend_static")
 
 

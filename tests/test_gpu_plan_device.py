@@ -103,3 +103,84 @@ def test_attend_through_device_built_plan_and_rebuild(K):
         oc = [O.compact_plan([x], c.capacity)[0] for x in lists]
         wo, wl = O.decode_attention(c.q, [((c.kind, c.kc, c.ks), (c.vkind, c.vc, c.vs), oc)], c.hkv, c.scale)
         check(out.cpu().numpy(), lse.cpu().numpy(), wo, wl)
+
+
+@pytest.mark.parametrize("kind", [O.Q8_B32, O.Q4_B32])
+@pytest.mark.parametrize("size", ["one-level", "two-level"])
+def test_generous_budget_bit_equal_to_tight(K, kind, size):
+    """The same lists through a tight record budget (each slot's own record
+    count) and a generous one, 1024-cell splits, matrix-core kernel: the
+    outputs are bit-equal with and without live_records -- a hole segment
+    adds nothing, and the extra splits only add empty records to a merge of
+    the same shape: every slot has 2 to 32 splits in both plans (one level),
+    or more than 32 in both (two levels: clusters of 16 consecutive splits,
+    the extra ones empty).  The two-level case (1152 workgroups tight, 2304
+    generous) shows the cost of scanning the padding and that live_records
+    -- the records in use, as kvdec_build_cells reports them -- removes it."""
+    import torch
+    r = synth.rng(310 + kind + (0 if size == "one-level" else 20))
+    if size == "one-level":
+        lists, cap = synth.interleaved_record_lists([4000, 3000, 2500], r, shuffle=True)
+    else:
+        lists, cap = synth.interleaved_record_lists([131072, 98304, 65536], r)
+    _, counts = expected(lists, cap, [0, 0, 0])
+    tight = list(counts)
+    generous = [min(3 * t + 8 if size == "one-level" else 2 * t, -(-cap // 128)) for t in tight]
+    q = synth.gen_q(r, 3, 24, 256)
+    kd, ksd = synth.device_quant_cache(330 + kind, kind, cap, 4, 256)
+    vd, vsd = synth.device_quant_cache(340 + kind, kind, cap, 4, 256)
+    qd = dev(q)
+    cells, off = flat(lists)
+    res, times = {}, {}
+    for name, budget in (("tight", tight), ("generous", generous)):
+        p = K.plan(24, 4, 256, 3, cap, k_type=kind, v_type=kind, max_records=budget, split_cells=1024)
+        assert p.info()["matrix_cores"] == 1
+        per_slot = np.bincount(p.splits()[:, 0], minlength=3) // 4  # split table rows / KV heads
+        if size == "one-level":
+            assert np.all(per_slot >= 2) and np.all(per_slot <= 32), per_slot
+        else:
+            assert np.all(per_slot > 32), per_slot
+        ws = K.workspace(p)
+        pc = torch.empty(p.info()["n_entries"], dtype=torch.int32, device="cuda")
+        nrec = torch.empty(4, dtype=torch.int32, device="cuda")
+        K.build_cells(p, dev(cells), dev(off), pc, ws, n_records=nrec)
+        torch.cuda.synchronize()
+        assert list(nrec.cpu().numpy()[:3]) == tight
+        for live in (None, nrec):
+            out = torch.full((3, 24, 256), float("nan"), device="cuda")
+            lse = torch.full((3, 24), float("nan"), device="cuda")
+
+            def call():
+                K.attend(p, qd, kd, vd, ws, out=out, lse=lse, k_scales=ksd, v_scales=vsd, plan_cells=pc,
+                         live_records=live)
+
+            call()
+            torch.cuda.synchronize()
+            key = (name, live is not None)
+            res[key] = (out.cpu().numpy(), lse.cpu().numpy())
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(20):
+                call()
+            b.record()
+            torch.cuda.synchronize()
+            times[key] = a.elapsed_time(b) * 1e3 / 20
+    ref = res[("tight", False)]
+    for key, got in res.items():
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), key
+    # the oracle on the smallest slot (its rows gathered on the device)
+    entries = expected(lists, cap, tight)[0]
+    bounds = np.concatenate([[0], np.cumsum(tight)]) * 128
+    seg = entries[bounds[2]:bounds[3]]
+    live_cells = torch.from_numpy(seg[seg >= 0].astype(np.int64)).cuda()
+    kh, vh = (t.index_select(0, live_cells).cpu().numpy() for t in (kd, vd))
+    ksh, vsh = (t.index_select(0, live_cells).contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                for t in (ksd, vsd))
+    want = O.decode_attention(q[2:3], [((kind, kh, ksh), (kind, vh, vsh), [np.arange(len(live_cells))])], 4, 1 / 16)
+    check(ref[0][2:3], ref[1][2:3], *want)
+    print("\nus per call:", {f"{k[0]}{'+live' if k[1] else ''}": round(v, 2) for k, v in times.items()})
+    # padding skipped: within 15% of the tight plan's time (plus launch noise)
+    assert times[("generous", True)] <= 1.15 * times[("tight", False)] + 3.0
+    if size == "two-level":
+        # without live_records the padding is scanned: visibly slower
+        assert times[("generous", False)] > 1.3 * times[("generous", True)]

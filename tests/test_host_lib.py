@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
     for name in names:
         assert hasattr(K.lib, name), name
     assert set(names) == set(K.EXPORTED)
-    assert K.version() == 10600
+    assert K.version() == 10700
 
 
 def test_probe_library_exports_and_rejects_bad_arguments():
@@ -305,6 +305,9 @@ def test_attend_validation_before_device_work():
     pt = K.plan(32, 8, 128, 1, 4096, n_occupied=[10], n_tail=[10], tail_capacity_cells=10, n_cu=256)
     wst = (FAKE, pt.workspace_bytes)
     assert _status(lambda: K.attend(pt, FAKE, FAKE, FAKE, wst, out=FAKE, stream=0)) == K.E_INVALID      # tail arrays missing
+    assert _status(lambda: K.attend(p, FAKE, FAKE, FAKE, ws, live_records=FAKE, **args)) == K.E_INVALID  # contiguous
+    assert _status(lambda: K.attend(pi, FAKE, FAKE, FAKE, wsi, out=FAKE, k_scales=FAKE, v_scales=FAKE, plan_cells=FAKE,
+                                    live_records=FAKE + 2, stream=0)) == K.E_INVALID     # misaligned live_records
 
 
 def test_attend_static_validation_before_device_work():
@@ -427,6 +430,27 @@ def test_device_built_plan_shape_and_errors():
     assert _status(lambda: K.build_cells(p, 0, FAKE, FAKE, ws, stream=0)) == K.E_INVALID
     host = K.plan(24, 4, 256, 1, 5000, cells=[[1, 2]], n_cu=256)
     assert _status(lambda: K.build_cells(host, FAKE, FAKE, FAKE, ws, stream=0)) == K.E_INVALID  # not device-built
+
+
+def test_device_built_splits_fixed_runs_whatever_the_budget():
+    """Splits of a device-built plan are runs of split_cells positions from
+    the slot's start (the last one ragged), so a larger record budget only
+    appends splits: the ones over the records of the smaller budget are the
+    same."""
+    def table(budget):
+        p = K.plan(24, 4, 256, 2, 20000, k_type=K.Q8_B32, v_type=K.Q8_B32, max_records=budget, split_cells=1024,
+                   n_cu=256)
+        t = p.splits()
+        return {(int(s), int(g)): [] for s, g in t[:, :2]}, t
+    for tight, generous in (([20, 7], [68, 29]), ([3, 1], [4, 2]), ([33, 9], [140, 30])):
+        _, a = table(tight)
+        _, b = table(generous)
+        for s in range(2):
+            ra, rb = a[(a[:, 0] == s) & (a[:, 1] == 0)], b[(b[:, 0] == s) & (b[:, 1] == 0)]
+            assert np.all(rb[:, 2] % 1024 == 0) and np.all(ra[:, 2] % 1024 == 0)
+            assert np.array_equal(ra[:-1], rb[:len(ra) - 1])        # the same full runs
+            assert ra[-1, 2] == rb[len(ra) - 1, 2]                   # the ragged one starts where its run does
+            assert ra[:, 3].sum() == tight[s] * 128
 
 
 def test_build_rejects_kernels_with_scratch():
