@@ -26,6 +26,10 @@ SOURCES = ["kernels.hip", "split_f16.hip", "split_q8.hip", "split_q4.hip", "spli
 # the streaming-read probe (bandwidth ceiling for the benchmark) is a library of its own
 PROBE_SOURCES = ["probe.hip"]
 PROBE_LIB = os.path.join(PKG, "libkvprobe.so")
+# test build: the same objects, api.cpp compiled with KVDEC_FAULT_INJECTION
+# (host-side failure injection of the tail streamer) plus its switches
+FI_LIB = os.path.join(PKG, "libkvdec_fi.so")
+FI_SOURCES = ["fault_injection.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",
@@ -84,8 +88,8 @@ def _scratch_kernels(log):
     return found
 
 
-def _compile(src, extra):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src, extra, suffix=""):
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + suffix + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     remarks = RESOURCE_REMARKS if src.endswith(".hip") else []
     cmd = [hipcc()] + lang + FLAGS + remarks + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -104,16 +108,19 @@ HASH_FILE = LIB + ".srchash"
 
 def build(verbose=False, extra=()):
     os.makedirs(BUILD, exist_ok=True)
-    srcs = SOURCES + PROBE_SOURCES
     digest = source_hash()
     hash_def = ['-DKVDEC_SOURCE_HASH="%s"' % digest]
-    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
-        results = dict(zip(srcs, ex.map(lambda s: _compile(s, list(extra) + hash_def), srcs)))
+    jobs = [(s, list(extra) + hash_def, "") for s in SOURCES + PROBE_SOURCES + FI_SOURCES]
+    jobs.append(("api.cpp", list(extra) + hash_def + ["-DKVDEC_FAULT_INJECTION"], "_fi"))
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        outs = list(ex.map(lambda j: _compile(*j), jobs))
+    results = {j[0] + j[2]: o for j, o in zip(jobs, outs)}
     if verbose:
         for _, log in results.values():
             if log.strip():
                 print(log, file=sys.stderr)
-    for lib, names in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES)):
+    fi_names = [n for n in SOURCES if n != "api.cpp"] + ["api.cpp_fi"] + FI_SOURCES
+    for lib, names in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES), (FI_LIB, fi_names)):
         tmp = lib + ".tmp"
         cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [results[n][0] for n in names]
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -137,7 +144,7 @@ def built_hash():
 def ensure_built():
     """Build when the libraries are missing or were built from other
     sources than the current ones (the recorded source hash differs)."""
-    if not (os.path.exists(LIB) and os.path.exists(PROBE_LIB)) or built_hash() != source_hash():
+    if not all(os.path.exists(x) for x in (LIB, PROBE_LIB, FI_LIB)) or built_hash() != source_hash():
         build()
 
 

@@ -53,7 +53,33 @@ void common_args(const kvdec_plan_t& p, const kvdec_io& io, kvdec::SplitArgs& a)
 
 }  // namespace
 
+#ifdef KVDEC_FAULT_INJECTION
+namespace kvdec {
+bool fi_fail_copy();
+bool fi_fail_launch();
+int fi_delay(void* stream);
+}  // namespace kvdec
+#endif
+
 namespace {
+
+// Host-to-device copy of tail rows (a test build can make one fail without
+// enqueueing it).
+hipError_t tail_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
+#ifdef KVDEC_FAULT_INJECTION
+    if (kvdec::fi_fail_copy()) return hipErrorUnknown;
+#endif
+    return hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, s);
+}
+
+// Split-kernel launch for the plan (a test build can make one fail without
+// enqueueing it).
+int launch(const kvdec_plan_t& p, const kvdec::SplitArgs& a, void* stream) {
+#ifdef KVDEC_FAULT_INJECTION
+    if (kvdec::fi_fail_launch()) return (int)hipErrorLaunchFailure;
+#endif
+    return kvdec::launch_split(p.head_dim, p.group, p.n_q, p.k_type, p.v_type, p.mfma, a, stream);
+}
 
 // The checks of kvdec_io against a plan shared by kvdec_attend and
 // kvdec_attend_static (everything but the workspace); no device calls.
@@ -145,7 +171,7 @@ int attend_checked(const kvdec_plan_t& p, const kvdec_io* io, uint8_t* ws, uint3
     }
 
     if (!p.has_tail) {
-        const int e = kvdec::launch_split(D, p.group, p.n_q, p.k_type, p.v_type, p.mfma, a, stream);
+        const int e = launch(p, a, stream);
         if (e != hipSuccess) return device_fail((hipError_t)e, "split kernel launch");
         return KVDEC_OK;
     }
@@ -216,7 +242,7 @@ int attend_checked(const kvdec_plan_t& p, const kvdec_io* io, uint8_t* ws, uint3
             return device_fail(e, "stream ordering");
         }
     }
-    int le = kvdec::launch_split(D, p.group, p.n_q, p.k_type, p.v_type, p.mfma, a, stream);
+    int le = launch(p, a, stream);
     if (le != hipSuccess) {
         destroy();
         return device_fail((hipError_t)le, "window kernel launch");
@@ -243,13 +269,13 @@ int attend_checked(const kvdec_plan_t& p, const kvdec_io* io, uint8_t* ws, uint3
                 uint8_t* slot = ws + p.off_ring + (size_t)r * p.ring_slot_bytes;
                 if (chunk_no >= depth) e = hipStreamWaitEvent(cs, ev_free[r], 0);
                 if (e == hipSuccess)
-                    e = hipMemcpyAsync(slot + p.ring_k, hk + c0 * krow_b, nc * krow_b, hipMemcpyHostToDevice, cs);
+                    e = tail_copy(slot + p.ring_k, hk + c0 * krow_b, nc * krow_b, cs);
                 if (e == hipSuccess)
-                    e = hipMemcpyAsync(slot + p.ring_v, hv + c0 * vrow_b, nc * vrow_b, hipMemcpyHostToDevice, cs);
+                    e = tail_copy(slot + p.ring_v, hv + c0 * vrow_b, nc * vrow_b, cs);
                 if (e == hipSuccess && kvdec::is_scaled(p.k_type))
-                    e = hipMemcpyAsync(slot + p.ring_ks, hks + c0 * srow_b, nc * srow_b, hipMemcpyHostToDevice, cs);
+                    e = tail_copy(slot + p.ring_ks, hks + c0 * srow_b, nc * srow_b, cs);
                 if (e == hipSuccess && kvdec::is_scaled(p.v_type))
-                    e = hipMemcpyAsync(slot + p.ring_vs, hvs + c0 * srow_b, nc * srow_b, hipMemcpyHostToDevice, cs);
+                    e = tail_copy(slot + p.ring_vs, hvs + c0 * srow_b, nc * srow_b, cs);
                 if (e == hipSuccess) e = hipEventRecord(ev_landed[r], cs);
                 if (e == hipSuccess && cs != ks) e = hipStreamWaitEvent(ks, ev_landed[r], 0);
                 if (e != hipSuccess) break;
@@ -302,7 +328,14 @@ int attend_checked(const kvdec_plan_t& p, const kvdec_io* io, uint8_t* ws, uint3
             t.n_workgroups = splits * p.n_kv_heads;
             t.acc_in = acc[c % 2];
             t.acc_out = acc[(c + 1) % 2];
-            le = kvdec::launch_split(D, p.group, p.n_q, p.k_type, p.v_type, p.mfma, t, stream);
+#ifdef KVDEC_FAULT_INJECTION
+            le = kvdec::fi_delay(stream);  // a slow reader of the ring slot
+            if (le != hipSuccess) {
+                e = (hipError_t)le;
+                break;
+            }
+#endif
+            le = launch(p, t, stream);
             if (le != hipSuccess) {
                 e = (hipError_t)le;
                 break;

@@ -20,7 +20,12 @@ import torch  # noqa: F401
 
 from long_context_decode_kv_amd.build import source_hash as _source_hash
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvdec.so")
+# KVDEC_LIB_NAME=libkvdec_fi.so selects the test build with host-side
+# failure injection (kvdec_fi_configure); the product library otherwise
+_LIB_NAME = os.environ.get("KVDEC_LIB_NAME", "libkvdec.so")
+if _LIB_NAME not in ("libkvdec.so", "libkvdec_fi.so"):
+    raise ImportError(f"KVDEC_LIB_NAME={_LIB_NAME}: not a build of this package")
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), _LIB_NAME)
 if not os.path.exists(_LIB_PATH):
     raise ImportError(f"{_LIB_PATH} is not built; run: python -m long_context_decode_kv_amd.build")
 lib = ctypes.CDLL(_LIB_PATH)

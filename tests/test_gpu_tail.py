@@ -164,3 +164,92 @@ def test_copy_after_two_workspaces_across_layers(K):
     for c, (o, l), (o2, l2) in zip(layers, base, pre):
         check(o2, l2, *c.oracle())
         assert np.array_equal(o, o2) and np.array_equal(l, l2)
+
+
+@pytest.fixture(scope="module")
+def KF():
+    """The binding over the test build with host-side failure injection
+    (libkvdec_fi.so: the same kernels; kvdec_fi_configure makes the n-th
+    tail copy or split-kernel launch fail without enqueueing it, or delays
+    every tail-chunk kernel behind a bounded sleep kernel)."""
+    import ctypes
+    import importlib.util
+    import os
+    import torch
+    assert torch.cuda.is_available()
+    from long_context_decode_kv_amd import kvdec
+    os.environ["KVDEC_LIB_NAME"] = "libkvdec_fi.so"
+    try:
+        spec = importlib.util.spec_from_file_location("kvdec_fi", kvdec.__file__)
+        m = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(m)
+    finally:
+        del os.environ["KVDEC_LIB_NAME"]
+    assert m.LIB_PATH.endswith("libkvdec_fi.so")
+    m.lib.kvdec_fi_configure.argtypes = [ctypes.c_int] * 3
+    m.lib.kvdec_fi_configure.restype = None
+    yield m
+    m.lib.kvdec_fi_configure(-1, -1, 0)
+
+
+# 3000 tail cells in 512-cell chunks: 6 chunks, 12 copies (K, V), launches
+# 0 (resident window) and 1..6 (chunks)
+@pytest.mark.parametrize("what,n", [("copy", 0), ("copy", 5), ("copy", 11), ("launch", 0), ("launch", 1),
+                                    ("launch", 6)])
+def test_tail_failure_reports_device_error_and_workspace_recovers(KF, what, n):
+    """A failing copy or launch in the middle of the tail stream: the call
+    returns KVDEC_E_DEVICE, no output of the tailed slot is written (they
+    stay NaN), and the next call on the same workspace is correct."""
+    import torch
+    c = Case(61, 32, 8, 128, occupied=[5000])
+    t = 3000
+    p = KF.plan(32, 8, 128, 1, c.capacity, scale=c.scale, n_occupied=[5000 - t], cell_begin=[t], n_tail=[t],
+                tail_begin=[0], tail_capacity_cells=t, tail_chunk_cells=512, tail_ring_depth=2)
+    assert p.info()["n_tail_chunks"] == 6
+    c.upload()
+    hk, hv = pinned(c.kc[:t]), pinned(c.vc[:t])
+    ws = KF.workspace(p)
+    cs = torch.cuda.Stream()
+    out = torch.full((1, 32, 128), float("nan"), device="cuda")
+    lse = torch.full((1, 32), float("nan"), device="cuda")
+    KF.lib.kvdec_fi_configure(n if what == "copy" else -1, n if what == "launch" else -1, 0)
+    try:
+        with pytest.raises(KF.KvdecError) as err:
+            KF.attend(p, c.q_d, c.kc_d, c.vc_d, ws, out=out, lse=lse, k_tail=hk, v_tail=hv, copy_stream=cs)
+    finally:
+        KF.lib.kvdec_fi_configure(-1, -1, 0)
+    assert err.value.status == KF.E_DEVICE
+    torch.cuda.synchronize()  # whatever was enqueued before the failure ends normally
+    assert torch.isnan(out).all() and torch.isnan(lse).all()
+    KF.attend(p, c.q_d, c.kc_d, c.vc_d, ws, out=out, lse=lse, k_tail=hk, v_tail=hv, copy_stream=cs)
+    torch.cuda.synchronize()
+    check(out.cpu().numpy(), lse.cpu().numpy(), *c.oracle())
+
+
+@pytest.mark.parametrize("depth", [2, 3])
+def test_ring_reuse_waits_for_slow_readers(KF, depth):
+    """Every tail-chunk kernel starts ~0.2 ms late (a bounded sleep kernel
+    ahead of it on the compute stream) while the copies run ahead on their
+    own stream: a copy into a ring slot must still wait until the kernel
+    reading the slot's previous chunk has finished, or that kernel would read
+    the next chunk's rows.  18 chunks through 2 or 3 slots, checked against
+    the oracle and the all-resident result."""
+    import time
+    import torch
+    c = Case(62, 32, 8, 128, occupied=[6000])
+    res_out, res_lse = c.run(KF)
+    wall = []
+    for delay in (0, 60):
+        KF.lib.kvdec_fi_configure(-1, -1, delay)
+        try:
+            t0 = time.perf_counter()
+            out, lse, p = run_tail(KF, c, window=[(4500, 1500)], tail=[(0, 4500)], chunk=256, depth=depth,
+                                   copy_stream=torch.cuda.Stream())
+            wall.append(time.perf_counter() - t0)
+        finally:
+            KF.lib.kvdec_fi_configure(-1, -1, 0)
+        assert p.info()["n_tail_chunks"] == 18
+        check(out, lse, *c.oracle())
+        check(out, lse, res_out, res_lse, tol=TOL_SPLITS)
+    # the delays did run: at least 0.1 ms per chunk kernel on top
+    assert wall[1] - wall[0] > 18 * 1e-4, wall

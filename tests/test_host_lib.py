@@ -453,6 +453,17 @@ def test_device_built_splits_fixed_runs_whatever_the_budget():
             assert ra[:, 3].sum() == tight[s] * 128
 
 
+def test_failure_injection_only_in_the_test_build():
+    """libkvdec_fi.so (the tail streamer's failure-injection switches) is a
+    separate test library; the product library has no such entry point."""
+    from long_context_decode_kv_amd import build
+    fi = ctypes.CDLL(build.FI_LIB)
+    assert hasattr(fi, "kvdec_fi_configure") and hasattr(fi, "kvdec_attend")
+    assert not hasattr(K.lib, "kvdec_fi_configure")
+    fi.kvdec_source_hash.restype = ctypes.c_char_p
+    assert fi.kvdec_source_hash().decode() == K.LIB_SOURCE_HASH
+
+
 def test_build_rejects_kernels_with_scratch():
     """The build parses the compiler's kernel-resource remarks and refuses
     any kernel that needs per-lane scratch memory."""
