@@ -106,7 +106,8 @@ extern "C" {
  *   KVDEC_E_UNSUPPORTED.
  * scale: multiplies q.k before the softmax (usually 1/sqrt(head_dim)).
  * capacity_cells: number of device cells addressable through the K/V
- *   pointers of kvdec_attend; every attended cell must lie below it.
+ *   pointers of kvdec_attend; every attended cell must lie below it.  At
+ *   most 2^48 (so is tail_capacity_cells), else KVDEC_E_INVALID.
  *
  * Cell selection, one of:
  *   contiguous (cells == NULL): slot s attends device cells

@@ -30,6 +30,14 @@ PROBE_LIB = os.path.join(PKG, "libkvprobe.so")
 # (host-side failure injection of the tail streamer) plus its switches
 FI_LIB = os.path.join(PKG, "libkvdec_fi.so")
 FI_SOURCES = ["fault_injection.hip"]
+# test build: the planner and the C-ABI validation (plan.cpp, api.cpp) with
+# AddressSanitizer and UndefinedBehaviorSanitizer on the host side, linked
+# with the ordinary device objects; loaded with the ASan runtime preloaded
+SAN_LIB = os.path.join(PKG, "libkvdec_san.so")
+SAN_HOST = ["plan.cpp", "api.cpp"]
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined"]
 
 FLAGS = [
     "--offload-arch=gfx950",
@@ -112,6 +120,7 @@ def build(verbose=False, extra=()):
     hash_def = ['-DKVDEC_SOURCE_HASH="%s"' % digest]
     jobs = [(s, list(extra) + hash_def, "") for s in SOURCES + PROBE_SOURCES + FI_SOURCES]
     jobs.append(("api.cpp", list(extra) + hash_def + ["-DKVDEC_FAULT_INJECTION"], "_fi"))
+    jobs += [(h, list(extra) + hash_def + SAN_FLAGS, "_san") for h in SAN_HOST]
     with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         outs = list(ex.map(lambda j: _compile(*j), jobs))
     results = {j[0] + j[2]: o for j, o in zip(jobs, outs)}
@@ -120,9 +129,12 @@ def build(verbose=False, extra=()):
             if log.strip():
                 print(log, file=sys.stderr)
     fi_names = [n for n in SOURCES if n != "api.cpp"] + ["api.cpp_fi"] + FI_SOURCES
-    for lib, names in ((LIB, SOURCES), (PROBE_LIB, PROBE_SOURCES), (FI_LIB, fi_names)):
+    san_names = [n for n in SOURCES if n not in SAN_HOST] + [h + "_san" for h in SAN_HOST]
+    san_link = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libasan"]
+    for lib, names, link in ((LIB, SOURCES, []), (PROBE_LIB, PROBE_SOURCES, []), (FI_LIB, fi_names, []),
+                             (SAN_LIB, san_names, san_link)):
         tmp = lib + ".tmp"
-        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [results[n][0] for n in names]
+        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + link + ["-o", tmp] + [results[n][0] for n in names]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -130,6 +142,14 @@ def build(verbose=False, extra=()):
     with open(HASH_FILE, "w") as fh:
         fh.write(digest + "\n")
     return LIB
+
+
+def asan_runtime():
+    """Path of the compiler's shared AddressSanitizer runtime (to preload
+    when loading the sanitizer build into an uninstrumented interpreter)."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    return path if r.returncode == 0 and os.path.isabs(path) and os.path.exists(path) else None
 
 
 def built_hash():
@@ -144,7 +164,7 @@ def built_hash():
 def ensure_built():
     """Build when the libraries are missing or were built from other
     sources than the current ones (the recorded source hash differs)."""
-    if not all(os.path.exists(x) for x in (LIB, PROBE_LIB, FI_LIB)) or built_hash() != source_hash():
+    if not all(os.path.exists(x) for x in (LIB, PROBE_LIB, FI_LIB, SAN_LIB)) or built_hash() != source_hash():
         build()
 
 

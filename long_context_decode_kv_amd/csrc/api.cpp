@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstring>
 #include <new>
+#include <stdexcept>
 #include <string>
 
 #include "internal.h"
@@ -398,6 +399,9 @@ int kvdec_plan(const kvdec_problem* problem, int32_t n_cu, kvdec_plan_t** out, s
     } catch (const std::bad_alloc&) {
         delete plan;
         return fail(KVDEC_E_NOMEM, "host allocation failed while planning");
+    } catch (const std::length_error&) {
+        delete plan;
+        return fail(KVDEC_E_NOMEM, "host allocation too large while planning");
     }
     *out = plan;
     if (workspace_bytes) *workspace_bytes = plan->workspace_bytes;

@@ -15,6 +15,7 @@
 namespace kvdec {
 
 constexpr int kTile = KVDEC_TILE_CELLS;  // cells per tile / per physical record
+constexpr int64_t kMaxCells = int64_t(1) << 48;  // bound of capacity_cells and tail_capacity_cells
 constexpr int kBlock = 32;               // elements sharing one f16 scale
 constexpr int kThreads = 256;            // threads per split workgroup (4 waves)
 constexpr int kSplitUnit = 32;           // split boundary granularity of the vector-ALU kernel

@@ -94,6 +94,12 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
         err = "capacity_cells, tiles_per_split must be >= 0 and n_cu >= 1";
         return KVDEC_E_INVALID;
     }
+    // far beyond any device's memory, and small enough that no cell index or
+    // byte offset computed from it can overflow
+    if (p.capacity_cells > kMaxCells || p.tail_capacity_cells > kMaxCells) {
+        err = "capacity_cells and tail_capacity_cells must be at most 2^48";
+        return KVDEC_E_INVALID;
+    }
     const bool device_cells = p.cells == nullptr && p.max_records != nullptr;
     const bool indirect = p.cells != nullptr || device_cells;
     if (p.cells != nullptr && !p.cells_off) {
@@ -164,7 +170,15 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
                 return KVDEC_E_INVALID;
             }
         }
-        std::vector<uint64_t> bitmap((size_t)ceil_div(std::max<int64_t>(p.capacity_cells, 1), kTile) * (kTile / 64), 0);
+        // the dedup bitmap covers the records up to the largest valid cell
+        // listed (entries are int32, so at most 2^31 cells), not the whole
+        // capacity; compact_slot reports the entries out of range
+        int64_t top = 0;
+        for (int64_t i = p.cells_off[0]; i < p.cells_off[p.n_slots]; ++i) {
+            const int64_t c = p.cells[i];
+            if (c >= 0 && c < p.capacity_cells && c + 1 > top) top = c + 1;
+        }
+        std::vector<uint64_t> bitmap((size_t)ceil_div(std::max<int64_t>(top, 1), kTile) * (kTile / 64), 0);
         std::vector<int64_t> records;
         for (int s = 0; s < p.n_slots; ++s) {
             const int64_t b = p.cells_off[s], e = p.cells_off[s + 1];
@@ -182,9 +196,9 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
         for (int s = 0; s < p.n_slots; ++s) {
             const int64_t b = p.cell_begin ? p.cell_begin[s] : 0;
             const int64_t n = p.n_occupied[s];
-            if (b < 0 || n < 0 || b + n > p.capacity_cells) {
-                err = "slot " + std::to_string(s) + ": cells [" + std::to_string(b) + ", " + std::to_string(b + n) +
-                      ") outside [0, capacity)";
+            if (b < 0 || n < 0 || b > p.capacity_cells || n > p.capacity_cells - b) {
+                err = "slot " + std::to_string(s) + ": cells from " + std::to_string(b) + ", " + std::to_string(n) +
+                      " of them, outside [0, capacity)";
                 return KVDEC_E_RANGE;
             }
             plan.slots[s].first = b;
@@ -393,7 +407,7 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
         for (int s = 0; s < p.n_slots; ++s) {
             const int64_t b = p.tail_begin ? p.tail_begin[s] : 0;
             const int64_t n = p.n_tail[s];
-            if (b < 0 || n < 0 || b + n > plan.tail_capacity) {
+            if (b < 0 || n < 0 || b > plan.tail_capacity || n > plan.tail_capacity - b) {
                 err = "slot " + std::to_string(s) + ": tail cells outside [0, tail_capacity_cells)";
                 return KVDEC_E_RANGE;
             }

@@ -281,6 +281,47 @@ def test_plan_errors():
     assert "tail_chunk_cells" in K.lib.kvdec_last_error().decode()
 
 
+def test_malformed_ranges_are_rejected():
+    """Ranges whose ends overflow int64, offsets that go backwards, record
+    budgets and capacities out of range: each is refused with a status code
+    (run also under the sanitizer build, where any overflow or out-of-bounds
+    read in the planner aborts)."""
+    big = 2 ** 63 - 5
+    cu = dict(n_cu=256)
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, n_occupied=[10], cell_begin=[big], **cu)) == K.E_RANGE
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, n_occupied=[big], cell_begin=[5], **cu)) == K.E_RANGE
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, n_occupied=[-1], **cu)) == K.E_RANGE
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, n_occupied=[1], cell_begin=[-3], **cu)) == K.E_RANGE
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, n_occupied=[1], n_tail=[10], tail_begin=[big],
+                                  tail_capacity_cells=100, **cu)) == K.E_RANGE
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, n_occupied=[1], n_tail=[big], tail_begin=[3],
+                                  tail_capacity_cells=100, **cu)) == K.E_RANGE
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, n_occupied=[1], n_tail=[-2], tail_capacity_cells=100,
+                                  **cu)) == K.E_RANGE
+    assert _status(lambda: K.plan(32, 8, 128, 1, 2 ** 62, n_occupied=[1], **cu)) == K.E_INVALID
+    assert _status(lambda: K.plan(32, 8, 128, 1, 2 ** 63 - 1, cells=[[1]], **cu)) == K.E_INVALID
+    assert _status(lambda: K.plan(32, 8, 128, 1, 100, n_occupied=[1], n_tail=[1], tail_capacity_cells=2 ** 60,
+                                  **cu)) == K.E_INVALID
+    assert _status(lambda: K.plan(32, 8, 128, 1, -1, n_occupied=[0], **cu)) == K.E_INVALID
+    for budget in ([-1], [2 ** 31 - 1], [1, -5]):
+        assert _status(lambda: K.plan(24, 4, 256, len(budget), 5000, k_type=K.Q8_B32, v_type=K.Q8_B32,
+                                      max_records=budget, **cu)) == K.E_INVALID
+    # raw lists with offsets that go backwards or start below zero (the
+    # Problem struct filled by hand: the binding only builds valid offsets)
+    cells = np.array([1, 2, 3, 4], np.int32)
+    for off in ([0, 3, 1], [-1, 2, 4], [2, 1, 4]):
+        o = np.array(off, np.int64)
+        pr = K.Problem(n_q_heads=32, n_kv_heads=8, head_dim=128, n_slots=2, k_type=K.F16, v_type=K.F16, scale=0.1,
+                       capacity_cells=100)
+        pr.cells = cells.ctypes.data
+        pr.cells_off = o.ctypes.data
+        h, ws = ctypes.c_void_p(), ctypes.c_size_t()
+        assert K.lib.kvdec_plan(ctypes.byref(pr), 256, ctypes.byref(h), ctypes.byref(ws)) == K.E_INVALID
+        assert "cells_off" in K.lib.kvdec_last_error().decode()
+    # the planner's memory follows the cells listed, not the capacity
+    assert K.plan(32, 8, 128, 1, 2 ** 48, cells=[[1, 2 ** 31 - 1]], **cu).info()["n_entries"] == 256
+
+
 FAKE = 1 << 20  # an aligned address that is never dereferenced: validation fails first
 
 
