@@ -1363,11 +1363,33 @@ struct Row16 {
     static constexpr int EPC = T == KVDEC_F16 ? 8 : T == KVDEC_Q8_B32 ? 16 : 32;
 };
 
+// Order of the elements of a 4-bit chunk in the matrix-core kernel's f16
+// pairs: pair 4w + k of dword w holds elements 8w + a and 8w + a + 2 with
+// a = 0, 4, 1, 5 for k = 0..3 -- even elements from the low nibbles, odd
+// ones from the high nibbles, each pair one byte permute against the f16
+// exponent byte.  Slot i of an 8-element group holds element q4_order(i).
+__device__ __forceinline__ constexpr int q4_order(int i) { return (i & 3) * 2 + (i >> 2); }
+
 // One 16-byte chunk -> its EPC values as f16 pairs (block-scaled kinds: d * code,
-// rounded to f16).
+// rounded to f16).  4-bit chunks come out in q4_order within each 8 elements.
 template <int T>
 __device__ __forceinline__ void dequant16(const Chunk<16>& c, uint16_t scale_bits, h2 (&out)[Row16<T>::EPC / 2]) {
-    to_pairs<T>(c, out);
+    if constexpr (T == KVDEC_Q4_B32) {
+        // 1024 + u in each f16 (exponent byte 0x64 above the nibble), minus
+        // 1032: u - 8 exactly
+        const h2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t lo = c.w[w] & 0x0F0F0F0Fu;         // elements 0, 2, 4, 6 of the dword
+            const uint32_t hi = (c.w[w] >> 4) & 0x0F0F0F0Fu;  // elements 1, 3, 5, 7
+            out[4 * w + 0] = as_h2(__builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u)) - bias;  // 0, 2
+            out[4 * w + 1] = as_h2(__builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u)) - bias;  // 4, 6
+            out[4 * w + 2] = as_h2(__builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u)) - bias;  // 1, 3
+            out[4 * w + 3] = as_h2(__builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u)) - bias;  // 5, 7
+        }
+    } else {
+        to_pairs<T>(c, out);
+    }
     if constexpr (T != KVDEC_F16) {
         const _Float16 d = __builtin_bit_cast(_Float16, scale_bits);
         const h2 dd = {d, d};
@@ -1477,7 +1499,11 @@ __global__ __launch_bounds__(64 * W) void split_mfma_kernel(const SplitArgs a) {
                     x[e + 1] = v.y;
                 }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) qb[j * (EK / 8) + sub][e] = real_row ? (_Float16)x[e] : (_Float16)0.0f;
+                for (int e = 0; e < 8; ++e) {
+                    // 4-bit K comes out of dequant16 in q4_order: q follows it
+                    const float xe = KT == KVDEC_Q4_B32 ? x[q4_order(e)] : x[e];
+                    qb[j * (EK / 8) + sub][e] = real_row ? (_Float16)xe : (_Float16)0.0f;
+                }
             }
         }
     }
@@ -1793,7 +1819,9 @@ __global__ __launch_bounds__(64 * W) void split_mfma_kernel(const SplitArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int h = 4 * lq + e;
-            if (h < G) sm_o[wave][h][16 * nb + li] = oacc[nb][e] * kMPOffInv;
+            // staged 4-bit V columns sit in q4_order within each 8 columns
+            const int col = VT == KVDEC_Q4_B32 ? ((16 * nb + li) & ~7) + q4_order(li & 7) : 16 * nb + li;
+            if (h < G) sm_o[wave][h][col] = oacc[nb][e] * kMPOffInv;
         }
     __syncthreads();
     finish_split<D, G, W, D, 64 * W>(a, sa, s, g, split, rm, sm_m, sm_l, sm_o, sm_last);
