@@ -1,0 +1,82 @@
+"""Error budget of the kernels' f16 arithmetic, term by term, on the CPU: a
+numpy model of each rounding the kernels apply (q to f16; staged K^ and V^
+to f16 on the matrix-core kernel; softmax weights to f16 toward zero on the
+vector kernels, or as an f16 hi + lo pair on the matrix-core kernel), each
+applied alone to the float64 oracle's exact dequantised values, on seeded
+caches of the benchmark workloads' value distribution.  It says which term
+dominates: for out every term is about 1e-5, far inside 2e-3; for lse the
+toward-zero weights dominate (they bias l down by about 2^-11 of itself,
+which the hi + lo pair removes).  This is a model of the kernels for
+accounting, in the tests, not part of the oracle."""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from long_context_decode_kv_amd import synth
+
+
+def f16(x):
+    return np.asarray(x, np.float64).astype(np.float16).astype(np.float64)
+
+
+def f16_toward_zero(x):
+    x = np.asarray(x, np.float64)
+    r = x.astype(np.float16)
+    away = np.abs(r.astype(np.float64)) > np.abs(x)
+    r[away] = np.nextafter(r[away], np.float16(0))
+    return r.astype(np.float64)
+
+
+def attend(q, k, v, scale, qr=None, kvr=None, pr=None):
+    """Softmax attention of rows q over (k, v) with optional roundings: qr on
+    q, kvr on K^ and V^, pr on the weights 2^15 e^(s - m) (l summed from the
+    rounded weights, as the kernels do)."""
+    qq = q if qr is None else qr(q)
+    kk, vv = (k, v) if kvr is None else (kvr(k), kvr(v))
+    s = (qq @ kk.T) * scale
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m) * 2.0 ** 15
+    if pr is not None:
+        p = pr(p)
+    l = p.sum(axis=1, keepdims=True)
+    return (p @ vv) / l, (m + np.log(l / 2.0 ** 15))[:, 0]
+
+
+TERMS = {
+    "q to f16": dict(qr=f16),
+    "K^, V^ to f16": dict(kvr=f16),
+    "weights f16 toward zero": dict(pr=f16_toward_zero),
+    "weights f16 hi + lo": dict(pr=lambda x: f16_toward_zero(x) + f16_toward_zero(x - f16_toward_zero(x))),
+}
+
+
+@pytest.mark.parametrize("kind,g,d,n", [(O.F16, 4, 128, 13100), (O.Q8_B32, 6, 256, 20000), (O.Q4_B32, 6, 256, 20000)])
+def test_error_budget_by_term(kind, g, d, n):
+    r = synth.rng(9000 + kind)
+    q = synth.gen_q(r, 1, g, d)[0].astype(np.float64)
+    kc, ks = synth.gen_cache(r, kind, n, 1, d)
+    vc, vs = synth.gen_cache(r, kind, n, 1, d)
+    k = O.dequantize(kind, kc[:, 0], None if ks is None else ks[:, 0])
+    v = O.dequantize(kind, vc[:, 0], None if vs is None else vs[:, 0])
+    scale = 1 / np.sqrt(d)
+    o0, l0 = attend(q, k, v, scale)
+    # the model without any rounding is the oracle itself
+    wo, wl = O.decode_attention(q[None].astype(np.float32), [((kind, kc, ks), (kind, vc, vs), [np.arange(n)])], 1,
+                                scale)
+    assert np.abs(o0 - wo[0]).max() < 1e-12 and np.abs(l0 - wl[0]).max() < 1e-12
+    err = {}
+    for name, kw in TERMS.items():
+        o, l = attend(q, k, v, scale, **kw)
+        err[name] = (float(np.abs(o - o0).max()), float(np.abs(l - l0).max()))
+    print(f"\nkind {kind}, G {g}, D {d}, {n} cells:",
+          {k: (f"out {a:.1e}", f"lse {b:.1e}") for k, (a, b) in err.items()})
+    # out: every term is two orders of magnitude inside the 2e-3 bound
+    assert all(a < 5e-5 for a, _ in err.values()), err
+    # lse: toward-zero weights cost about 2^-11 of l (below 2^-10), the
+    # hi + lo pair about 2^-21; q and K^ / V^ far less
+    assert 1e-4 < err["weights f16 toward zero"][1] < 2.0 ** -10
+    assert err["weights f16 hi + lo"][1] < 1e-6
+    assert err["q to f16"][1] < 2e-4 and err["K^, V^ to f16"][1] < 1e-4
+    if kind == O.F16:
+        assert err["K^, V^ to f16"] == (0.0, 0.0)  # f16 values are staged exactly

@@ -253,3 +253,18 @@ def test_ring_reuse_waits_for_slow_readers(KF, depth):
         check(out, lse, res_out, res_lse, tol=TOL_SPLITS)
     # the delays did run: at least 0.1 ms per chunk kernel on top
     assert wall[1] - wall[0] > 18 * 1e-4, wall
+
+
+@pytest.mark.parametrize("hq,slots", [(5, 1), (5, 3), (7, 1)])
+def test_tail_odd_row_count(K, hq, slots):
+    """An odd number of rows in the running partial (5 or 7 query heads over
+    one KV head, one or three slots: 5, 15 or 7 rows), whose o part must
+    still sit 16-byte aligned after the (m, l) prefix."""
+    occ = [3000, 2100, 1200][:slots]
+    begins = [0, 3000, 5100][:slots]
+    c = Case(64 + hq + slots, hq, 1, 128, occupied=occ, begins=begins)
+    window = [(b + 1000, n - 1000) for b, n in zip(begins, occ)]
+    tail = [(b, 1000) for b in begins]
+    out, lse, p = run_tail(K, c, window, tail, chunk=256, depth=2)
+    assert p.info()["n_tail_chunks"] == 4 * slots
+    check(out, lse, *c.oracle())
