@@ -39,6 +39,7 @@ namespace kvdec {
 namespace {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f2v __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kNegInf = -__builtin_inff();
@@ -50,6 +51,11 @@ constexpr float kPOff = 15.0f;
 constexpr float kPOffInv = 1.0f / 32768.0f;
 
 __device__ __forceinline__ h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
+
+// Two floats -> an f16 pair, each rounded to nearest (one v_cvt_pk_f16_f32).
+// Softmax weights go through this: unbiased, so l summed from the rounded
+// weights carries no systematic error into lse.
+__device__ __forceinline__ h2 to_h2(float a, float b) { return __builtin_convertvector(f2v{a, b}, h2); }
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -826,7 +832,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
                 h2 pp[G];
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
-                    pp[h] = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p[A][h], p[B][h]));
+                    pp[h] = to_h2(p[A][h], p[B][h]);
                     l[h] = __builtin_amdgcn_fdot2(pp[h], ones, l[h], false);
                 }
 #pragma unroll
@@ -1216,7 +1222,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
             m_w[h] = pair_max<32>(pair_max<16>(mx));
         }
 
-        // 4. weights, rounded to f16 (toward zero); l from the rounded values;
+        // 4. weights, rounded to f16 (to nearest); l from the rounded values;
         // pairs of cells (8j + cl, 8j + cl + 1) to LDS from the even groups
 #pragma unroll
         for (int j = 0; j < JM; ++j) {
@@ -1225,7 +1231,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
             for (int h = 0; h < G; ++h) {
                 const float p = (sc[j][h] == kNegInf) ? 0.f : exp2_fast(sc[j][h] - m_w[h] + kPOff);
                 const float pn = dpp<0x128>(p);
-                const h2 pp = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p, pn));
+                const h2 pp = to_h2(p, pn);
                 l_w[h] += (float)pp.x;
                 pk[h] = __builtin_bit_cast(uint32_t, pp);
             }
@@ -1708,10 +1714,10 @@ __global__ __launch_bounds__(64 * W) void split_mfma_kernel(const SplitArgs a) {
         const float alpha = bump ? exp2_fast(m_h - mn) : 1.f;
         const bool rescale = bump && m_h != kNegInf;
         m_h = mn;
-        // Each weight as an f16 pair hi + lo: hi is p rounded toward zero,
+        // Each weight as an f16 pair hi + lo: hi is p rounded to nearest,
         // lo the residual p - hi (exact in f32) rounded again, so hi + lo
-        // carries p to about 2^-21 of itself.  A single f16 weight would
-        // re-weight the cells by up to 2^-10 of their weights -- on two cells
+        // carries p to about 2^-22 of itself.  A single f16 weight would
+        // re-weight two cells by up to 2^-11 of each weight -- on two cells
         // of near-equal score and values v1, v2 an error of up to
         // 2^-12 |v1 - v2| in the output.
         h8 pa, pl;
@@ -1720,8 +1726,8 @@ __global__ __launch_bounds__(64 * W) void split_mfma_kernel(const SplitArgs a) {
         for (int e = 0; e < 8; e += 2) {
             const float p0 = (sc[e] == kNegInf) ? 0.f : exp2_fast(sc[e] - mn + kMPOff);
             const float p1 = (sc[e + 1] == kNegInf) ? 0.f : exp2_fast(sc[e + 1] - mn + kMPOff);
-            const h2 pp = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p0, p1));
-            const h2 pr = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p0 - (float)pp.x, p1 - (float)pp.y));
+            const h2 pp = to_h2(p0, p1);
+            const h2 pr = to_h2(p0 - (float)pp.x, p1 - (float)pp.y);
             pa[e] = pp.x;
             pa[e + 1] = pp.y;
             pl[e] = pr.x;

@@ -12,9 +12,9 @@ from long_context_decode_kv_amd import synth
 
 TOL = 2e-3  # max |err| of out and lse against the float64 oracle
 # Two GPU results over different split partitions of the same cells: the f16
-# softmax weights are rounded (toward zero) against each stream's own
-# maximum, so the two are re-weighted differently by up to 2^-10 per weight;
-# lse then differs by up to ~1e-4 and out by less.  (Each result is also
+# softmax weights are rounded (to nearest) against each stream's own
+# maximum, so the two are re-weighted differently by up to 2^-11 per weight;
+# lse and out then differ by far less than this bound.  (Each result is also
 # held to TOL against the oracle.)
 TOL_SPLITS = 1e-3
 

@@ -163,8 +163,9 @@ def test_two_cell_slots_f16_near_ties(K, shape):
     """f16 K and V: two cells per slot whose K rows differ in one element by
     1 to 4000 f16 steps (score gaps of many sizes), V values of either sign
     with magnitude in [2, 4); V is exact in f16, so only the weights round
-    (by less than 2^-10 of themselves toward zero on the vector kernels:
-    at most 2^-12 |v1 - v2| < 2^-9 in the output)."""
+    (to nearest on the vector kernels, at most 2^-11 of the smaller weight
+    -- the larger one, the stream's maximum, is exact: at most
+    2^-13 |v1 - v2| < 2^-10 in the output)."""
     import torch
     hq, hkv, d, kern = shape
     r = synth.rng(7300 + d + len(kern))
