@@ -64,33 +64,50 @@ def measure_h2d(torch, nbytes=256 << 20, reps=5):
     return round(nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9, 2)
 
 
+# launch shapes of the read-ceiling sweep: (LDS DMA?, threads, loads in
+# flight per thread, workgroups or None for the LDS-DMA grid)
+CEILING_SHAPES = ([(0, t, u, w) for t, us in ((256, (4, 8, 16, 32)), (512, (4, 8, 16, 32)), (1024, (4, 8, 16)))
+                   for u in us for w in (256, 512, 1024, 2048, 4096)] +
+                  [(1, t, n, None) for t, n in ((256, 8), (256, 16), (256, 32), (512, 8), (512, 16), (1024, 4),
+                                                (1024, 8))])
+
+
 def measure_read_ceiling(torch, nbytes, launches):
     """Streaming-read ceiling for the same bytes per launch and launches per
-    step: `launches` back-to-back reads (kvprobe_read, 16-byte loads) of
-    distinct buffers of `nbytes` each, rotated over >= 1 GiB so the 256 MB
-    MALL cannot serve repeats; the best over a few launch shapes.  Returns
-    (GB/s, us per launch, shape)."""
+    step: `launches` back-to-back reads (kvprobe_read_shape, 16-byte loads)
+    of distinct buffers of `nbytes` each, rotated over >= 1 GiB so the 256 MB
+    MALL cannot serve repeats, over a sweep of launch shapes (register loads
+    with 256 to 1024 threads, 4 to 32 loads in flight, 256 to 4096
+    workgroups; LDS DMA of each thread's whole share at entry).  Returns
+    (GB/s, us per launch, shape) of the best, and a dict with the best of
+    each load method and the number of shapes tried."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "long_context_decode_kv_amd", "libkvprobe.so"))
-    f = lib.kvprobe_read
+    f = lib.kvprobe_read_shape
     f.restype = ctypes.c_int
-    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    g = lib.kvprobe_lds_workgroups
+    g.restype = ctypes.c_int64
+    g.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
     nb = -(-nbytes // 16) * 16
     copies = max(2, -(-(1 << 30) // nb))
     reps = max(2, -(-(20 << 30) // (nb * launches)))
     bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(copies)]
-    shapes = [(wgs, u) for wgs in (512, 1024, 2048) for u in (4, 8, 16)]
-    sink = torch.empty(max(w for w, _ in shapes) * 256, dtype=torch.int32, device="cuda")
+    grids = {sh: (sh[3] if not sh[0] else g(nb, sh[1], sh[2])) for sh in CEILING_SHAPES}
+    sink = torch.empty(max(grids[sh] * sh[1] for sh in CEILING_SHAPES), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    best = None
-    for wgs, u in shapes:
+    best, per_method = None, {}
+    for sh in CEILING_SHAPES:
+        lds, t, u, w = sh
+
         def run(n):
             k = 0
             for _ in range(n):
                 for _ in range(launches):
-                    rc = f(bufs[k % copies].data_ptr(), nb, wgs, u, sink.data_ptr(), stream.cuda_stream)
+                    rc = f(bufs[k % copies].data_ptr(), nb, w or 0, t, u, lds, sink.data_ptr(), stream.cuda_stream)
                     if rc != 0:
-                        raise RuntimeError(f"kvprobe_read failed: {rc}")
+                        raise RuntimeError(f"kvprobe_read_shape{sh} failed: {rc}")
                     k += 1
             return k
         run(1)
@@ -101,11 +118,17 @@ def measure_read_ceiling(torch, nbytes, launches):
         e.record(stream)
         torch.cuda.synchronize()
         us = a.elapsed_time(e) * 1e3 / k
+        desc = (f"{grids[sh]} workgroups x {t} threads, " +
+                (f"{u} loads of 16 B in flight per thread" if not lds else f"{u} LDS-DMA loads of 16 B per thread at entry"))
+        rec = (round(nb / (us * 1e-6) / 1e9, 1), round(us, 3), desc)
+        m = "lds_dma" if lds else "register_loads"
+        if m not in per_method or us < per_method[m][1]:
+            per_method[m] = rec
         if best is None or us < best[1]:
-            best = (round(nb / (us * 1e-6) / 1e9, 1), round(us, 3), f"{wgs} workgroups x 256 threads, {u} loads "
-                                                                     f"of 16 B in flight per thread")
+            best = rec
     del bufs
-    return best
+    return best, {"shapes_tried": len(CEILING_SHAPES),
+                  "best_by_method": {m: {"gbs": r[0], "us_per_launch": r[1], "shape": r[2]} for m, r in per_method.items()}}
 
 
 def log(*a):
@@ -694,10 +717,11 @@ def main():
     traffic = committed_traffic(wl.name)
     ceiling = None
     if not args.no_read_ceiling:
-        c_gbs, c_us, c_shape = measure_read_ceiling(torch, bytes_launch, launches_per_step)
-        ceiling = {"method": "kvprobe_read: plain 16-byte streaming read of the same bytes per launch, same "
-                             "launches per step, best launch shape",
-                   "shape": c_shape, "gbs": c_gbs, "us_per_launch": c_us, "frac_of_ceiling": round(achieved / c_gbs, 4)}
+        (c_gbs, c_us, c_shape), c_sweep = measure_read_ceiling(torch, bytes_launch, launches_per_step)
+        ceiling = {"method": "kvprobe_read_shape: plain 16-byte streaming read of the same bytes per launch, same "
+                             "launches per step, best of a sweep of launch shapes",
+                   "shape": c_shape, "gbs": c_gbs, "us_per_launch": c_us, "frac_of_ceiling": round(achieved / c_gbs, 4),
+                   **c_sweep}
 
     cpu = None
     if not args.no_cpu_baseline:

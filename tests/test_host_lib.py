@@ -39,7 +39,7 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     import ctypes
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "kvprobe.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(kvprobe_\w+)\s*\(", text, flags=re.M)))
-    assert names == ["kvprobe_read"]
+    assert names == ["kvprobe_lds_workgroups", "kvprobe_read", "kvprobe_read_shape"]
     lib = ctypes.CDLL(os.path.join(ROOT, "long_context_decode_kv_amd", "libkvprobe.so"))
     f = lib.kvprobe_read
     f.restype = ctypes.c_int
@@ -51,6 +51,19 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert f(fake, 1024, 0, 4, fake, None) == -1          # no workgroups
     assert f(fake, 1024, 4, 3, fake, None) == -1          # unsupported unroll
     assert f(fake, 1024, 4, 4, None, None) == -1          # null sink
+    g = lib.kvprobe_read_shape
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    assert g(fake, 1024, 4, 256, 64, 0, fake, None) == -1     # no such register-load shape
+    assert g(fake, 1024, 4, 1024, 32, 0, fake, None) == -1    # nor this one
+    assert g(fake, 1024, 4, 256, 4, 1, fake, None) == -1      # no such LDS-DMA shape
+    assert g(fake, 1024, 0, 512, 8, 0, fake, None) == -1      # no workgroups
+    assert g(fake + 4, 1024, 4, 256, 8, 1, fake, None) == -1  # misaligned
+    h = lib.kvprobe_lds_workgroups
+    h.restype = ctypes.c_int64
+    h.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+    assert h(53690368, 256, 8) == -(-53690368 // (16 * 256 * 8)) and h(0, 256, 8) == -1
 
 
 def test_strerror_codes():
