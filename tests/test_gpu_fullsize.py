@@ -66,7 +66,8 @@ def test_qwen3_8b_layer_13100_of_16384(K):
 
 def test_qwen25_14b_1m_layer_524288(K):
     """One layer of the 48-layer long-context step: 40 q heads, 8 KV heads,
-    524288 cells (2 GiB of K+V); KV heads 0 and 7 checked against the oracle."""
+    524288 cells (2 GiB of K+V), the benchmark's launch; every KV head
+    checked against the oracle (one head's rows on the host at a time)."""
     import torch
     n = 524288
     k = synth.device_f16_cache(4000, n, 8, 128)
@@ -78,7 +79,7 @@ def test_qwen25_14b_1m_layer_524288(K):
     K.attend(p, q, k, v, K.workspace(p), out=out, lse=lse)
     torch.cuda.synchronize()
     got_o, got_l = out.cpu().numpy(), lse.cpu().numpy()
-    for g, (wo, wl) in oracle_heads(K, q, k, v, (0, 7), 5, 1 / math.sqrt(128)).items():
+    for g, (wo, wl) in oracle_heads(K, q, k, v, range(8), 5, 1 / math.sqrt(128)).items():
         check(got_o[:, g * 5:(g + 1) * 5], got_l[:, g * 5:(g + 1) * 5], wo, wl)
 
 
