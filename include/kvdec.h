@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_VERSION 10700 /* 1.7.0: kvdec_io.live_records */
+#define KVDEC_VERSION 10800 /* 1.8.0: one cache line per merge ticket, kvdec_plan_info.ticket_bytes */
 
 /* Status codes. */
 #define KVDEC_OK 0
@@ -84,9 +84,14 @@ extern "C" {
 
 /* kvdec_attend_static: the library's own per-device scratch array holds a
  * merge-ticket area of KVDEC_STATIC_TICKET_BYTES followed by a workspace of
- * KVDEC_STATIC_WORKSPACE_BYTES (16 MiB + 64 KiB of device memory per GPU the
+ * KVDEC_STATIC_WORKSPACE_BYTES (16 MiB + 1 MiB of device memory per GPU the
  * library runs on, held until the process ends). */
-#define KVDEC_STATIC_TICKET_BYTES (64 * 1024)
+#define KVDEC_STATIC_TICKET_BYTES (1024 * 1024)
+
+/* The merge-ticket area at the start of every plan's workspace: this size
+ * for plans with up to KVDEC_TICKET_AREA_BYTES / 128 merge tickets, a
+ * multiple of it beyond (kvdec_plan_info.ticket_bytes). */
+#define KVDEC_TICKET_AREA_BYTES (1024 * 1024)
 #define KVDEC_STATIC_WORKSPACE_BYTES (16 * 1024 * 1024)
 
 /*
@@ -293,8 +298,12 @@ typedef struct kvdec_partial {
  * units to fill; 0 queries the current HIP device.  On success *out receives
  * the plan and *workspace_bytes the size of the device workspace that
  * kvdec_attend needs with it (the tile/split partials, merge tickets and the
- * tail staging ring).  A workspace must be zero-filled once before its first
- * use; every completed call leaves its ticket words at zero again.
+ * tail staging ring).  A workspace's merge-ticket area (its first
+ * kvdec_plan_info.ticket_bytes) must be zero-filled once before its first
+ * use; every completed call leaves it at zero again, and nothing else in a
+ * workspace is read before the call writes it.  So plans with the same
+ * ticket_bytes (all plans with up to KVDEC_TICKET_AREA_BYTES / 128 merge
+ * tickets) can take turns on one workspace of the largest workspace_bytes.
  * Errors: KVDEC_E_INVALID, KVDEC_E_RANGE, KVDEC_E_UNSUPPORTED, KVDEC_E_NOMEM,
  * KVDEC_E_DEVICE (only when n_cu == 0 and the device query fails).
  */
@@ -354,6 +363,8 @@ typedef struct kvdec_plan_info {
     int32_t kernel;           /* KVDEC_KERNEL_STREAMED or _ONESHOT for the vector-ALU kernels, 0 on matrix cores */
     int32_t split_interleave; /* U > 0: split s of a (slot, KV head) holds the U-cell units s, s + n_splits,
                                  s + 2 n_splits, ... of its positions; 0: each split is a contiguous run */
+    int64_t ticket_bytes;     /* the merge-ticket area at the start of the workspace (one 128-byte line per
+                                 ticket); the rest of the workspace need not be zero */
 } kvdec_plan_info;
 
 int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info);

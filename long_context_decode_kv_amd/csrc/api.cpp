@@ -158,7 +158,7 @@ int attend_checked(const kvdec_plan_t& p, const kvdec_io* io, uint8_t* ws, uint3
     a.part_l = reinterpret_cast<float*>(ws + p.off_parts_l);
     a.part_o_bytes = (int64_t)p.parts_o_bytes;
     a.tickets = tickets ? tickets : reinterpret_cast<uint32_t*>(ws + p.off_tickets);
-    a.ctickets = a.tickets + (size_t)p.n_slots * p.n_kv_heads;
+    a.ctickets = a.tickets + (size_t)kvdec::kTicketStride * p.n_slots * p.n_kv_heads;
     a.crec_base = p.crec_base;
     a.n_slots = p.n_slots;
     a.slot_base = 0;
@@ -441,6 +441,7 @@ int kvdec_plan_get_info(const kvdec_plan_t* plan, kvdec_plan_info* info) {
     info->waves = plan->waves;
     info->kernel = plan->mfma ? 0 : (plan->oneshot > 0 ? KVDEC_KERNEL_ONESHOT : KVDEC_KERNEL_STREAMED);
     info->split_interleave = plan->interleave ? plan->split_unit : 0;
+    info->ticket_bytes = (int64_t)plan->ticket_bytes;
     return KVDEC_OK;
 }
 
@@ -499,10 +500,11 @@ int kvdec_attend_static(const kvdec_plan_t* plan, const kvdec_io* io, void* stre
         return fail(KVDEC_E_WORKSPACE, "the plan's workspace needs " + std::to_string(p.workspace_bytes) +
                                            " bytes, the static scratch holds " +
                                            std::to_string((size_t)KVDEC_STATIC_WORKSPACE_BYTES));
-    const int64_t words = (int64_t)p.n_slots * p.n_kv_heads + p.n_cluster_capacity;
-    if (words * 4 > (int64_t)KVDEC_STATIC_TICKET_BYTES)
-        return fail(KVDEC_E_WORKSPACE, "the plan needs " + std::to_string(words) + " merge tickets, the static scratch holds " +
-                                           std::to_string(KVDEC_STATIC_TICKET_BYTES / 4));
+    const int64_t n_tickets = (int64_t)p.n_slots * p.n_kv_heads + p.n_cluster_capacity;
+    if ((int64_t)p.ticket_bytes > (int64_t)KVDEC_STATIC_TICKET_BYTES)
+        return fail(KVDEC_E_WORKSPACE, "the plan needs " + std::to_string(n_tickets) +
+                                           " merge tickets, the static scratch holds " +
+                                           std::to_string(KVDEC_STATIC_TICKET_BYTES / (4 * kvdec::kTicketStride)));
     if (p.has_tail && !p.tail_zero_copy)
         return fail(KVDEC_E_UNSUPPORTED, "a copied tail needs per-call events; use tail_zero_copy or kvdec_attend");
     const int rc = check_io(p, io);

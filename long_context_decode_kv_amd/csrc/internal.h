@@ -19,6 +19,10 @@ constexpr int64_t kMaxCells = int64_t(1) << 48;  // bound of capacity_cells and 
 constexpr int kBlock = 32;               // elements sharing one f16 scale
 constexpr int kThreads = 256;            // threads per split workgroup (4 waves)
 constexpr int kSplitUnit = 32;           // split boundary granularity of the vector-ALU kernel
+// Merge tickets sit one per 128-byte line: device-scope atomics on one line
+// are performed one after another, and the splits of every KV head arrive
+// at about the same time.
+constexpr int kTicketStride = 32;        // uint32 words from one ticket to the next
 constexpr int kMergeMaxParts = 64;       // kvdec_merge fan-in
 
 // Bytes of one stored (cell, KV head) row of codes.
@@ -110,8 +114,8 @@ struct SplitArgs {
     float* part_m;           //   running max in log2 units [record][G]
     float* part_l;           //   sum [record][G]
     int64_t part_o_bytes;    // bytes of the o region (bound of its buffer resource)
-    uint32_t* tickets;       // one per (slot, KV head)
-    uint32_t* ctickets;      // one per cluster of splits
+    uint32_t* tickets;       // one per (slot, KV head), kTicketStride words apart
+    uint32_t* ctickets;      // one per cluster of splits, kTicketStride words apart
     int32_t crec_base;       // record index of cluster 0's record
     int32_t waves;           // waves per workgroup of either kernel: 4 or 8
     float* out;              // [slots][Hq][D] or null
@@ -238,6 +242,7 @@ struct kvdec_plan {
     // Workspace layout (byte offsets, 256-aligned).
     // acc0 / acc1: running partials (ping-pong) of the window + tail chain.
     size_t off_tickets = 0, off_parts = 0, off_acc0 = 0, off_acc1 = 0, off_ring = 0;
+    size_t ticket_bytes = 0;  // the merge-ticket area at the start of the workspace
     int32_t n_part_capacity = 0;     // partial records the parts region holds
     int32_t crec_base = 0;           // record index of the first cluster record
     int32_t n_cluster_capacity = 0;  // cluster tickets / records reserved

@@ -437,7 +437,12 @@ int build_plan(const kvdec_problem& p, int32_t n_cu, kvdec_plan_t& plan, std::st
     const size_t D = (size_t)p.head_dim;
     size_t off = 0;
     plan.off_tickets = off;
-    off = align_up(off + sizeof(uint32_t) * ((size_t)p.n_slots * p.n_kv_heads + (size_t)clusters), 256);
+    // a fixed-size ticket area (a multiple of it for very many tickets), so
+    // that plans can take turns on one workspace: every call leaves the area
+    // zero, and no plan writes records where another keeps its tickets
+    const size_t ticket_need = sizeof(uint32_t) * kTicketStride * ((size_t)p.n_slots * p.n_kv_heads + (size_t)clusters);
+    plan.ticket_bytes = align_up(std::max<size_t>(ticket_need, 1), KVDEC_TICKET_AREA_BYTES);
+    off += plan.ticket_bytes;
     plan.off_parts = off;
     plan.parts_o_bytes = sizeof(float) * (size_t)part_capacity * rec_rows * D;
     if (plan.parts_o_bytes >= (1ull << 31)) {

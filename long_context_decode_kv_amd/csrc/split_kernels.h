@@ -107,6 +107,54 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Rows of a G-row group padded to a power of two for scatter_sum8.
+template <int G>
+constexpr int scatter_rows() {
+    return G <= 1 ? 1 : (G <= 2 ? 2 : (G <= 4 ? 4 : 8));
+}
+
+// The row whose full sum lane `sub` (0..7) of an 8-lane group receives from
+// scatter_sum8<GS>.
+template <int GS>
+__device__ __forceinline__ int scatter_row(int sub) {
+    return (GS >= 2 ? ((sub >> 2) & 1) * (GS / 2) : 0) + (GS >= 4 ? ((sub >> 1) & 1) * (GS / 4) : 0) +
+           (GS >= 8 ? (sub & 1) : 0);
+}
+
+// One step of scatter_sum8 over N rows with the partner lane CTRL selects:
+// with N > 1 the lane keeps the upper half of its rows when `up` is set (its
+// partner's `up` is the opposite), the lower half otherwise, and adds the
+// partner's copy of that half; with N = 1 it adds the partner's value.
+template <int N, int CTRL>
+__device__ __forceinline__ void scatter_step(float* x, bool up) {
+    if constexpr (N == 1) {
+        x[0] += dpp<CTRL>(x[0]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) {
+            const float keep = up ? x[i + N / 2] : x[i];
+            const float send = up ? x[i] : x[i + N / 2];
+            x[i] = keep + dpp<CTRL>(send);
+        }
+    }
+}
+
+// Reduce-scatter over each group of 8 consecutive lanes: every lane brings
+// GS partial sums, one per row, and receives the group's full sum of row
+// scatter_row<GS>(sub).  Partners: 7 - sub (row_half_mirror), then sub ^ 2
+// and sub ^ 1 (quad_perm); 3 (GS - 1) + 3 - log2(GS) instructions where GS
+// all-reduces take 3 GS, and whatever follows handles one value per lane.
+template <int GS>
+__device__ __forceinline__ float scatter_sum8(const float (&v)[GS], int sub) {
+    float x[GS];
+#pragma unroll
+    for (int i = 0; i < GS; ++i) x[i] = v[i];
+    scatter_step<GS, 0x141>(x, (sub & 4) != 0);
+    scatter_step<(GS > 1 ? GS / 2 : 1), 0x4E>(x, (sub & 2) != 0);
+    scatter_step<(GS > 2 ? GS / 4 : 1), 0xB1>(x, (sub & 1) != 0);
+    return x[0];
+}
+
 // Max / sum over the whole wave; every lane receives the result.
 __device__ __forceinline__ float wave_max(float x) {
     x = fmaxf(x, dpp<0xB1>(x));
@@ -601,7 +649,7 @@ __device__ __forceinline__ void arrive_and_merge(const SplitArgs& a, const SlotA
     // Records are published (stores complete) before the arrival is counted.
     wait_stores();
     __syncthreads();
-    uint32_t* gticket = a.tickets + (int64_t)(a.slot_base + s) * a.n_kv_heads + g;
+    uint32_t* gticket = a.tickets + kTicketStride * ((int64_t)(a.slot_base + s) * a.n_kv_heads + g);
     const int64_t srec0 = sa.part_begin + (int64_t)g * sa.n_splits;
     if (ncl <= 1) {
         // the last workgroup of the (slot, KV head) merges every split
@@ -617,7 +665,7 @@ __device__ __forceinline__ void arrive_and_merge(const SplitArgs& a, const SlotA
     const int c0 = cid * CH;
     const int cn = (n_splits - c0) < CH ? (n_splits - c0) : CH;
     const int64_t cidx = sa.cl_begin + (int64_t)g * sa.n_clusters + cid;
-    if (!last_arrival(a.ctickets + cidx, cn, sm_last)) return;
+    if (!last_arrival(a.ctickets + kTicketStride * cidx, cn, sm_last)) return;
     merge_records<D, G, NT>(a, sa, rm, srec0 + c0, cn, a.crec_base + cidx, chunk);
     wait_stores();
     __syncthreads();
@@ -1101,8 +1149,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int g = local - split * a.n_kv_heads;
     // The split's positions: a contiguous run, or (interleaved) the split
     // units split, split + n_splits, ...; position p of the split is slot
-    // position pos(p).
-    const int U = a.split_unit;
+    // position pos(p).  The unit is the vector-ALU kernels' (the dispatch
+    // checks), a constant, so the positions take shifts, not divisions.
+    constexpr int U = kSplitUnit;
     int64_t pos_begin = 0;
     int n = 0;
     if (a.interleave) {
@@ -1131,13 +1180,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int64_t row0 = (int64_t)(a.slot_base + s) * a.n_q_heads + hq0;
     unsigned char* vt = v_lds + wave * CW * VSTR;
 
-    float m_w[G], l_w[G], o[G][2];
+    // Softmax state of one row per lane: the scores' reduce-scatter leaves
+    // lane sub of each cell the row my_row of GS rows (the G real ones padded
+    // to a power of two); lanes of a cell whose sub differs only in the kDup
+    // bits hold the same row.
+    constexpr int GS = scatter_rows<G>();
+    constexpr int kDup = GS == 8 ? 0 : (GS == 4 ? 1 : (GS == 2 ? 3 : 7));
+    const int my_row = scatter_row<GS>(sub);
+    float m_r = kNegInf, l_r = 0.f, o[G][2];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m_w[h] = kNegInf;
-        l_w[h] = 0.f;
-        o[h][0] = o[h][1] = 0.f;
-    }
+    for (int h = 0; h < G; ++h) o[h][0] = o[h][1] = 0.f;
 
     if (cnt > 0) {
         // cell of the wave's row r; rows past the wave's cells read its first cell instead
@@ -1191,13 +1243,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
                 qh[h][c * 4 + 3] = as_h2(x.w);
             }
 
-        // 3. scores (log2 units) of the lane's cells, and the wave maximum
-        float sc[JM][G];
+        // 3. scores (log2 units) of the lane's cells: the 8 lanes of a cell
+        // hold partial dot products of the G rows, reduce-scattered so that
+        // each lane gets the score of row my_row; then that row's maximum
+        // over the wave's cells
+        float sc[JM];
 #pragma unroll
         for (int j = 0; j < JM; ++j) {
-            float acc[G];
+            float acc[GS];
 #pragma unroll
-            for (int h = 0; h < G; ++h) acc[h] = 0.f;
+            for (int h = 0; h < GS; ++h) acc[h] = 0.f;
 #pragma unroll
             for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -1206,46 +1261,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
                     for (int h = 0; h < G; ++h) acc[h] = __builtin_amdgcn_fdot2(kp, qh[h][c * 4 + i], acc[h], false);
                 }
-            const bool live = j * CPL + cl < cnt;
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float full = group_sum<R>(acc[h]);
-                sc[j][h] = live ? full * a.scale_log2 : kNegInf;
-            }
+            const float full = scatter_sum8<GS>(acc, sub);
+            const bool live = j * CPL + cl < cnt && my_row < G;
+            sc[j] = live ? full * a.scale_log2 : kNegInf;
         }
+        {
+            float mx = sc[0];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float mx = sc[0][h];
-#pragma unroll
-            for (int j = 1; j < JM; ++j) mx = fmaxf(mx, sc[j][h]);
+            for (int j = 1; j < JM; ++j) mx = fmaxf(mx, sc[j]);
             mx = fmaxf(mx, dpp<0x128>(mx));  // lane ^ 8: the other cell group of the row
-            m_w[h] = pair_max<32>(pair_max<16>(mx));
+            m_r = pair_max<32>(pair_max<16>(mx));
         }
 
         // 4. weights, rounded to f16 (to nearest); l from the rounded values;
-        // pairs of cells (8j + cl, 8j + cl + 1) to LDS from the even groups
+        // pairs of cells (8j + cl, 8j + cl + 1) to LDS from the even groups,
+        // one lane per row
+        const bool writer = (cl & 1) == 0 && (sub & kDup) == 0 && my_row < G;
 #pragma unroll
         for (int j = 0; j < JM; ++j) {
-            uint32_t pk[G];
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float p = (sc[j][h] == kNegInf) ? 0.f : exp2_fast(sc[j][h] - m_w[h] + kPOff);
-                const float pn = dpp<0x128>(p);
-                const h2 pp = to_h2(p, pn);
-                l_w[h] += (float)pp.x;
-                pk[h] = __builtin_bit_cast(uint32_t, pp);
-            }
-            if ((cl & 1) == 0 && sub == 0) {
-                uint32_t* dst = &p_lds[wave][j * (CPL / 2) + cl / 2][0];
-#pragma unroll
-                for (int h = 0; h < G; ++h) dst[h] = pk[h];
-            }
+            const float p = (sc[j] == kNegInf) ? 0.f : exp2_fast(sc[j] - m_r + kPOff);
+            const float pn = dpp<0x128>(p);
+            const h2 pp = to_h2(p, pn);
+            l_r += (float)pp.x;
+            if (writer) p_lds[wave][j * (CPL / 2) + cl / 2][my_row] = __builtin_bit_cast(uint32_t, pp);
         }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float x = l_w[h];
+        {
+            float x = l_r;
             x += dpp<0x128>(x);
-            l_w[h] = pair_sum<32>(pair_sum<16>(x));
+            l_r = pair_sum<32>(pair_sum<16>(x));
         }
 
         // 5. per wave load j: its 8 V rows -> LDS, then P.V over them (lane
@@ -1291,12 +1334,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     // 6. merge the wave streams: thread t -> column t of the group's rows
     __syncthreads();  // every wave is done with its V tile
     float (*mg_o)[G][D] = reinterpret_cast<float (*)[G][D]>(v_lds);
-    if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            mg_m[wave][h] = m_w[h];
-            mg_l[wave][h] = l_w[h] * kPOffInv;
-        }
+    if (lane < R && (lane & kDup) == 0 && my_row < G) {  // cell group 0: one lane per row
+        mg_m[wave][my_row] = m_r;
+        mg_l[wave][my_row] = l_r * kPOffInv;
     }
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -1838,6 +1878,7 @@ int launch_valu(const SplitArgs& a, void* stream) {
     // one-shot splits: head_dim 128, f16 K and V, up to 5 query rows
     if constexpr (D == 128 && G <= 5 && KT == KVDEC_F16 && VT == KVDEC_F16) {
         if (a.oneshot > 0 && !a.plan) {
+            if (a.split_unit != kSplitUnit) return (int)hipErrorInvalidValue;  // the kernel's unit is a constant
             const hipStream_t st = (hipStream_t)stream;
             if (a.oneshot <= 2)
                 hipLaunchKernelGGL((split_oneshot_kernel<G, 2>), dim3(a.n_workgroups), dim3(512), 0, st, a);

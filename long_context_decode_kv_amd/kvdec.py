@@ -83,7 +83,7 @@ class PlanInfo(ctypes.Structure):
         ("n_slots", _i32), ("group", _i32), ("n_workgroups", _i32), ("tiles_per_split", _i32),
         ("n_tiles", _i64), ("n_entries", _i64), ("n_tail_chunks", _i64), ("workspace_bytes", _i64),
         ("n_queries", _i32), ("matrix_cores", _i32), ("split_cells", _i32), ("split_unit", _i32),
-        ("waves", _i32), ("kernel", _i32), ("split_interleave", _i32),
+        ("waves", _i32), ("kernel", _i32), ("split_interleave", _i32), ("ticket_bytes", _i64),
     ]
 
 
@@ -118,8 +118,10 @@ EXPORTED = [
     "kvdec_source_hash", "kvdec_attend_static",
 ]
 
+# merge-ticket area at the start of a workspace (one 128-byte line per ticket)
+TICKET_AREA_BYTES = 1024 * 1024
 # capacity of the library's static scratch array (kvdec_attend_static)
-STATIC_TICKET_BYTES = 64 * 1024
+STATIC_TICKET_BYTES = 1024 * 1024
 STATIC_WORKSPACE_BYTES = 16 * 1024 * 1024
 
 

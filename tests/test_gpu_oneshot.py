@@ -152,8 +152,9 @@ def test_nan_poisoned_workspace_and_unattended_cells(K):
     p = c.plan(K, n_cu=256)
     assert p.info()["kernel"] == K.KERNEL_ONESHOT
     ws = K.workspace(p)
-    ws.view(torch.float32)[64:] = float("nan")  # tickets (the first bytes) stay zero
-    assert 64 * 4 >= 4 * c.n_slots * c.hkv
+    tb = p.info()["ticket_bytes"]  # the merge tickets stay zero, the rest is poisoned
+    assert tb >= 128 * c.n_slots * c.hkv
+    ws[tb:].view(torch.float32).fill_(float("nan"))
     check(*c.run(K, plan=p, ws=ws), *c.oracle())
 
 

@@ -278,8 +278,9 @@ def test_nan_poisoned_workspace_and_unused_cells(K):
     c.vc[~attended] = nan16
     p = c.plan(K, tiles_per_split=1)
     ws = K.workspace(p)
-    ws.view(torch.float32)[64:] = float("nan")  # tickets (first bytes) stay zero
-    assert 64 * 4 >= 4 * c.n_slots * c.hkv
+    tb = p.info()["ticket_bytes"]  # the merge tickets stay zero, the rest is poisoned
+    assert tb >= 128 * c.n_slots * c.hkv
+    ws[tb:].view(torch.float32).fill_(float("nan"))
     out, lse = c.run(K, plan=p, ws=ws)
     check(out, lse, *c.oracle())
 
@@ -295,7 +296,7 @@ def test_workspace_reuse_across_plans(K):
     for _ in range(2):
         check(*c1.run(K, plan=p1, ws=ws), *c1.oracle())
         check(*c2.run(K, plan=p2, ws=ws), *c2.oracle())
-    tick = ws[:4 * 2 * 8].view(torch.int32)
+    tick = ws[:max(p1.info()["ticket_bytes"], p2.info()["ticket_bytes"])].view(torch.int32)
     assert int(tick.abs().sum()) == 0
 
 

@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
     for name in names:
         assert hasattr(K.lib, name), name
     assert set(names) == set(K.EXPORTED)
-    assert K.version() == 10700
+    assert K.version() == 10800
 
 
 def test_probe_library_exports_and_rejects_bad_arguments():
@@ -364,12 +364,33 @@ def test_attend_validation_before_device_work():
                                     live_records=FAKE + 2, stream=0)) == K.E_INVALID     # misaligned live_records
 
 
+def test_ticket_area_fixed_size():
+    """Every plan's workspace starts with a merge-ticket area of one 128-byte
+    line per ticket, rounded up to KVDEC_TICKET_AREA_BYTES, so plans of up
+    to 8192 tickets share one layout of it and can take turns on a workspace."""
+    hdr = open(os.path.join(ROOT, "include", "kvdec.h")).read()
+    assert "#define KVDEC_TICKET_AREA_BYTES (1024 * 1024)" in hdr and K.TICKET_AREA_BYTES == 1024 * 1024
+    plans = [K.plan(32, 8, 128, 1, 16384, n_occupied=[13100], n_cu=256),
+             K.plan(32, 8, 128, 2, 16384, n_occupied=[300, 9000], cell_begin=[0, 4096], n_cu=256),
+             K.plan(32, 8, 128, 64, 64 * 4096, n_occupied=[4096] * 64, cell_begin=[4096 * s for s in range(64)],
+                    n_cu=256),
+             K.plan(24, 4, 256, 4, 1 << 18, n_occupied=[131072, 65536, 20000, 777],
+                    cell_begin=[0, 131072, 196608, 217088], k_type=K.Q8_B32, v_type=K.Q8_B32, n_cu=256)]
+    for p in plans:
+        info = p.info()
+        assert info["ticket_bytes"] == K.TICKET_AREA_BYTES
+        assert p.workspace_bytes > info["ticket_bytes"]
+    # 16 slots x 2048 KV heads: 32768 tickets of 128 bytes, exactly 4 areas
+    many = K.plan(2048, 2048, 64, 16, 64, n_occupied=[1] * 16, cell_begin=list(range(16)), n_cu=256)
+    assert many.info()["ticket_bytes"] == 4 * K.TICKET_AREA_BYTES
+
+
 def test_attend_static_validation_before_device_work():
     """kvdec_attend_static refuses, before it touches a device, a plan whose
     workspace or merge tickets do not fit the static scratch, a copied tail,
     and bad io; the limits are the header's."""
     hdr = open(os.path.join(ROOT, "include", "kvdec.h")).read()
-    assert "#define KVDEC_STATIC_TICKET_BYTES (64 * 1024)" in hdr and K.STATIC_TICKET_BYTES == 64 * 1024
+    assert "#define KVDEC_STATIC_TICKET_BYTES (1024 * 1024)" in hdr and K.STATIC_TICKET_BYTES == 1024 * 1024
     assert "#define KVDEC_STATIC_WORKSPACE_BYTES (16 * 1024 * 1024)" in hdr
     assert K.STATIC_WORKSPACE_BYTES == 16 * 1024 * 1024
     args = dict(out=FAKE, stream=0)
