@@ -438,16 +438,22 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMa
     }
     for (int sp0 = 0; sp0 < n_splits; sp0 += SPC) {
         const int nsp = (n_splits - sp0) < SPC ? (n_splits - sp0) : SPC;
+        // Round u of loads runs when some thread has a record in it (a
+        // test uniform over the workgroup); a thread past the chunk's last
+        // record reads that record again, which then gets weight 0.
+        // (every thread has a column when NT is a multiple of NV or NV of NT)
+        constexpr bool kAllCols = NV <= NT ? NT % NV == 0 : NV % NT == 0;
         float4 x[COLS][UB];
 #pragma unroll
         for (int c = 0; c < COLS; ++c) {
             const int v = col + c * NT;
 #pragma unroll
             for (int u = 0; u < UB; ++u) {
-                const int sp = cls + u * TS;
-                x[c][u] = (cls < TS && v < NV && sp < nsp)
-                              ? ld_dev4(rs, ((rec0 + sp0 + sp) * (G * D) + 4 * v) * 4)
-                              : make_float4(0.f, 0.f, 0.f, 0.f);
+                x[c][u] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (u * TS < nsp && (kAllCols || (cls < TS && v < NV))) {
+                    const int sp = cls + u * TS < nsp ? cls + u * TS : nsp - 1;
+                    x[c][u] = ld_dev4(rs, ((rec0 + sp0 + sp) * (G * D) + 4 * v) * 4);
+                }
             }
         }
         // (m, l) of the chunk: wave w takes record rows w, w + NW, w + 2 NW,
