@@ -35,6 +35,10 @@ FI_SOURCES = ["fault_injection.hip"]
 # with the ordinary device objects; loaded with the ASan runtime preloaded
 SAN_LIB = os.path.join(PKG, "libkvdec_san.so")
 SAN_HOST = ["plan.cpp", "api.cpp"]
+# diagnostic build: every source compiled with KVDEC_PHASE_TRACE -- the
+# one-shot kernel and its merge write clock stamps of their phases to a
+# buffer given through kvdec_trace_configure (long_context_decode_kv_amd.phase_trace)
+TRACE_LIB = os.path.join(PKG, "libkvdec_trace.so")
 SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer",
              "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
              "-Xarch_host", "-fno-sanitize-recover=undefined"]
@@ -121,7 +125,8 @@ def build(verbose=False, extra=()):
     jobs = [(s, list(extra) + hash_def, "") for s in SOURCES + PROBE_SOURCES + FI_SOURCES]
     jobs.append(("api.cpp", list(extra) + hash_def + ["-DKVDEC_FAULT_INJECTION"], "_fi"))
     jobs += [(h, list(extra) + hash_def + SAN_FLAGS, "_san") for h in SAN_HOST]
-    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+    jobs += [(s, list(extra) + hash_def + ["-DKVDEC_PHASE_TRACE"], "_tr") for s in SOURCES]
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 8)) as ex:
         outs = list(ex.map(lambda j: _compile(*j), jobs))
     results = {j[0] + j[2]: o for j, o in zip(jobs, outs)}
     if verbose:
@@ -131,8 +136,9 @@ def build(verbose=False, extra=()):
     fi_names = [n for n in SOURCES if n != "api.cpp"] + ["api.cpp_fi"] + FI_SOURCES
     san_names = [n for n in SOURCES if n not in SAN_HOST] + [h + "_san" for h in SAN_HOST]
     san_link = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libasan"]
+    tr_names = [n + "_tr" for n in SOURCES]
     for lib, names, link in ((LIB, SOURCES, []), (PROBE_LIB, PROBE_SOURCES, []), (FI_LIB, fi_names, []),
-                             (SAN_LIB, san_names, san_link)):
+                             (SAN_LIB, san_names, san_link), (TRACE_LIB, tr_names, [])):
         tmp = lib + ".tmp"
         cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + link + ["-o", tmp] + [results[n][0] for n in names]
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -164,7 +170,8 @@ def built_hash():
 def ensure_built():
     """Build when the libraries are missing or were built from other
     sources than the current ones (the recorded source hash differs)."""
-    if not all(os.path.exists(x) for x in (LIB, PROBE_LIB, FI_LIB, SAN_LIB)) or built_hash() != source_hash():
+    if not all(os.path.exists(x) for x in (LIB, PROBE_LIB, FI_LIB, SAN_LIB, TRACE_LIB)) or \
+            built_hash() != source_hash():
         build()
 
 

@@ -15,6 +15,11 @@ namespace {
 
 thread_local std::string g_last_error;
 
+#ifdef KVDEC_PHASE_TRACE
+// Diagnostic build: where the next launches write their phase stamps.
+unsigned long long* g_trace = nullptr;
+#endif
+
 int fail(int status, const std::string& msg) {
     g_last_error = msg;
     return status;
@@ -50,6 +55,9 @@ void common_args(const kvdec_plan_t& p, const kvdec_io& io, kvdec::SplitArgs& a)
     a.q_pos = p.n_q > 1 ? io.q_pos : nullptr;
     a.cell_pos = p.n_q > 1 ? io.cell_pos : nullptr;
     a.pos_offset = 0;
+#ifdef KVDEC_PHASE_TRACE
+    a.trace = g_trace;
+#endif
 }
 
 }  // namespace
@@ -585,5 +593,13 @@ int kvdec_merge(int32_t n_parts, const kvdec_partial* parts, int64_t n_rows, int
     if (e != hipSuccess) return device_fail((hipError_t)e, "merge kernel launch");
     return KVDEC_OK;
 }
+
+#ifdef KVDEC_PHASE_TRACE
+// Diagnostic build only (libkvdec_trace.so): launches enqueued from now on
+// write phase stamps to `buffer` (device memory, 32 uint64 per workgroup of
+// the launch, workgroup b at 32 b), or stop when it is null.  Process-wide;
+// a captured graph keeps the pointer it was captured with.
+void kvdec_trace_configure(void* buffer) { g_trace = static_cast<unsigned long long*>(buffer); }
+#endif
 
 }  // extern "C"

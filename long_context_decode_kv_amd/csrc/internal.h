@@ -141,6 +141,9 @@ struct SplitArgs {
     int32_t n_kv_heads;
     int32_t n_workgroups;
     SlotArg slot[KVDEC_MAX_SLOTS];
+#ifdef KVDEC_PHASE_TRACE
+    unsigned long long* trace;  // diagnostic build: 32 clock stamps per workgroup (see split_kernels.h), or null
+#endif
 };
 
 struct MergeArgs {

@@ -38,6 +38,35 @@
 namespace kvdec {
 namespace {
 
+// Phase trace of the one-shot kernel and its merge (diagnostic build only,
+// KVDEC_PHASE_TRACE; compiled out otherwise).  Each workgroup owns 32 slots
+// of the buffer and writes the constant 100 MHz clock (s_memrealtime) into
+// them: 0 entry, 1 loads issued, 2 query converted, 3 scores and maximum,
+// 4 weights, 5 + w wave w's P.V done, 13 streams merged, 14 record stores
+// issued, 15 record stores acknowledged, 16 ticket returned, 17 merge done
+// (merging workgroup only, after its output stores), 18 (m, l) loads
+// issued, 19 (m, l) reduced, 20 records accumulated, 21 columns combined,
+// 22 + w wave w's last V data landed, 30 merge entered, 31 record loads
+// issued.  Slots 0-4 and 13-21, 30, 31 are written by thread 0.
+#ifdef KVDEC_PHASE_TRACE
+#define KVDEC_TRACE(k)                                                                                        \
+    do {                                                                                                      \
+        if (a.trace && threadIdx.x == 0) a.trace[(size_t)blockIdx.x * 32 + (k)] = __builtin_amdgcn_s_memrealtime(); \
+    } while (0)
+#define KVDEC_TRACE_WAVE(k)                                                                                   \
+    do {                                                                                                      \
+        if (a.trace && (threadIdx.x & 63) == 0)                                                              \
+            a.trace[(size_t)blockIdx.x * 32 + (k)] = __builtin_amdgcn_s_memrealtime();                       \
+    } while (0)
+#else
+#define KVDEC_TRACE(k) \
+    do {               \
+    } while (0)
+#define KVDEC_TRACE_WAVE(k) \
+    do {                    \
+    } while (0)
+#endif
+
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f2v __attribute__((ext_vector_type(2)));
 
@@ -428,6 +457,7 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMa
     const int cls = tid / (NV < NT ? NV : NT);  // threads with cls >= TS idle
     const __amdgpu_buffer_rsrc_t rs = part_rsrc(a);
     const int n_splits = count;
+    if constexpr (G <= 5 && NT == 512) if (dest < 0) KVDEC_TRACE(30);
 
     float4 acc[COLS];
 #pragma unroll
@@ -456,6 +486,7 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMa
                 }
             }
         }
+        if constexpr (G <= 5 && NT == 512) if (dest < 0 && sp0 == 0) KVDEC_TRACE(31);
         // (m, l) of the chunk: wave w takes record rows w, w + NW, w + 2 NW,
         // ..., one split per lane.
         constexpr int HW = (G + NW - 1) / NW;  // record rows per wave
@@ -470,6 +501,7 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMa
                 lv[hh] = ld_dev(a.part_l + (rec0 + sp0 + lane) * G + h);
             }
         }
+        if constexpr (G <= 5 && NT == 512) if (dest < 0 && sp0 == 0) KVDEC_TRACE(18);
         __syncthreads();  // the previous chunk is done with f_m / scale_old
 #pragma unroll
         for (int hh = 0; hh < HW; ++hh) {
@@ -488,6 +520,7 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMa
             }
         }
         __syncthreads();
+        if constexpr (G <= 5 && NT == 512) if (dest < 0 && sp0 == 0) KVDEC_TRACE(19);
 #pragma unroll
         for (int c = 0; c < COLS; ++c) {
             const int v = col + c * NT;
@@ -511,6 +544,7 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMa
             acc[c] = o;
         }
     }
+    if constexpr (G <= 5 && NT == 512) if (dest < 0) KVDEC_TRACE(20);
     // combine the TS residue classes of each column
     if constexpr (TS > 1) {
         red[tid] = acc[0];
@@ -527,6 +561,7 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMa
             acc[0] = o;
         }
     }
+    if constexpr (G <= 5 && NT == 512) if (dest < 0) KVDEC_TRACE(21);
     if (cls == 0) {
 #pragma unroll
         for (int c = 0; c < COLS; ++c) {
@@ -655,12 +690,19 @@ __device__ __forceinline__ void arrive_and_merge(const SplitArgs& a, const SlotA
     // Records are published (stores complete) before the arrival is counted.
     wait_stores();
     __syncthreads();
+    if constexpr (G <= 5) KVDEC_TRACE(15);
     uint32_t* gticket = a.tickets + kTicketStride * ((int64_t)(a.slot_base + s) * a.n_kv_heads + g);
     const int64_t srec0 = sa.part_begin + (int64_t)g * sa.n_splits;
     if (ncl <= 1) {
         // the last workgroup of the (slot, KV head) merges every split
-        if (!last_arrival(gticket, n_splits, sm_last)) return;
+        const bool last = last_arrival(gticket, n_splits, sm_last);
+        if constexpr (G <= 5) KVDEC_TRACE(16);
+        if (!last) return;
         merge_records<D, G, NT>(a, sa, rm, srec0, n_splits, -1, chunk);
+#ifdef KVDEC_PHASE_TRACE
+        wait_stores();
+        if constexpr (G <= 5) KVDEC_TRACE(17);
+#endif
         return;
     }
     // two levels: the last of each cluster of splits merges the cluster into
@@ -1140,6 +1182,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     __shared__ float mg_m[W][G], mg_l[W][G];
     __shared__ int sm_last;
 
+    KVDEC_TRACE(0);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1229,6 +1272,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
         }
         __builtin_amdgcn_sched_barrier(0);
 
+        KVDEC_TRACE(1);
         // 2. query rows -> f16 pairs in the wave's LDS copy, then this lane's
         // pairs: elements (c * 8 + sub) * 8 .. + 8 of each row
 #pragma unroll
@@ -1249,6 +1293,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
                 qh[h][c * 4 + 3] = as_h2(x.w);
             }
 
+        KVDEC_TRACE(2);
         // 3. scores (log2 units) of the lane's cells: the 8 lanes of a cell
         // hold partial dot products of the G rows, reduce-scattered so that
         // each lane gets the score of row my_row; then that row's maximum
@@ -1279,6 +1324,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
             m_r = pair_max<32>(pair_max<16>(mx));
         }
 
+        KVDEC_TRACE(3);
         // 4. weights, rounded to f16 (to nearest); l from the rounded values;
         // pairs of cells (8j + cl, 8j + cl + 1) to LDS from the even groups,
         // one lane per row
@@ -1297,6 +1343,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
             l_r = pair_sum<32>(pair_sum<16>(x));
         }
 
+        KVDEC_TRACE(4);
         // 5. per wave load j: its 8 V rows -> LDS, then P.V over them (lane
         // owns columns 2 lane, 2 lane + 1), the four row pairs at once (rows
         // past the wave's cells hold finite data of its first cell and carry
@@ -1304,6 +1351,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 #pragma unroll
         for (int j = 0; j < JM; ++j) {
             if (j * CPL >= cnt) break;  // uniform over the wave
+#ifdef KVDEC_PHASE_TRACE
+            if (j == (cnt - 1) / CPL) {  // the wave's last V rows: wait for them, then stamp
+                __builtin_amdgcn_s_waitcnt(0);
+                KVDEC_TRACE_WAVE(22 + wave);
+            }
+#endif
 #pragma unroll
             for (int c = 0; c < NC; ++c)
                 *reinterpret_cast<uint4*>(vt + (j * CPL + cl) * VSTR + (c * R + sub) * 16) =
@@ -1337,6 +1390,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
         }
     }
 
+    KVDEC_TRACE_WAVE(5 + wave);
     // 6. merge the wave streams: thread t -> column t of the group's rows
     __syncthreads();  // every wave is done with its V tile
     float (*mg_o)[G][D] = reinterpret_cast<float (*)[G][D]>(v_lds);
@@ -1349,6 +1403,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
         *reinterpret_cast<float2*>(&mg_o[wave][h][2 * lane]) = make_float2(o[h][0] * kPOffInv, o[h][1] * kPOffInv);
     __syncthreads();
 
+    KVDEC_TRACE(13);
     const RowMap rm{row0, G, a.n_q_heads, G};
     const bool single = sa.n_splits == 1;
     const int64_t rec = sa.part_begin + (int64_t)g * sa.n_splits + split;
@@ -1378,6 +1433,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
             }
         }
     }
+    KVDEC_TRACE(14);
     if (single) return;
     arrive_and_merge<D, G, 64 * W>(a, sa, s, g, split, rm, sm_last);
 }

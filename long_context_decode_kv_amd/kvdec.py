@@ -21,10 +21,11 @@ import torch  # noqa: F401
 from long_context_decode_kv_amd.build import source_hash as _source_hash
 
 # KVDEC_LIB_NAME selects a test build: libkvdec_fi.so (host-side failure
-# injection, kvdec_fi_configure) or libkvdec_san.so (planner and validation
+# injection, kvdec_fi_configure), libkvdec_trace.so (phase stamps of the
+# one-shot kernel, kvdec_trace_configure) or libkvdec_san.so (planner and validation
 # under ASan / UBSan); the product library otherwise
 _LIB_NAME = os.environ.get("KVDEC_LIB_NAME", "libkvdec.so")
-if _LIB_NAME not in ("libkvdec.so", "libkvdec_fi.so", "libkvdec_san.so"):
+if _LIB_NAME not in ("libkvdec.so", "libkvdec_fi.so", "libkvdec_trace.so", "libkvdec_san.so"):
     raise ImportError(f"KVDEC_LIB_NAME={_LIB_NAME}: not a build of this package")
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), _LIB_NAME)
 if not os.path.exists(_LIB_PATH):

@@ -539,6 +539,18 @@ def test_failure_injection_only_in_the_test_build():
     assert fi.kvdec_source_hash().decode() == K.LIB_SOURCE_HASH
 
 
+def test_phase_trace_only_in_the_diagnostic_build():
+    """libkvdec_trace.so (phase stamps of the one-shot kernel) is a separate
+    diagnostic library built from the same sources; the product library has
+    no trace switch."""
+    from long_context_decode_kv_amd import build
+    tr = ctypes.CDLL(build.TRACE_LIB)
+    assert hasattr(tr, "kvdec_trace_configure") and hasattr(tr, "kvdec_attend")
+    assert not hasattr(K.lib, "kvdec_trace_configure")
+    tr.kvdec_source_hash.restype = ctypes.c_char_p
+    assert tr.kvdec_source_hash().decode() == K.LIB_SOURCE_HASH
+
+
 def test_build_rejects_kernels_with_scratch():
     """The build parses the compiler's kernel-resource remarks and refuses
     any kernel that needs per-lane scratch memory."""
