@@ -8,6 +8,7 @@
 #include <new>
 #include <stdexcept>
 #include <string>
+#include <vector>
 
 #include "internal.h"
 
@@ -79,6 +80,37 @@ hipError_t tail_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
     if (kvdec::fi_fail_copy()) return hipErrorUnknown;
 #endif
     return hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, s);
+}
+
+// n events for the tail stream, kept per host thread and device and reused
+// from call to call rather than created and destroyed each time.  Reuse is
+// safe: a stream wait waits for the event's record that preceded it, and
+// every wait a call enqueues follows a record the same call made.  The
+// events live until the process ends.
+hipError_t tail_events(int n, hipEvent_t* out) {
+    struct Pool {
+        int device;
+        std::vector<hipEvent_t> ev;
+    };
+    thread_local std::vector<Pool> pools;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    Pool* pool = nullptr;
+    for (auto& pl : pools)
+        if (pl.device == dev) pool = &pl;
+    if (!pool) {
+        pools.push_back(Pool{dev, {}});
+        pool = &pools.back();
+    }
+    while ((int)pool->ev.size() < n) {
+        hipEvent_t ev = nullptr;
+        e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e != hipSuccess) return e;
+        pool->ev.push_back(ev);
+    }
+    for (int i = 0; i < n; ++i) out[i] = pool->ev[i];
+    return hipSuccess;
 }
 
 // Split-kernel launch for the plan (a test build can make one fail without
@@ -199,13 +231,6 @@ int attend_checked(const kvdec_plan_t& p, const kvdec_io* io, uint8_t* ws, uint3
     const bool zc = p.tail_zero_copy;
     const int depth = zc ? 0 : p.ring_depth;
     hipEvent_t ev_start = nullptr, ev_landed[16] = {}, ev_free[16] = {};
-    auto destroy = [&]() {
-        if (ev_start) (void)hipEventDestroy(ev_start);
-        for (int i = 0; i < depth; ++i) {
-            if (ev_landed[i]) (void)hipEventDestroy(ev_landed[i]);
-            if (ev_free[i]) (void)hipEventDestroy(ev_free[i]);
-        }
-    };
     const uint8_t* hk = static_cast<const uint8_t*>(io->k_tail);
     const uint8_t* hv = static_cast<const uint8_t*>(io->v_tail);
     const uint8_t* hks = static_cast<const uint8_t*>(io->k_tail_scales);
@@ -228,14 +253,13 @@ int attend_checked(const kvdec_plan_t& p, const kvdec_io* io, uint8_t* ws, uint3
         if (!mapped(hk) || !mapped(hv) || !mapped(hks) || !mapped(hvs))
             return fail(KVDEC_E_INVALID, "tail_zero_copy needs device-mapped pinned host tail arrays");
     } else {
-        e = hipEventCreateWithFlags(&ev_start, hipEventDisableTiming);
-        for (int i = 0; i < depth && e == hipSuccess; ++i) {
-            e = hipEventCreateWithFlags(&ev_landed[i], hipEventDisableTiming);
-            if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_free[i], hipEventDisableTiming);
-        }
-        if (e != hipSuccess) {
-            destroy();
-            return device_fail(e, "hipEventCreate");
+        hipEvent_t ev[1 + 2 * 16];
+        e = tail_events(1 + 2 * depth, ev);
+        if (e != hipSuccess) return device_fail(e, "hipEventCreate");
+        ev_start = ev[0];
+        for (int i = 0; i < depth; ++i) {
+            ev_landed[i] = ev[1 + i];
+            ev_free[i] = ev[1 + depth + i];
         }
         // Copies start only after the work that may still read the ring:
         // everything already on `stream` (an earlier call on this workspace),
@@ -246,16 +270,10 @@ int attend_checked(const kvdec_plan_t& p, const kvdec_io* io, uint8_t* ws, uint3
             e = hipEventRecord(ev_start, ks);
             if (e == hipSuccess && cs != ks) e = hipStreamWaitEvent(cs, ev_start, 0);
         }
-        if (e != hipSuccess) {
-            destroy();
-            return device_fail(e, "stream ordering");
-        }
+        if (e != hipSuccess) return device_fail(e, "stream ordering");
     }
     int le = launch(p, a, stream);
-    if (le != hipSuccess) {
-        destroy();
-        return device_fail((hipError_t)le, "window kernel launch");
-    }
+    if (le != hipSuccess) return device_fail((hipError_t)le, "window kernel launch");
 
     const int64_t krow_b = kvdec::row_bytes(p.k_type, D) * p.n_kv_heads;
     const int64_t vrow_b = kvdec::row_bytes(p.v_type, D) * p.n_kv_heads;
@@ -352,7 +370,6 @@ int attend_checked(const kvdec_plan_t& p, const kvdec_io* io, uint8_t* ws, uint3
             if (!zc) e = hipEventRecord(ev_free[r], ks);
         }
     }
-    destroy();
     if (e != hipSuccess) return device_fail(e, "tail streaming");
     return KVDEC_OK;
 }
