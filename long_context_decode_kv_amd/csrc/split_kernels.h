@@ -468,6 +468,24 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMa
     }
     for (int sp0 = 0; sp0 < n_splits; sp0 += SPC) {
         const int nsp = (n_splits - sp0) < SPC ? (n_splits - sp0) : SPC;
+        // (m, l) of the chunk first -- a kilobyte the maxima and weights wait
+        // for, which would otherwise queue behind the chunk's o loads in the
+        // compute unit's address path: wave w takes record rows w, w + NW,
+        // w + 2 NW, ..., one split per lane.
+        constexpr int HW = (G + NW - 1) / NW;  // record rows per wave
+        float mv[HW], lv[HW];
+#pragma unroll
+        for (int hh = 0; hh < HW; ++hh) {
+            const int h = wave + NW * hh;
+            mv[hh] = kNegInf;
+            lv[hh] = 0.f;
+            if (h < G && lane < nsp) {
+                mv[hh] = ld_dev(a.part_m + (rec0 + sp0 + lane) * G + h);
+                lv[hh] = ld_dev(a.part_l + (rec0 + sp0 + lane) * G + h);
+            }
+        }
+        if constexpr (G <= 5 && NT == 512) if (dest < 0 && sp0 == 0) KVDEC_TRACE(18);
+        __builtin_amdgcn_sched_barrier(0);  // issue them before the o loads
         // Round u of loads runs when some thread has a record in it (a
         // test uniform over the workgroup); a thread past the chunk's last
         // record reads that record again, which then gets weight 0.
@@ -487,21 +505,6 @@ __device__ void merge_records(const SplitArgs& a, const SlotArg& sa, const RowMa
             }
         }
         if constexpr (G <= 5 && NT == 512) if (dest < 0 && sp0 == 0) KVDEC_TRACE(31);
-        // (m, l) of the chunk: wave w takes record rows w, w + NW, w + 2 NW,
-        // ..., one split per lane.
-        constexpr int HW = (G + NW - 1) / NW;  // record rows per wave
-        float mv[HW], lv[HW];
-#pragma unroll
-        for (int hh = 0; hh < HW; ++hh) {
-            const int h = wave + NW * hh;
-            mv[hh] = kNegInf;
-            lv[hh] = 0.f;
-            if (h < G && lane < nsp) {
-                mv[hh] = ld_dev(a.part_m + (rec0 + sp0 + lane) * G + h);
-                lv[hh] = ld_dev(a.part_l + (rec0 + sp0 + lane) * G + h);
-            }
-        }
-        if constexpr (G <= 5 && NT == 512) if (dest < 0 && sp0 == 0) KVDEC_TRACE(18);
         __syncthreads();  // the previous chunk is done with f_m / scale_old
 #pragma unroll
         for (int hh = 0; hh < HW; ++hh) {

@@ -23,8 +23,8 @@ import numpy as np
 SLOTS = {0: "entry", 1: "loads issued", 2: "query converted", 3: "scores and maximum", 4: "weights",
          13: "streams merged", 14: "record stores issued", 15: "record stores acknowledged", 16: "ticket returned",
          17: "merge done (merging workgroups)"}
-MERGE_SLOTS = [(16, "ticket returned"), (30, "merge entered"), (31, "record loads issued"),
-               (18, "(m, l) loads issued"), (19, "(m, l) reduced"), (20, "records accumulated"),
+MERGE_SLOTS = [(16, "ticket returned"), (30, "merge entered"), (18, "(m, l) loads issued"),
+               (31, "record loads issued"), (19, "(m, l) reduced"), (20, "records accumulated"),
                (21, "columns combined"), (17, "outputs stored")]
 TICK_US = 0.01  # s_memrealtime runs at 100 MHz
 

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 OWN_CHAIN = [0, 1, 2, 3, 4, 13, 14]          # every workgroup of a multi-split group
 PUBLISH = [14, 15, 16]                       # ... that publishes a record
-MERGE_CHAIN = [16, 30, 31, 18, 19, 20, 21, 17]  # the merging workgroup
+MERGE_CHAIN = [16, 30, 18, 31, 19, 20, 21, 17]  # the merging workgroup
 
 
 @pytest.fixture(scope="module")

@@ -30,9 +30,12 @@ def pinned(a):
     return t
 
 
-def run_tail(K, c, window, tail, chunk, depth, copy_stream=None, zero_copy=False):
+def run_tail(K, c, window, tail, chunk, depth, copy_stream=None, zero_copy=False, timed=False):
     """window: per slot (begin, n) resident cells; tail: per slot (begin, n)
-    cells of the host tail, which holds rows [0, tail_capacity) of the cache."""
+    cells of the host tail, which holds rows [0, tail_capacity) of the cache.
+    timed: also return the seconds of the attend call and its completion
+    (planning, uploads and pinned copies excluded)."""
+    import time
     import torch
     tail_cap = max(b + n for b, n in tail)
     p = K.plan(c.hq, c.hkv, c.d, c.n_slots, c.capacity, k_type=c.kind, v_type=c.vkind, scale=c.scale,
@@ -46,9 +49,14 @@ def run_tail(K, c, window, tail, chunk, depth, copy_stream=None, zero_copy=False
     ws = K.workspace(p)
     out = torch.full((c.n_slots, c.hq, c.d), float("nan"), device="cuda")
     lse = torch.full((c.n_slots, c.hq), float("nan"), device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     K.attend(p, c.q_d, c.kc_d, c.vc_d, ws, out=out, lse=lse, k_scales=c.ks_d, v_scales=c.vs_d, k_tail=hk, v_tail=hv,
              k_tail_scales=hks, v_tail_scales=hvs, copy_stream=copy_stream)
     torch.cuda.synchronize()
+    seconds = time.perf_counter() - t0
+    if timed:
+        return out.cpu().numpy(), lse.cpu().numpy(), p, seconds
     return out.cpu().numpy(), lse.cpu().numpy(), p
 
 
@@ -234,7 +242,6 @@ def test_ring_reuse_waits_for_slow_readers(KF, depth):
     reading the slot's previous chunk has finished, or that kernel would read
     the next chunk's rows.  18 chunks through 2 or 3 slots, checked against
     the oracle and the all-resident result."""
-    import time
     import torch
     c = Case(62, 32, 8, 128, occupied=[6000])
     res_out, res_lse = c.run(KF)
@@ -244,16 +251,16 @@ def test_ring_reuse_waits_for_slow_readers(KF, depth):
     for delay in (0, 60):
         KF.lib.kvdec_fi_configure(-1, -1, delay)
         try:
-            t0 = time.perf_counter()
-            out, lse, p = run_tail(KF, c, window=[(4500, 1500)], tail=[(0, 4500)], chunk=256, depth=depth,
-                                   copy_stream=torch.cuda.Stream())
-            wall.append(time.perf_counter() - t0)
+            out, lse, p, seconds = run_tail(KF, c, window=[(4500, 1500)], tail=[(0, 4500)], chunk=256, depth=depth,
+                                            copy_stream=torch.cuda.Stream(), timed=True)
+            wall.append(seconds)
         finally:
             KF.lib.kvdec_fi_configure(-1, -1, 0)
         assert p.info()["n_tail_chunks"] == 18
         check(out, lse, *c.oracle())
         check(out, lse, res_out, res_lse, tol=TOL_SPLITS)
-    # the delays did run: at least 0.1 ms per chunk kernel on top
+    # the delays did run: at least 0.1 ms per chunk kernel on top of the
+    # call (its own time, without planning, uploads and pinned copies)
     assert wall[1] - wall[0] > 18 * 1e-4, wall
 
 
