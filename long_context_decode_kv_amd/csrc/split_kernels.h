@@ -184,6 +184,11 @@ __device__ __forceinline__ float scatter_sum8(const float (&v)[GS], int sub) {
     return x[0];
 }
 
+// x of lane `l` (a constant over the wave), in a scalar register.
+__device__ __forceinline__ float lane_value(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
 // Max / sum over the whole wave; every lane receives the result.
 __device__ __forceinline__ float wave_max(float x) {
     x = fmaxf(x, dpp<0xB1>(x));
@@ -1412,16 +1417,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     const int64_t rec = sa.part_begin + (int64_t)g * sa.n_splits + split;
     const __amdgpu_buffer_rsrc_t rs = part_rsrc(a);
     for (int t = tid; t < G * D; t += 64 * W) {
-        const int h = t / D, d = t - h * D;
-        float M = kNegInf;
-#pragma unroll
-        for (int w = 0; w < W; ++w) M = fmaxf(M, mg_m[w][h]);
+        static_assert(W == 8 && D % 64 == 0, "stream factors in lanes 0..7, one row per wave");
+        // A wave covers 64 columns of one row h (D is a multiple of 64): the
+        // W streams' factors of the row are computed once, in lanes 0..W-1,
+        // and read back as scalars; the sums keep the stream order.
+        const int h = __builtin_amdgcn_readfirstlane(t / D), d = t - h * D;
+        const float mw = lane < W ? mg_m[lane][h] : kNegInf;
+        float M = fmaxf(mw, dpp<0xB1>(mw));  // maximum over lanes 0..7
+        M = fmaxf(M, dpp<0x4E>(M));
+        M = fmaxf(M, dpp<0x141>(M));
+        const float fw = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);
+        const float lw = lane < W ? mg_l[lane][h] : 0.f;
+        M = lane_value(M, 0);
         float L = 0.f, O = 0.f;
 #pragma unroll
         for (int w = 0; w < W; ++w) {
-            const float mw = mg_m[w][h];
-            const float f = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);
-            L = fmaf(mg_l[w][h], f, L);
+            const float f = lane_value(fw, w);
+            L = fmaf(lane_value(lw, w), f, L);
             O = fmaf(mg_o[w][h][d], f, O);
         }
         if (single) {
