@@ -50,7 +50,8 @@ def load():
 def record(K, layers=36, occupied=13100, capacity=16384, hq=32, hkv=8, d=128, reps=20):
     """Run the step in a captured graph with and without stamps; return
     (plan info, us per step without stamps, with stamps, stamps int64
-    [layers, workgroups, 32] in clock ticks, 0 where a slot was not written)."""
+    [layers, workgroups, 32] in clock ticks, 0 where a slot was not written,
+    the KV head each workgroup reads)."""
     import torch
     from long_context_decode_kv_amd import synth
     ks, vs, qs, outs, lses = [], [], [], [], []
@@ -64,6 +65,7 @@ def record(K, layers=36, occupied=13100, capacity=16384, hq=32, hkv=8, d=128, re
     p = K.plan(hq, hkv, d, 1, capacity, n_occupied=[occupied])
     info = p.info()
     nw = info["n_workgroups"]
+    heads = np.asarray(p.splits())[:, 1].astype(np.int64)
     ws = K.workspace(p)
     st = torch.zeros(layers * nw * 32, dtype=torch.int64, device="cuda")
 
@@ -96,14 +98,16 @@ def record(K, layers=36, occupied=13100, capacity=16384, hq=32, hkv=8, d=128, re
             g.replay()
             torch.cuda.synchronize()
     x = st.view(layers, nw, 32).cpu().numpy().astype(np.int64)
-    return info, times[False], times[True], x
+    return info, times[False], times[True], x, heads
 
 
-def summarize(x):
+def summarize(x, heads=None):
     """Phase times (us) from the stamps of record(): per slot the median and
     the slowest workgroup, per-wave P.V and last-V times, the merging
     workgroups' chain (us after their ticket), the gap from a layer's last
-    merge to the next layer's first entry, and first entry to last merge."""
+    merge to the next layer's first entry, and first entry to last merge.
+    With `heads` (KV head per workgroup): per KV head, the mean time from a
+    workgroup's entry to its last V row landing."""
     L = x.shape[0]
     rel = lambda layer, v: (v - x[layer, :, 0].min()) * TICK_US  # noqa: E731
     out = {"phases": {}, "merge": {}, "waves": {}}
@@ -132,6 +136,9 @@ def summarize(x):
     gap = [(x[layer + 1, :, 0].min() - x[layer, :, 17].max()) * TICK_US for layer in range(1, L - 1)]
     out["gap"] = float(np.mean(gap))
     out["span"] = float(np.mean([(x[layer, :, 17].max() - x[layer, :, 0].min()) * TICK_US for layer in range(1, L)]))
+    if heads is not None:
+        own = np.array([(x[layer, :, 22:30].max(1) - x[layer, :, 0]) * TICK_US for layer in range(1, L)]).mean(0)
+        out["heads"] = [round(float(own[heads == h].mean()), 2) for h in range(int(heads.max()) + 1)]
     return out
 
 
@@ -141,12 +148,12 @@ def main(argv=None):
     ap.add_argument("--occupied", type=int, default=13100)
     args = ap.parse_args(argv)
     K = load()
-    info, us_plain, us_traced, x = record(K, layers=args.layers, occupied=args.occupied)
+    info, us_plain, us_traced, x, heads = record(K, layers=args.layers, occupied=args.occupied)
     print(f"library source hash {K.LIB_SOURCE_HASH}; plan: {info['n_workgroups']} workgroups, "
           f"{info['split_cells']} cells per split, kernel {info['kernel']}")
     print(f"step without stamps {us_plain:.1f} us ({us_plain / args.layers:.2f} us / layer), "
           f"with stamps {us_traced:.1f} us ({us_traced / args.layers:.2f} us / layer)")
-    s = summarize(x)
+    s = summarize(x, heads)
     print("phase (us after the layer's first workgroup entry)   median   slowest workgroup")
     for name, (med, slow) in s["phases"].items():
         print(f"  {name:48s} {med:7.2f}   {slow:7.2f}")
@@ -155,6 +162,7 @@ def main(argv=None):
     print("merging workgroups, us after their ticket returned:")
     for name, t in s["merge"].items():
         print(f"  {name:48s} {t:7.2f}")
+    print(f"entry to last V landed, mean per KV head: {s['heads']}")
     print(f"gap from a layer's last merge to the next layer's first entry: {s['gap']:.2f} us")
     print(f"first entry to last merge done: {s['span']:.2f} us")
 

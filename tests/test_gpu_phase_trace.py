@@ -84,9 +84,10 @@ def test_timeline_summary_runs_on_recorded_stamps(KT):
     """A short run of the timeline tool: two layers of a 4096-cell
     Qwen3-8B-shaped cache, every phase present and ordered on average."""
     from long_context_decode_kv_amd import phase_trace
-    info, us_plain, us_traced, x = phase_trace.record(KT, layers=3, occupied=4000, capacity=4096, reps=3)
+    info, us_plain, us_traced, x, heads = phase_trace.record(KT, layers=3, occupied=4000, capacity=4096, reps=3)
     assert info["kernel"] == KT.KERNEL_ONESHOT and us_plain > 0 and us_traced > 0
-    s = phase_trace.summarize(x)
+    assert heads.shape == (info["n_workgroups"],) and set(heads.tolist()) == set(range(8))
+    s = phase_trace.summarize(x, heads)
     names = list(phase_trace.SLOTS.values())
     assert list(s["phases"]) == names
     meds = [s["phases"][n][0] for n in names]
@@ -94,3 +95,4 @@ def test_timeline_summary_runs_on_recorded_stamps(KT):
     m = [s["merge"][n] for _, n in phase_trace.MERGE_SLOTS]
     assert m[0] == 0 and all(a <= b + 1e-9 for a, b in zip(m, m[1:]))
     assert s["span"] > 0 and s["gap"] > 0
+    assert len(s["heads"]) == 8 and all(0 < t < s["span"] for t in s["heads"])
