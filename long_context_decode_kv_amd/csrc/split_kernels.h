@@ -1422,19 +1422,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
         // W streams' factors of the row are computed once, in lanes 0..W-1,
         // and read back as scalars; the sums keep the stream order.
         const int h = __builtin_amdgcn_readfirstlane(t / D), d = t - h * D;
-        const float mw = lane < W ? mg_m[lane][h] : kNegInf;
+        // every LDS read of the column first, so that their latencies overlap
+        float ow[W];
+#pragma unroll
+        for (int w = 0; w < W; ++w) ow[w] = mg_o[w][h][d];
+        const float mr = mg_m[lane % W][h], lr = mg_l[lane % W][h];
+        const float mw = lane < W ? mr : kNegInf;
         float M = fmaxf(mw, dpp<0xB1>(mw));  // maximum over lanes 0..7
         M = fmaxf(M, dpp<0x4E>(M));
         M = fmaxf(M, dpp<0x141>(M));
         const float fw = (mw == kNegInf) ? 0.f : exp2_fast(mw - M);
-        const float lw = lane < W ? mg_l[lane][h] : 0.f;
+        const float lw = lane < W ? lr : 0.f;
         M = lane_value(M, 0);
         float L = 0.f, O = 0.f;
 #pragma unroll
         for (int w = 0; w < W; ++w) {
             const float f = lane_value(fw, w);
             L = fmaf(lane_value(lw, w), f, L);
-            O = fmaf(mg_o[w][h][d], f, O);
+            O = fmaf(ow[w], f, O);
         }
         if (single) {
             merge_acc_in1(a, rm.row(h), d, D, M, L, O);
