@@ -237,7 +237,8 @@ def test_tail_failure_reports_device_error_and_workspace_recovers(KF, what, n):
 @pytest.mark.parametrize("depth", [2, 3])
 def test_ring_reuse_waits_for_slow_readers(KF, depth):
     """Every tail-chunk kernel starts about 1 ms late (a bounded sleep kernel
-    ahead of it on the compute stream) while the copies run ahead on their
+    ahead of it on the compute stream; its length follows the shader clock,
+    0.9 to 2 ms on the machines measured) while the copies run ahead on their
     own stream: a copy into a ring slot must still wait until the kernel
     reading the slot's previous chunk has finished, or that kernel would read
     the next chunk's rows.  18 chunks through 2 or 3 slots, checked against
@@ -248,7 +249,7 @@ def test_ring_reuse_waits_for_slow_readers(KF, depth):
     # one untimed run first: plan, workspace and pinned arrays, first launches
     run_tail(KF, c, window=[(4500, 1500)], tail=[(0, 4500)], chunk=256, depth=depth, copy_stream=torch.cuda.Stream())
     wall = []
-    for delay in (0, 300):
+    for delay in (0, 600):
         KF.lib.kvdec_fi_configure(-1, -1, delay)
         try:
             out, lse, p, seconds = run_tail(KF, c, window=[(4500, 1500)], tail=[(0, 4500)], chunk=256, depth=depth,
@@ -259,11 +260,11 @@ def test_ring_reuse_waits_for_slow_readers(KF, depth):
         assert p.info()["n_tail_chunks"] == 18
         check(out, lse, *c.oracle())
         check(out, lse, res_out, res_lse, tol=TOL_SPLITS)
-    # the delays did run: at least 0.5 ms per chunk kernel on top of the
+    # the delays did run: at least 0.4 ms per chunk kernel on top of the
     # call (its own time, without planning, uploads and pinned copies; the
     # delays must outlast the host's enqueueing of the copies to show)
     print(f"\ntail call without / with delays (ring depth {depth}): {wall[0] * 1e3:.2f} / {wall[1] * 1e3:.2f} ms")
-    assert wall[1] - wall[0] > 18 * 5e-4, wall
+    assert wall[1] - wall[0] > 18 * 4e-4, wall
 
 
 @pytest.mark.parametrize("hq,slots", [(5, 1), (5, 3), (7, 1)])
