@@ -2,7 +2,7 @@
 workgroup entry; head_dim 128, f16 K and V, G <= 5, contiguous cells)
 against the float64 oracle: every split length a wave can hold (partial
 waves, odd counts, the 448-cell maximum), forced split sizes covering each
-compiled loads-per-lane instance, all group sizes, several slots, the
+compiled loads-per-lane instance, all group sizes, 1 to 8 KV heads, several slots, the
 device-filling plan of the Qwen3-8B-shaped layer, needles, partial outputs,
 strided layouts, poisoned unattended cells, a window with a host tail, an
 8-byte-aligned q and graph replays."""
@@ -58,6 +58,22 @@ def test_group_sizes_device_filling(K, g):
     p = c.plan(K, n_cu=256)
     info = p.info()
     assert info["kernel"] == K.KERNEL_ONESHOT and info["n_workgroups"] == 256 and info["split_cells"] == 416
+    check(*c.run(K, plan=p), *c.oracle())
+
+
+@pytest.mark.parametrize("hkv", [1, 2, 3, 5, 6, 7])
+def test_kv_head_counts_device_filling(K, hkv):
+    """The planner's own choice for 1 to 7 KV heads of 4 query heads each
+    on a 6000-cell layer.  Workgroup b runs on XCD b mod 8 and reads KV head
+    b mod hkv, so with fewer than 8 KV heads the splits of one head run on
+    several XCDs and publish and count their records across them; one KV
+    head (94 splits of 64 cells) also takes the two-level merge."""
+    c = Case(1310 + hkv, 4 * hkv, hkv, 128, occupied=[6000])
+    p = c.plan(K, n_cu=256)
+    info = p.info()
+    assert info["kernel"] == K.KERNEL_ONESHOT and info["n_workgroups"] <= 256
+    per_head = np.bincount(p.splits()[:, 1], minlength=hkv)
+    assert np.all(per_head == per_head[0]) and per_head[0] > 8, per_head
     check(*c.run(K, plan=p), *c.oracle())
 
 
