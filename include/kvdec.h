@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KVDEC_VERSION 10800 /* 1.8.0: one cache line per merge ticket, kvdec_plan_info.ticket_bytes */
+#define KVDEC_VERSION 10801 /* 1.8.1: k, v, their scales and plan_cells may be NULL where no cell or entry exists */
 
 /* Status codes. */
 #define KVDEC_OK 0
@@ -216,19 +216,21 @@ typedef struct kvdec_plan kvdec_plan_t;
  * q: device fp32 [n_slots][n_queries][n_q_heads][head_dim] (n_queries = 1:
  *   [n_slots][n_q_heads][head_dim]); out, lse and the partial triple below
  *   carry the same [n_queries] axis after the slot.
- * k, v: device code arrays, non-null even when no cell is attended (the
- *   matrix-core kernel reads row 0 in place of hole entries).  Row (cell c,
+ * k, v: device code arrays, non-null whenever capacity_cells > 0, even when
+ *   no cell is attended (the matrix-core kernel reads row 0 in place of hole
+ *   entries); with capacity_cells 0 nothing reads them and they may be
+ *   NULL.  Row (cell c,
  *   KV head g) starts at byte
  *   c * cell_stride + g * head_stride; a row holds head_dim f16 values,
  *   head_dim int8 codes, or head_dim / 2 bytes of 4-bit codes.  A stride of 0
  *   means the dense layout [cell][kv head][row].  Base pointers and strides
  *   must be multiples of 16 bytes (of 8 bytes for 4-bit rows).
  * k_scales, v_scales: device f16 scales, dense [cell][kv head][head_dim/32],
- *   required for the block-scaled kinds and ignored for f16; aligned to one
- *   row of scales, min(16, head_dim / 16) bytes.
+ *   required for the block-scaled kinds when capacity_cells > 0 and ignored
+ *   for f16; aligned to one row of scales, min(16, head_dim / 16) bytes.
  * plan_cells: device int32 copy of the plan's entries (kvdec_plan_cells) in
- *   indirect mode, else NULL.  Entries outside [0, capacity_cells) are read
- *   as holes.
+ *   indirect mode, else NULL (also NULL allowed for an indirect plan of no
+ *   entries).  Entries outside [0, capacity_cells) are read as holes.
  * k_tail, v_tail (+ k_tail_scales, v_tail_scales): pinned host tail arrays
  *   when the plan has a tail, else NULL.  They must stay valid and unchanged
  *   until the work enqueued by the call has finished.

@@ -127,7 +127,11 @@ int launch(const kvdec_plan_t& p, const kvdec::SplitArgs& a, void* stream) {
 int check_io(const kvdec_plan_t& p, const kvdec_io* io) {
     const int D = p.head_dim;
     if (!io->q || !aligned(io->q, 8)) return fail(KVDEC_E_INVALID, "q must be non-null and 8-byte aligned");
-    if (!io->k || !io->v) return fail(KVDEC_E_INVALID, "k and v must be non-null");
+    // With no device cells (capacity_cells 0) no split holds a cell or a plan
+    // entry, so no kernel reads k, v or their scales: they may be null.
+    const bool cells = p.capacity > 0;
+    if (cells && (!io->k || !io->v))
+        return fail(KVDEC_E_INVALID, "k and v must be non-null when capacity_cells > 0");
     const int64_t krow = kvdec::row_bytes(p.k_type, D), vrow = kvdec::row_bytes(p.v_type, D);
     const int64_t k_cs = io->k_cell_stride ? io->k_cell_stride : krow * p.n_kv_heads;
     const int64_t k_hs = io->k_head_stride ? io->k_head_stride : krow;
@@ -140,11 +144,14 @@ int check_io(const kvdec_plan_t& p, const kvdec_io* io) {
         return fail(KVDEC_E_INVALID, "v pointer and strides must be non-negative multiples of the row load size");
     // one row of scales (head_dim/32 f16 values) is read with one load
     const size_t sal = std::min<size_t>(16, (size_t)p.head_dim / 16);
-    if (kvdec::is_scaled(p.k_type) && (!io->k_scales || !aligned(io->k_scales, sal)))
+    if (kvdec::is_scaled(p.k_type) && ((cells && !io->k_scales) || !aligned(io->k_scales, sal)))
         return fail(KVDEC_E_INVALID, "k_scales required for block-scaled K, aligned to min(16, head_dim/16) bytes");
-    if (kvdec::is_scaled(p.v_type) && (!io->v_scales || !aligned(io->v_scales, sal)))
+    if (kvdec::is_scaled(p.v_type) && ((cells && !io->v_scales) || !aligned(io->v_scales, sal)))
         return fail(KVDEC_E_INVALID, "v_scales required for block-scaled V, aligned to min(16, head_dim/16) bytes");
-    if (p.indirect && !io->plan_cells) return fail(KVDEC_E_INVALID, "indirect plan needs plan_cells on the device");
+    // (a plan without entries leaves every slot empty: nothing reads plan_cells)
+    const int64_t n_entries = p.device_cells ? p.n_device_entries : (int64_t)p.cells.size();
+    if (p.indirect && n_entries > 0 && !io->plan_cells)
+        return fail(KVDEC_E_INVALID, "indirect plan needs plan_cells on the device");
     const bool any_part = io->part_m || io->part_l || io->part_o;
     const bool all_part = io->part_m && io->part_l && io->part_o;
     if (any_part && !all_part) return fail(KVDEC_E_INVALID, "part_m, part_l and part_o go together");

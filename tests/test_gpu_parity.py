@@ -70,6 +70,27 @@ def test_empty_slots(K):
     assert np.all(out[0] == 0) and np.all(np.isneginf(lse[0])) and np.all(np.isneginf(lse[2]))
 
 
+@pytest.mark.parametrize("kind", [O.F16, O.Q8_B32, O.Q4_B32], ids=["f16", "int8", "4bit"])
+@pytest.mark.parametrize("indirect", [False, True], ids=["contiguous", "indirect"])
+def test_no_device_cells_with_null_cache_arrays(K, kind, indirect):
+    """capacity_cells 0: k, v, scales and plan_cells passed as NULL, every
+    slot empty -- outputs are the empty result (0, lse -inf) and the
+    partial triple the merge identity (m -inf, l 0, o 0)."""
+    import torch
+    d, hkv = (128, 8) if kind == O.F16 else (256, 4)
+    hq = 4 * hkv
+    kw = dict(cells=[[], [], []]) if indirect else dict(n_occupied=[0, 0, 0])
+    p = K.plan(hq, hkv, d, 3, 0, k_type=kind, v_type=kind, n_cu=256, **kw)
+    q = dev(np.random.default_rng(31).standard_normal((3, hq, d)).astype(np.float32))
+    out = torch.full((3, hq, d), float("nan"), device="cuda")
+    lse = torch.full((3, hq), float("nan"), device="cuda")
+    pm, pl, po = (torch.full(s, float("nan"), device="cuda") for s in ((3, hq), (3, hq), (3, hq, d)))
+    K.attend(p, q, 0, 0, K.workspace(p), out=out, lse=lse, part=(pm, pl, po))
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+    assert torch.all(torch.isneginf(pm)) and torch.all(pl == 0) and torch.all(po == 0)
+
+
 @pytest.mark.parametrize("tps", [1, 2, 7, 100000])
 def test_split_count_only_changes_rounding(K, tps):
     c = Case(13, 32, 8, 128, occupied=[13100])

@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
     for name in names:
         assert hasattr(K.lib, name), name
     assert set(names) == set(K.EXPORTED)
-    assert K.version() == 10800
+    assert K.version() == 10801
 
 
 def test_probe_library_exports_and_rejects_bad_arguments():
@@ -347,6 +347,8 @@ def test_attend_validation_before_device_work():
     assert _status(lambda: K.attend(p, FAKE, FAKE, FAKE, (FAKE + 16, p.workspace_bytes), **args)) == K.E_INVALID
     assert _status(lambda: K.attend(p, 0, FAKE, FAKE, ws, **args)) == K.E_INVALID            # no q
     assert _status(lambda: K.attend(p, FAKE, FAKE + 8, FAKE, ws, **args)) == K.E_INVALID     # misaligned k
+    assert _status(lambda: K.attend(p, FAKE, 0, FAKE, ws, **args)) == K.E_INVALID            # no k
+    assert _status(lambda: K.attend(p, FAKE, FAKE, 0, ws, **args)) == K.E_INVALID            # no v
     assert _status(lambda: K.attend(p, FAKE, FAKE, FAKE, ws, k_cell_stride=24, **args)) == K.E_INVALID
     assert _status(lambda: K.attend(p, FAKE, FAKE, FAKE, ws, stream=0)) == K.E_INVALID       # no output
     assert _status(lambda: K.attend(p, FAKE, FAKE, FAKE, ws, part=(FAKE, FAKE, 0), stream=0)) == K.E_INVALID
@@ -362,6 +364,30 @@ def test_attend_validation_before_device_work():
     assert _status(lambda: K.attend(p, FAKE, FAKE, FAKE, ws, live_records=FAKE, **args)) == K.E_INVALID  # contiguous
     assert _status(lambda: K.attend(pi, FAKE, FAKE, FAKE, wsi, out=FAKE, k_scales=FAKE, v_scales=FAKE, plan_cells=FAKE,
                                     live_records=FAKE + 2, stream=0)) == K.E_INVALID     # misaligned live_records
+
+
+def test_no_device_cells_needs_no_cache_arrays():
+    """With capacity_cells 0 no split holds a cell or an entry, so k, v,
+    their scales and (for an indirect plan, which then has no entries)
+    plan_cells may be NULL: the call passes validation and reaches the
+    device (which this host lacks); with capacity_cells > 0 they may not."""
+    for kind in (K.F16, K.Q8_B32, K.Q4_B32):
+        d = 128 if kind == K.F16 else 256
+        for p in (K.plan(4 * 2, 2, d, 2, 0, k_type=kind, v_type=kind, n_occupied=[0, 0], n_cu=256),
+                  K.plan(4 * 2, 2, d, 2, 0, k_type=kind, v_type=kind, cells=[[], []], n_cu=256)):
+            assert p.info()["n_entries"] == 0
+            ws = (FAKE, max(p.workspace_bytes, 256))
+            st = _status(lambda: K.attend(p, FAKE, 0, 0, ws, out=FAKE, stream=0))
+            assert st != K.E_INVALID, K.lib.kvdec_last_error().decode()
+    p1 = K.plan(24, 4, 256, 1, 1, k_type=K.Q8_B32, v_type=K.Q8_B32, n_occupied=[0], n_cu=256)
+    ws1 = (FAKE, p1.workspace_bytes)
+    assert _status(lambda: K.attend(p1, FAKE, 0, 0, ws1, out=FAKE, stream=0)) == K.E_INVALID
+    assert "capacity_cells > 0" in K.lib.kvdec_last_error().decode()
+    assert _status(lambda: K.attend(p1, FAKE, FAKE, FAKE, ws1, out=FAKE, stream=0)) == K.E_INVALID  # no scales
+    pi = K.plan(24, 4, 256, 1, 128, k_type=K.Q8_B32, v_type=K.Q8_B32, cells=[[5]], n_cu=256)
+    wsi = (FAKE, pi.workspace_bytes)
+    assert _status(lambda: K.attend(pi, FAKE, FAKE, FAKE, wsi, out=FAKE, k_scales=FAKE, v_scales=FAKE,
+                                    stream=0)) == K.E_INVALID                               # entries, no plan_cells
 
 
 def test_ticket_area_fixed_size():
