@@ -1,7 +1,9 @@
 """GPU parity of the resident-window + pinned-host-tail path: the tail is
 streamed through the staging ring in the workspace and merged with the
 window by log-sum-exp; the result must match the float64 oracle over the
-union of cells and the all-resident GPU result over the same cells."""
+union of cells and the all-resident GPU result over the same cells.  Fixed
+cases, failure injection, slow ring readers, and a family of seeded random
+configurations."""
 
 import numpy as np
 import pytest
@@ -279,4 +281,43 @@ def test_tail_odd_row_count(K, hq, slots):
     tail = [(b, 1000) for b in begins]
     out, lse, p = run_tail(K, c, window, tail, chunk=256, depth=2)
     assert p.info()["n_tail_chunks"] == 4 * slots
+    check(out, lse, *c.oracle())
+
+
+TAIL_KIND_PAIRS = [(O.F16, O.F16), (O.Q8_B32, O.Q8_B32), (O.Q4_B32, O.Q4_B32), (O.F16, O.Q8_B32),
+                   (O.F16, O.Q4_B32), (O.Q8_B32, O.Q4_B32)]
+
+
+def draw_tail(seed):
+    """A seeded window + tail configuration: head_dim, group size, KV heads,
+    storage kinds, 1-3 slots of assorted lengths (empty, one cell, tile
+    edges), each slot's first cells in the host tail (none, some or all),
+    chunk size, ring depth, zero-copy or staged, and the copy stream."""
+    r = np.random.default_rng(50000 + seed)
+    d = int(r.choice([64, 128, 256]))
+    g = int(r.integers(1, (8 if d == 64 else 16) + 1))
+    hkv = int(r.choice([1, 2, 4, 8]))
+    kind, vkind = TAIL_KIND_PAIRS[int(r.integers(len(TAIL_KIND_PAIRS)))]
+    n_slots = int(r.integers(1, 4))
+    lens = [int(x) for x in r.choice([0, 1, 100, 128, 129, 700, 2000, 4100], size=n_slots)]
+    begins = [int(x) for x in np.cumsum([0] + lens[:-1]) + int(r.integers(0, 64))]
+    tails = [int(r.integers(0, n + 1)) for n in lens]
+    chunk = int(r.choice([128, 256, 384, 512, 1024, 2048]))
+    depth = int(r.integers(2, 5))
+    zero_copy = bool(r.integers(2)) and r.random() < 0.3
+    own_stream = bool(r.integers(2))
+    return d, g, hkv, kind, vkind, lens, begins, tails, chunk, depth, zero_copy, own_stream
+
+
+@pytest.mark.parametrize("seed", [s for s in range(40) if sum(draw_tail(s)[7]) > 0][:24])
+def test_random_window_and_tail(K, seed):
+    """Seeded random window + tail calls (draw_tail) against the oracle over
+    each slot's whole range."""
+    import torch
+    d, g, hkv, kind, vkind, lens, begins, tails, chunk, depth, zero_copy, own_stream = draw_tail(seed)
+    c = Case(seed, g * hkv, hkv, d, kind=kind, v_kind=vkind, occupied=lens, begins=begins)
+    window = [(b + t, n - t) for b, n, t in zip(begins, lens, tails)]
+    tail = [(b, t) for b, t in zip(begins, tails)]
+    out, lse, _ = run_tail(K, c, window, tail, chunk=chunk, depth=depth,
+                           copy_stream=torch.cuda.Stream() if own_stream else None, zero_copy=zero_copy)
     check(out, lse, *c.oracle())
