@@ -158,3 +158,44 @@ def test_window_plus_tail_multi_query(K):
              copy_stream=torch.cuda.Stream())
     torch.cuda.synchronize()
     check(out.cpu().numpy(), lse.cpu().numpy(), *oracle_mq(c, q, qp))
+
+
+MQ_KIND_PAIRS = [(O.F16, O.F16), (O.Q8_B32, O.Q8_B32), (O.Q4_B32, O.Q4_B32), (O.F16, O.Q8_B32),
+                 (O.F16, O.Q4_B32), (O.Q8_B32, O.Q4_B32)]
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_multi_query_configuration(K, seed):
+    """Seeded random multi-query calls: head_dim, 2-8 query rows, group size
+    (rows per KV head at most 16), KV heads, storage kinds, 1-3 slots of
+    assorted lengths, contiguous or indirect (with or without cell
+    positions), the planner's split or a forced one, and query positions
+    causal or anywhere (before the first cell, past the last)."""
+    r = np.random.default_rng(60000 + seed)
+    d = int(r.choice([128, 256]))
+    n_q = int(r.integers(2, 9))
+    g = int(r.integers(1, 16 // n_q + 1))
+    hkv = int(r.choice([1, 2, 4, 8]))
+    kind, vkind = MQ_KIND_PAIRS[int(r.integers(len(MQ_KIND_PAIRS)))]
+    n_slots = int(r.integers(1, 4))
+    lens = [int(x) for x in r.choice([0, 1, 5, 128, 129, 700, 3000, 9000], size=n_slots)]
+    indirect = bool(r.integers(2))
+    use_cell_pos = indirect and bool(r.integers(2))
+    split = [{}, {"tiles_per_split": int(r.integers(1, 9))}][int(r.integers(2))]
+    if indirect:
+        c = Case(seed, g * hkv, hkv, d, kind=kind, v_kind=vkind, indirect_lengths=lens, shuffle=True)
+    else:
+        c = Case(seed, g * hkv, hkv, d, kind=kind, v_kind=vkind, occupied=lens,
+                 begins=list(np.cumsum([0] + lens[:-1]) + int(r.integers(0, 50))))
+    q = mq_q(seed, c, n_q)
+    cell_pos = None
+    if use_cell_pos:
+        cell_pos = r.permutation(c.capacity).astype(np.int32)
+        q_pos = r.integers(-3, c.capacity + 3, size=(c.n_slots, n_q)).astype(np.int32)
+    elif indirect or not r.integers(2):
+        q_pos = r.integers(-3, c.capacity + 3, size=(c.n_slots, n_q)).astype(np.int32)
+    else:
+        q_pos = causal_q_pos(c, n_q)
+    got = run_mq(K, c, n_q, q, q_pos, cell_pos=cell_pos, n_cu=256, **split)
+    want = oracle_mq(c, q, q_pos, cell_pos)
+    check(got[0].reshape(want[0].shape), got[1].reshape(want[1].shape), *want)
