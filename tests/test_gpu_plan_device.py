@@ -184,3 +184,43 @@ def test_generous_budget_bit_equal_to_tight(K, kind, size):
     if size == "two-level":
         # without live_records the padding is scanned: visibly slower
         assert times[("generous", False)] > 1.3 * times[("generous", True)]
+
+
+def draw_lists(seed):
+    """Seeded raw lists for a device-built plan: capacity around record
+    edges, 1-5 slots, cells anywhere, as a wrapping run or within a few
+    records, with holes, out-of-range entries (below -1, at / past the
+    capacity, INT32_MAX) and duplicates inserted; budgets a little under,
+    at or over each slot's record count (within 0 .. ceil(capacity / 128))."""
+    r = np.random.default_rng(70000 + seed)
+    cap = int(r.choice([1, 127, 128, 129, 1000, 5000, 40000]))
+    lists = []
+    for _ in range(int(r.integers(1, 6))):
+        n = int(r.choice([0, 1, 5, 100, 1000, 5000]))
+        style = int(r.integers(3))
+        if style == 0:
+            x = r.integers(0, cap, size=n)
+        elif style == 1:
+            x = (int(r.integers(0, cap)) + np.arange(n)) % cap
+        else:
+            recs = r.integers(0, -(-cap // 128), size=max(1, n // 100))
+            x = (recs[r.integers(0, len(recs), size=n)] * 128 + r.integers(0, 128, size=n)) % cap
+        x = [int(v) for v in x]
+        for _ in range(int(r.integers(0, 6))):
+            pick = int(r.integers(5))
+            v = [-1, -2 - int(r.integers(0, 5)), cap + int(r.integers(0, 5)), x[0] if x else -1, 2 ** 31 - 1][pick]
+            x.insert(int(r.integers(0, len(x) + 1)), v)
+        lists.append(x)
+    need = [len({c // 128 for c in x if 0 <= c < cap}) for x in lists]
+    budget = [max(0, min(-(-cap // 128), n + int(r.integers(-2, 4)))) for n in need]
+    return lists, cap, budget
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_lists_bit_exact_against_oracle(K, seed):
+    lists, cap, budget = draw_lists(seed)
+    _, _, got, nrec = build(K, lists, cap, budget)
+    want, counts = expected(lists, cap, budget)
+    assert np.array_equal(got, want)
+    dropped = sum(1 for x in lists for c in x if c < -1 or c >= cap)
+    assert list(nrec[:len(lists)]) == counts and nrec[len(lists)] == dropped
