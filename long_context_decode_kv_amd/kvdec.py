@@ -229,7 +229,8 @@ def plan(n_q_heads, n_kv_heads, head_dim, n_slots, capacity_cells, *, k_type=F16
     p = Problem()
     p.n_q_heads, p.n_kv_heads, p.head_dim, p.n_slots = n_q_heads, n_kv_heads, head_dim, n_slots
     p.k_type, p.v_type = k_type, v_type
-    p.scale = (1.0 / np.sqrt(head_dim)) if scale is None else scale
+    # default 1/sqrt(head_dim); a head_dim the library will reject gets NaN
+    p.scale = (1.0 / np.sqrt(head_dim) if head_dim > 0 else float("nan")) if scale is None else scale
     p.tiles_per_split = tiles_per_split
     p.split_cells = split_cells
     p.kernel = kernel

@@ -588,3 +588,86 @@ def test_build_rejects_kernels_with_scratch():
         "x.h:9:1: remark:     ScratchSize [bytes/lane]: 188 [-Rpass-analysis=kernel-resource-usage]",
     ])
     assert build._scratch_kernels(log) == [("_Z2k2v", 188)]
+
+
+def _draw_plan_request(seed):
+    """A seeded kvdec_plan request, valid in most of its fields (each field
+    is malformed with probability 0.03): head_dim, group size, KV heads,
+    slots, capacity, storage kinds, query rows and one of contiguous ranges,
+    host cell lists, a device-built record budget or a window + tail."""
+    r = np.random.default_rng(90000 + seed)
+    bad = lambda good, badv: badv if r.random() < 0.03 else good  # noqa: E731
+    d = bad(int(r.choice([64, 128, 256])), int(r.choice([96, 0])))
+    hkv = bad(int(r.choice([1, 2, 4, 8])), int(r.choice([0, 3])))
+    g = bad(int(r.choice([1, 2, 3, 4, 5, 6, 8, 16])), 17)
+    n_slots = bad(int(r.choice([1, 2, 3, 7, 64])), int(r.choice([0, 65])))
+    cap = bad(int(r.choice([0, 1, 127, 128, 129, 5000, 2 ** 20])), -1)
+    if d == 64 and g > 8:  # groups above 8 need head_dim 128 or 256
+        g = bad(8, g)
+    n_q = int(r.choice([1, 1, 1, 2, 4]))
+    if d == 64 or g * n_q > 16:  # several query rows: head_dim 128 / 256, at most 16 rows per KV head
+        n_q = bad(1, n_q)
+    kt = int(r.integers(0, 3))  # K stored at least as finely as V (f16 < int8 < 4-bit)
+    kw = dict(k_type=bad(kt, 3), v_type=bad(int(r.integers(kt, 3)), int(r.integers(0, 3))), n_queries=n_q,
+              n_cu=int(r.choice([256, 1, 80])))
+    ns, c0 = max(n_slots, 0), max(cap, 0)
+    mode = int(r.integers(4))
+    if mode in (0, 3):
+        b = [int(r.integers(0, c0 + 1)) for _ in range(ns)]
+        kw["cell_begin"] = [bad(x, -3) for x in b]
+        kw["n_occupied"] = [bad(int(r.integers(0, c0 - x + 1)), c0 - x + 1) for x in b]
+        if mode == 3:
+            kw["n_tail"] = [int(r.choice([0, 1, 300])) for _ in range(ns)]
+            kw["tail_begin"] = [bad(int(r.choice([0, 10])), -1) for _ in range(ns)]
+            kw["tail_capacity_cells"] = int(r.choice([400, 6000]))
+            kw["tail_chunk_cells"] = bad(int(r.choice([128, 512])), 100)
+            kw["tail_ring_depth"] = bad(int(r.choice([2, 4])), 17)
+            kw["tail_zero_copy"] = bool(r.integers(2))
+    elif mode == 1:
+        kw["cells"] = [[int(x) for x in r.integers(-1, max(c0, 1), size=int(r.choice([0, 1, 50, 300])))]
+                       for _ in range(ns)]
+        if ns and r.random() < 0.03:
+            kw["cells"][int(r.integers(ns))].append(c0 + 2)  # out of range
+    else:
+        kw["max_records"] = [bad(int(r.integers(0, -(-c0 // 128) + 1)), -1) for _ in range(ns)]
+    if r.integers(3) == 0:
+        kw["split_cells"] = bad(int(r.choice([32, 64, 448, 4096])), 33)
+    return (g * max(hkv, 1), hkv, d, n_slots, cap), kw, mode
+
+
+def test_random_plans_split_every_position_once():
+    """400 seeded plan requests (_draw_plan_request): a rejected one raises
+    with a status and a message; in an accepted one the split table holds
+    n_workgroups rows and the splits of every (slot, KV head) cover the
+    slot's positions -- its occupied cells, its list's entries or its
+    record budget -- exactly once (contiguous runs tile them).  Under the
+    sanitized build this also drives the planner's index arithmetic."""
+    accepted = 0
+    for seed in range(400):
+        args, kw, mode = _draw_plan_request(seed)
+        try:
+            p = K.plan(*args, **kw)
+        except K.KvdecError as e:
+            assert e.status < 0 and K.lib.kvdec_last_error().decode()
+            continue
+        accepted += 1
+        info, sp = p.info(), p.splits()
+        assert len(sp) == info["n_workgroups"] >= 1
+        n_slots, hkv = args[3], args[1]
+        if mode in (0, 3):
+            n = kw["n_occupied"]
+        elif mode == 1:
+            off = p.cells()[1]
+            n = [int(off[s + 1] - off[s]) for s in range(n_slots)]
+        else:
+            n = [128 * m for m in kw["max_records"]]
+        for s in range(n_slots):
+            for h in range(hkv):
+                rows = sp[(sp[:, 0] == s) & (sp[:, 1] == h)]
+                assert len(rows) >= 1 and np.all(rows[:, 3] >= 0), (seed, s, h)
+                assert rows[:, 3].sum() == n[s], (seed, s, h, rows[:, 3].sum(), n[s])
+                if info["split_interleave"] == 0:
+                    runs = rows[np.argsort(rows[:, 2])]
+                    ends = runs[:, 2] + runs[:, 3]
+                    assert runs[0, 2] == 0 and np.all(runs[1:, 2] == ends[:-1]), (seed, s, h)
+    assert accepted >= 150, accepted
