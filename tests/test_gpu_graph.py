@@ -77,3 +77,46 @@ def test_graph_replays_equal_eager(K, name):
         torch.cuda.synchronize()
         for (eo, el), o, l in zip(eager, outs, lses):
             assert torch.equal(o, eo) and torch.equal(l, el)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_configuration_replays(K, seed):
+    """A random configuration (the draw of test_gpu_random) captured once and
+    replayed three times, with an eager call on the same workspace after
+    each replay: every replay and every eager call bit-equal to the first
+    eager call, which matches the oracle."""
+    import torch
+    from test_gpu_random import draw
+    d, g, hkv, kind, vkind, lengths, indirect, split = draw(5000 + seed)
+    if indirect:
+        c = Case(seed, g * hkv, hkv, d, kind=kind, v_kind=vkind, indirect_lengths=lengths, shuffle=True)
+    else:
+        c = Case(seed, g * hkv, hkv, d, kind=kind, v_kind=vkind, occupied=lengths)
+    p = c.plan(K, n_cu=256, **split)
+    c.upload()
+    pc = None if c.raw is None else dev(p.cells()[0])
+    ws = K.workspace(p)
+    out = torch.full((c.n_slots, c.hq, c.d), float("nan"), device="cuda")
+    lse = torch.full((c.n_slots, c.hq), float("nan"), device="cuda")
+
+    def call():
+        K.attend(p, c.q_d, c.kc_d, c.vc_d, ws, out=out, lse=lse, k_scales=c.ks_d, v_scales=c.vs_d, plan_cells=pc)
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.synchronize()
+    want = (out.cpu().numpy().copy(), lse.cpu().numpy().copy())
+    check(*want, *c.oracle())
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        call()
+    for _ in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        gr.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), want[0]) and np.array_equal(lse.cpu().numpy(), want[1])
+        call()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), want[0]) and np.array_equal(lse.cpu().numpy(), want[1])
