@@ -321,3 +321,21 @@ def test_random_window_and_tail(K, seed):
     out, lse, _ = run_tail(K, c, window, tail, chunk=chunk, depth=depth,
                            copy_stream=torch.cuda.Stream() if own_stream else None, zero_copy=zero_copy)
     check(out, lse, *c.oracle())
+
+
+@pytest.mark.parametrize("zero_copy", [False, True], ids=["staged", "zerocopy"])
+def test_whole_context_from_the_tail_without_device_cells(K, zero_copy):
+    """capacity_cells 0 -- no device cells, k and v NULL -- and every slot's
+    cells in the host tail: the result is the oracle's over the tail cells."""
+    import torch
+    c = Case(66 + zero_copy, 16, 4, 128, occupied=[700, 1300], begins=[0, 700])
+    t = 2000
+    p = K.plan(c.hq, c.hkv, c.d, 2, 0, n_occupied=[0, 0], cell_begin=[0, 0], n_tail=[700, 1300],
+               tail_begin=[0, 700], tail_capacity_cells=t, tail_chunk_cells=512, tail_ring_depth=2,
+               tail_zero_copy=zero_copy)
+    hk, hv = pinned(c.kc[:t]), pinned(c.vc[:t])
+    out = torch.full((2, c.hq, c.d), float("nan"), device="cuda")
+    lse = torch.full((2, c.hq), float("nan"), device="cuda")
+    K.attend(p, dev(c.q), 0, 0, K.workspace(p), out=out, lse=lse, k_tail=hk, v_tail=hv)
+    torch.cuda.synchronize()
+    check(out.cpu().numpy(), lse.cpu().numpy(), *c.oracle())
