@@ -5,7 +5,8 @@ a fixed byte pattern; after the call, every margin byte must be unchanged
 and the results must match the float64 oracle.  One case per kernel family
 and path: the one-shot kernel, the streamed kernel on several slots with
 partials, the matrix-core kernel on int8 and 4-bit indirect plans and on
-several query rows, a resident window with a host tail, and kvdec_merge."""
+several query rows, a resident window with a host tail, and kvdec_merge;
+then seeded random configurations of every planner regime."""
 
 import numpy as np
 import pytest
@@ -163,3 +164,39 @@ def test_standalone_merge(K):
     for k, b in g.items():
         b.assert_guards_intact(k)
     check(v["out"].cpu().numpy(), v["lse"].cpu().numpy(), Ov / L[:, None], M + np.log(L))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_configurations_between_guards(K, seed):
+    """Random configurations (the generators of test_gpu_random: general
+    draws and draws sized for the planner's regimes, multi-query rows
+    included) with out, lse, every third one the partial triple, and the
+    workspace between guard margins: no byte outside them changes, and the
+    single-query results match the oracle."""
+    from test_gpu_random import draw, draw_filling
+    if seed % 2 == 0:
+        d, g, hkv, kind, vkind, lengths, indirect, split = draw(7000 + seed)
+        n_q = 1
+    else:
+        d, g, hkv, kind, vkind, lengths, indirect, n_q = draw_filling(7000 + seed)
+        split = {}
+    if indirect:
+        c = Case(seed, g * hkv, hkv, d, kind=kind, v_kind=vkind, indirect_lengths=lengths, shuffle=True)
+    else:
+        c = Case(seed, g * hkv, hkv, d, kind=kind, v_kind=vkind, occupied=lengths)
+    p = c.plan(K, n_cu=256, n_queries=n_q, **split)
+    c.upload()
+    part = seed % 3 == 0
+    bufs, t = outputs(c, n_q=n_q, part=part)
+    ws, wst = guarded_workspace(p)
+    pc = None if c.raw is None else dev(p.cells()[0])
+    q, kw = c.q_d, {}
+    if n_q > 1:
+        q = dev(np.random.default_rng(seed + 1).standard_normal((c.n_slots, n_q, c.hq, c.d)).astype(np.float32))
+        kw = dict(q_pos=dev(np.random.default_rng(seed).integers(-5, c.capacity + 5, size=(c.n_slots, n_q))
+                            .astype(np.int32)))
+    K.attend(p, q, c.kc_d, c.vc_d, wst, out=t["out"], lse=t["lse"], part=(t["pm"], t["pl"], t["po"]) if part else None,
+             k_scales=c.ks_d, v_scales=c.vs_d, plan_cells=pc, **kw)
+    out, lse = finish(bufs, ws, c, t, n_q=n_q)
+    if n_q == 1:
+        check(out, lse, *c.oracle())
