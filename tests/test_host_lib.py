@@ -671,3 +671,44 @@ def test_random_plans_split_every_position_once():
                     ends = runs[:, 2] + runs[:, 3]
                     assert runs[0, 2] == 0 and np.all(runs[1:, 2] == ends[:-1]), (seed, s, h)
     assert accepted >= 150, accepted
+
+
+def test_phase_timeline_summary_on_built_stamps():
+    """summarize() of the phase-trace tool on stamps built by hand (100 MHz
+    ticks): 3 layers of 4 workgroups; each layer starts 2000 ticks after the
+    previous one, workgroup w enters w ticks late, slot k of every workgroup
+    is stamped 100 k ticks after its entry, the per-wave V stamps of wave v
+    at 700 + 10 v, and workgroup 3 is the merger (slot 17 at 1500).
+    Layer 0 is skipped as warm-up, so every value is known in closed form."""
+    from long_context_decode_kv_amd import phase_trace as PT
+    L, N = 3, 4
+    x = np.zeros((L, N, 32), dtype=np.int64)
+    for layer in range(L):
+        for w in range(N):
+            e = 10_000 + 2000 * layer + w
+            x[layer, w, 0] = e
+            for k in list(range(1, 17)) + [18, 19, 20, 21, 30, 31]:
+                x[layer, w, k] = e + 100 * k
+            for v in range(8):
+                x[layer, w, 5 + v] = e + 600 + 10 * v
+                x[layer, w, 22 + v] = e + 700 + 10 * v
+        x[layer, 3, 17] = 10_000 + 2000 * layer + 3 + 1500
+    heads = np.array([0, 1, 0, 1])
+    s = PT.summarize(x, heads)
+    us = PT.TICK_US
+    def close(a, b, atol=1e-9):
+        return np.allclose(np.asarray(a, float), np.asarray(b, float), rtol=0, atol=atol)
+    rounded = 0.0051  # fields the tool rounds to 0.01 us
+    # phase k: median over workgroups of (w + 100 k) ticks -> (1.5 + 100 k) ticks; slowest (3 + 100 k)
+    for k, name in PT.SLOTS.items():
+        want = (1503, 1503) if k == 17 else (1.5 + 100 * k, 3 + 100 * k)
+        assert close(s["phases"][name], [t * us for t in want]), name
+    assert close(s["waves"]["last V landed by wave"], [(1.5 + 700 + 10 * v) * us for v in range(8)], rounded)
+    assert close(s["waves"]["last V landed, slowest of the layer"], (3 + 770) * us)
+    # merger chain after its ticket (slot 16 at 1600): slot k at 100 k, slot 17 at 1500
+    want = {16: 0, 30: 1400, 18: 200, 31: 1500, 19: 300, 20: 400, 21: 500, 17: -100}
+    assert close([s["merge"][name] for _, name in PT.MERGE_SLOTS], [want[k] * us for k, _ in PT.MERGE_SLOTS], rounded)
+    assert close(s["gap"], (2000 - 1503) * us)              # next layer's first entry - last merge
+    assert close(s["span"], 1503 * us)
+    # entry to last V per head: workgroups 0, 2 -> head 0, 1, 3 -> head 1; each 770 ticks
+    assert close(s["heads"], [770 * us, 770 * us], rounded)
