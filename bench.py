@@ -551,8 +551,9 @@ def strip_c_comments(text):
 
 def kernel_source_hash():
     """Hash of the code (comments and layout ignored) of every source that
-    decides what the split and merge kernels do: the kernels, the planner
-    that picks their launch shape, and the dispatch."""
+    decides what the split and merge kernels do -- the kernels, the planner
+    that picks their launch shape, and the dispatch -- and of the flags
+    particular sources are compiled with."""
     import glob
     csrc = os.path.join(ROOT, "long_context_decode_kv_amd", "csrc")
     files = sorted(glob.glob(os.path.join(csrc, "*.hip"))) + [os.path.join(csrc, f) for f in
@@ -562,6 +563,8 @@ def kernel_source_hash():
     for f in files:
         if os.path.basename(f) != "probe.hip":
             h.update(strip_c_comments(open(f, encoding="utf-8").read()).encode())
+    from long_context_decode_kv_amd.build import SOURCE_FLAGS  # per-source compiler flags change the code too
+    h.update(repr(sorted(SOURCE_FLAGS.items())).encode())
     return h.hexdigest()[:16]
 
 
